@@ -7,15 +7,15 @@
  * linux guide, "MoE memory handling" section) but not how its scores are summed;
  * the order below is this project's reading, and the GPU router follows it too.
  *
- * Order, for a row of length d:
- *   chunk width V = 16 / sizeof(element) if d % (64 V) == 0, otherwise V = 1;
- *   element i belongs to partial sum j = (i / V) mod 64;
- *   each partial starts at +0 and adds fl(x_i * w_i) for its elements in
- *   ascending i, each product and sum rounded to nearest even (no fused
- *   multiply-add: this file is built with -ffp-contract=off);
- *   the 64 partials are combined by the butterfly a_j <- a_j + a_{j xor s}
- *   for s = 32, 16, 8, 4, 2, 1 (all j at once), and the sum is a_0;
- *   with a bias, the logit is fl(a_0 + b_e).
+ * Order, for a row of length d (a multiple of 64):
+ *   the row is cut into 64 contiguous segments of S = d/64 elements;
+ *   segment j's sum starts at +0 and adds fl(x_i * w_i) for i = jS .. jS+S-1 in
+ *   ascending order, each product and each sum rounded to nearest even (this file
+ *   is built with -ffp-contract=off, so no fused multiply-add);
+ *   the 64 segment sums are joined pairwise, neighbours first:
+ *       level 0 = segment sums, level m+1 [i] = level m [2i] + level m [2i+1],
+ *   six levels down to one value;
+ *   with a bias, the logit is fl(sum + b_e).
  */
 #include <stdint.h>
 #include <string.h>
@@ -27,32 +27,30 @@ static inline float bf16_bits_to_f32(uint16_t h) {
     return f;
 }
 
-static float dot_canonical(const float* xr, const float* wr, int d, int V) {
-    float a[64];
-    for (int j = 0; j < 64; ++j) a[j] = 0.0f;
-    for (int i = 0; i < d; ++i) {
-        int j = (i / V) % 64;
-        float p = xr[i] * wr[i];
-        a[j] = a[j] + p;
+static float dot_canonical(const float* xr, const float* wr, int d) {
+    int S = d / 64;
+    float lvl[64];
+    for (int j = 0; j < 64; ++j) {
+        float a = 0.0f;
+        for (int i = j * S; i < (j + 1) * S; ++i) {
+            float p = xr[i] * wr[i];
+            a = a + p;
+        }
+        lvl[j] = a;
     }
-    for (int s = 32; s >= 1; s >>= 1) {
-        float b[64];
-        for (int j = 0; j < 64; ++j) b[j] = a[j] + a[j ^ s];
-        memcpy(a, b, sizeof(a));
-    }
-    return a[0];
+    for (int n = 32; n >= 1; n >>= 1)
+        for (int i = 0; i < n; ++i) lvl[i] = lvl[2 * i] + lvl[2 * i + 1];
+    return lvl[0];
 }
 
 /*
  * x: [T, d], w: [E, d], both binary32 (is_bf16 = 0) or bfloat16 bit patterns
  * (is_bf16 = 1); bias: [E] binary32 or NULL; out: [T, E] binary32.
+ * Returns 0, or -1 if d is not a multiple of 64 or exceeds 16384.
  */
-void oracle_router_logits(const void* x, const void* w, int is_bf16, const float* bias, int T, int d,
-                          int E, float* out) {
-    int esize = is_bf16 ? 2 : 4;
-    int V = 16 / esize;
-    if (d % (64 * V) != 0) V = 1;
-    if (d > 16384) return; /* rows are staged on the stack */
+int oracle_router_logits(const void* x, const void* w, int is_bf16, const float* bias, int T, int d,
+                         int E, float* out) {
+    if (d % 64 != 0 || d > 16384 || d <= 0) return -1;
 #pragma omp parallel
     {
         float xr[16384];
@@ -69,8 +67,9 @@ void oracle_router_logits(const void* x, const void* w, int is_bf16, const float
                     wrow[i] = ((const float*)w)[(int64_t)e * d + i];
                 }
             }
-            float s = dot_canonical(xr, wrow, d, V);
+            float s = dot_canonical(xr, wrow, d);
             out[te] = bias ? s + bias[e] : s;
         }
     }
+    return 0;
 }

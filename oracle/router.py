@@ -5,7 +5,9 @@ routed experts per layer for DeepSeek-V4-Flash (FreeToken linux guide, "MoE
 memory handling" section; FreeToken RTX 5090 page, introduction).  The router
 form is not given there; the plain reading used here:
 
-* logits  l = x W_r^T + b  (binary32, fixed summation order, ``c/router_canon.c``)
+* logits  l = x W_r^T + b  (binary32, fixed summation order: 64 contiguous
+          segments summed in ascending index, joined pairwise neighbours first;
+          ``c/router_canon.c``)
 * top-k   the k largest logits, largest first; equal logits -> lower expert id
           first (selection on logits equals selection on softmax
           probabilities, since exp is increasing)
@@ -44,7 +46,7 @@ def _load():
         vp = ctypes.c_void_p
         lib.oracle_router_logits.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_int, vp]
-        lib.oracle_router_logits.restype = None
+        lib.oracle_router_logits.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -57,8 +59,8 @@ def router_logits(x: np.ndarray, w_router: np.ndarray, bias, act: str) -> np.nda
     w = np.ascontiguousarray(w_router, dtype=dt)
     T, d = x.shape
     E = w.shape[0]
-    if d > 16384:
-        raise ValueError("oracle router stages rows of at most 16384 elements")
+    if d > 16384 or d % 64:
+        raise ValueError("oracle router needs d a multiple of 64 and at most 16384")
     out = np.empty((T, E), dtype=np.float32)
     b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
     _load().oracle_router_logits(x.ctypes.data, w.ctypes.data, int(is_bf16),
