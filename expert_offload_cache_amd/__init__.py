@@ -1,0 +1,272 @@
+"""Routed-expert MoE layer behind an HBM expert-slot cache, on MI355X (gfx950).
+
+Thin Python binding of libmoe (include/moe.h): argument marshalling only.  Every step
+of the layer runs in the library's HIP kernels; device memory and streams come from
+PyTorch.  There is no CPU fallback: calls fail when libmoe.so is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+
+from ._lib import (MOE_BF16, MOE_F32, MOE_INT4_G128, MoeError, check, lib)
+
+__all__ = ["route", "permute", "expert_ffn_grouped", "combine", "slot_bytes", "pack_expert",
+           "workspace_bytes", "SlotCache", "pinned_alloc", "pinned_free", "profile_enable",
+           "profile_collect", "profile_results", "profile_reset", "MoeError", "WDT", "lib"]
+
+WDT = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4_G128}
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _act(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"activations must be float32 or bfloat16, got {t.dtype}")
+
+
+def _p(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _s(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors passed to libmoe must be contiguous")
+
+
+# ---------------------------------------------------------------------------------------------
+# hot-path calls
+# ---------------------------------------------------------------------------------------------
+def route(x, w_router, bias, k: int, forced_idx=None, out=None, stream=None):
+    """-> (topk_idx int32 [T,k], topk_w f32 [T,k], logits f32 [T,E])."""
+    torch = _torch()
+    _contig(x, w_router, bias, forced_idx)
+    T, d = x.shape
+    E = w_router.shape[0]
+    if out is None:
+        out = (torch.empty((T, k), dtype=torch.int32, device=x.device),
+               torch.empty((T, k), dtype=torch.float32, device=x.device),
+               torch.empty((T, E), dtype=torch.float32, device=x.device))
+    idx, w, logits = out
+    check(lib().moe_route(_p(x), _act(x), T, d, _p(w_router), _p(bias), E, k, _p(forced_idx), _p(idx), _p(w),
+                          _p(logits), _s(stream)))
+    return idx, w, logits
+
+
+def permute(topk_idx, E: int, out=None, stream=None):
+    """-> (counts [E], offsets [E+1], perm [T*k], inv_perm [T*k]) int32."""
+    torch = _torch()
+    _contig(topk_idx)
+    T, k = topk_idx.shape
+    if out is None:
+        dev = topk_idx.device
+        out = (torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev), torch.empty(T * k, dtype=torch.int32, device=dev))
+    c, o, p, ip = out
+    check(lib().moe_permute(_p(topk_idx), T, k, E, _p(c), _p(o), _p(p), _p(ip), None, 0, _s(stream)))
+    return c, o, p, ip
+
+
+def workspace_bytes(T, d, f, E, k, has_shared, act: int, wdt: int) -> int:
+    return int(lib().moe_workspace_bytes(T, d, f, E, k, int(bool(has_shared)), act, wdt))
+
+
+def expert_ffn_grouped(x, perm, offsets, counts, slot_of_expert, slot_pool, n_slots: int, slot_stride: int,
+                       wdt: str, f: int, k: int, shared_w=None, y_perm=None, ws=None, stream=None):
+    """Grouped SwiGLU experts through the slot table. -> (y_perm f32 [T*k (+T), d], ws)."""
+    torch = _torch()
+    _contig(x, perm, offsets, counts, slot_of_expert)
+    T, d = x.shape
+    E = counts.shape[0]
+    act = _act(x)
+    rows = T * k + (T if shared_w is not None else 0)
+    if y_perm is None:
+        y_perm = torch.empty((rows, d), dtype=torch.float32, device=x.device)
+    need = workspace_bytes(T, d, f, E, k, shared_w is not None, act, WDT[wdt])
+    if ws is None:
+        ws = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    check(lib().moe_expert_ffn_grouped(_p(x), act, T, d, f, E, k, _p(perm), _p(offsets), _p(counts),
+                                       _p(slot_of_expert), n_slots, _p(slot_pool), slot_stride, WDT[wdt],
+                                       _p(shared_w), _p(y_perm), _p(ws), ws.numel(), _s(stream)))
+    return y_perm, ws
+
+
+def combine(y_perm, topk_w, inv_perm, k: int, has_shared: bool, out_dtype, y=None, stream=None):
+    torch = _torch()
+    _contig(y_perm, topk_w, inv_perm)
+    T = topk_w.shape[0]
+    d = y_perm.shape[1]
+    if y is None:
+        y = torch.empty((T, d), dtype=out_dtype, device=y_perm.device)
+    code = MOE_BF16 if y.dtype == torch.bfloat16 else MOE_F32
+    check(lib().moe_combine(_p(y_perm), _p(topk_w), _p(inv_perm), T, k, d, int(bool(has_shared)), _p(y), code,
+                            _s(stream)))
+    return y
+
+
+# ---------------------------------------------------------------------------------------------
+# slots
+# ---------------------------------------------------------------------------------------------
+def slot_bytes(d: int, f: int, wdt: str) -> int:
+    return int(lib().moe_slot_bytes(d, f, WDT[wdt]))
+
+
+def _np_ptr(a):
+    return None if a is None else np.ascontiguousarray(a).ctypes.data
+
+
+def pack_expert(wdt: str, d: int, f: int, wg, wu, wd, sg=None, su=None, sd=None, out=None) -> np.ndarray:
+    """Canonical expert weights (numpy) -> slot image (numpy uint8, or written into ``out``)."""
+    n = slot_bytes(d, f, wdt)
+    if n == 0:
+        raise MoeError(-2, f"unsupported slot shape d={d} f={f} {wdt}")
+    if out is None:
+        out = np.empty(n, dtype=np.uint8)
+    arrs = [np.ascontiguousarray(a) if a is not None else None for a in (wg, wu, wd, sg, su, sd)]
+    optr = out.ctypes.data if isinstance(out, np.ndarray) else int(out)
+    check(lib().moe_pack_expert(WDT[wdt], d, f, *[_np_ptr(a) for a in arrs], optr))
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# expert-slot cache
+# ---------------------------------------------------------------------------------------------
+class SlotCache:
+    """LRU expert-slot cache shared by all layers (wraps moe_cache_*)."""
+
+    def __init__(self, L: int, E: int, n_slots: int, slot_stride: int = 0, slot_pool=None, slot_table=None,
+                 host_ptrs=None):
+        self.L, self.E, self.C = L, E, n_slots
+        self._host = None
+        hp = None
+        if host_ptrs is not None:
+            self._host = (ctypes.c_void_p * (L * E))(*[int(p) for p in host_ptrs])
+            hp = ctypes.cast(self._host, ctypes.c_void_p)
+        h = ctypes.c_void_p()
+        check(lib().moe_cache_create(L, E, n_slots, slot_stride, _p(slot_pool), _p(slot_table), hp,
+                                     ctypes.byref(h)))
+        self.h = h
+
+    def lookup(self, layer: int, ids):
+        ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+        slots = np.empty(len(ids), dtype=np.int32)
+        nm = ctypes.c_int32()
+        check(lib().moe_cache_lookup(self.h, layer, ids.ctypes.data, len(ids), slots.ctypes.data, ctypes.byref(nm)))
+        return slots, nm.value
+
+    def fill(self, copy_stream=None, compute_stream=None):
+        check(lib().moe_cache_fill(self.h, _s(copy_stream), _s(compute_stream)))
+
+    def prefetch_layer(self, layer: int, copy_stream=None, compute_stream=None):
+        check(lib().moe_cache_prefetch_layer(self.h, layer, _s(copy_stream), _s(compute_stream)))
+
+    def mark_read(self, layer: int, compute_stream=None):
+        check(lib().moe_cache_mark_read(self.h, layer, _s(compute_stream)))
+
+    def policy_fill(self):
+        """fill() of a policy-only cache (no streams involved)."""
+        check(lib().moe_cache_fill(self.h, None, None))
+
+    def policy_prefetch(self, layer: int):
+        """prefetch_layer() of a policy-only cache (no streams involved)."""
+        check(lib().moe_cache_prefetch_layer(self.h, layer, None, None))
+
+    def policy_mark_read(self, layer: int):
+        check(lib().moe_cache_mark_read(self.h, layer, None))
+
+    def stats(self):
+        out = np.zeros(6, dtype=np.int64)
+        check(lib().moe_cache_stats(self.h, out.ctypes.data))
+        keys = ("dec_acc", "dec_hit", "dec_miss", "pre_acc", "pre_miss", "bytes_h2d")
+        return dict(zip(keys, (int(v) for v in out)))
+
+    def trace(self):
+        n = ctypes.c_int64()
+        check(lib().moe_cache_trace(self.h, None, 0, ctypes.byref(n)))
+        buf = np.empty(n.value, dtype=np.uint8)
+        if n.value:
+            check(lib().moe_cache_trace(self.h, buf.ctypes.data, n.value, ctypes.byref(n)))
+        return buf
+
+    def copy_log(self):
+        n = ctypes.c_int64()
+        check(lib().moe_cache_copy_log(self.h, None, 0, ctypes.byref(n)))
+        buf = np.empty((n.value, 3), dtype=np.int64)
+        if n.value:
+            check(lib().moe_cache_copy_log(self.h, buf.ctypes.data, n.value, ctypes.byref(n)))
+        return buf
+
+    def inject_copy_failures(self, n: int):
+        check(lib().moe_cache_inject_copy_failures(self.h, n))
+
+    def slot_of(self, layer: int, expert: int) -> int:
+        s = ctypes.c_int32()
+        check(lib().moe_cache_slot_of(self.h, layer, expert, ctypes.byref(s)))
+        return s.value
+
+    def close(self):
+        if self.h:
+            lib().moe_cache_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def pinned_alloc(nbytes: int) -> int:
+    p = ctypes.c_void_p()
+    check(lib().moe_pinned_alloc(nbytes, ctypes.byref(p)))
+    return p.value
+
+
+def pinned_free(ptr: int):
+    lib().moe_pinned_free(ptr)
+
+
+# ---------------------------------------------------------------------------------------------
+# kernel timing
+# ---------------------------------------------------------------------------------------------
+def profile_enable(on: bool = True):
+    lib().moe_profile_enable(int(on))
+
+
+def profile_collect():
+    check(lib().moe_profile_collect())
+
+
+def profile_results() -> dict:
+    """{kernel name: (total ms, launches)} accumulated since the last reset."""
+    out = {}
+    i = 0
+    name = ctypes.create_string_buffer(128)
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    while lib().moe_profile_get(i, name, 128, ctypes.byref(ms), ctypes.byref(n)) == 0:
+        out[name.value.decode()] = (ms.value, n.value)
+        i += 1
+    return out
+
+
+def profile_reset():
+    lib().moe_profile_reset()

@@ -1,0 +1,66 @@
+// moe_combine: y[t] = sum_j g[t,j] * y_perm[inv_perm[t*k+j]] (+ shared expert row), j ascending,
+// binary32 accumulation, one rounding to the output type.  The pages do not give the combine;
+// a gate-weighted sum of the selected experts' outputs is the plain reading.
+// Memory-bound: every thread owns 4 consecutive columns of one token (16-byte loads).
+#include <hip/hip_runtime.h>
+
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+template <bool kBf16Out>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ yp, const float* __restrict__ g,
+                                                      const int32_t* __restrict__ inv, int T, int k, int d,
+                                                      int has_shared, void* __restrict__ y) {
+    const int t = blockIdx.y;
+    const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (c >= d) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+        const float gj = g[(size_t)t * k + j];
+        const float4 v = *(const float4*)(yp + (size_t)inv[(size_t)t * k + j] * d + c);
+        acc.x = __builtin_fmaf(gj, v.x, acc.x);
+        acc.y = __builtin_fmaf(gj, v.y, acc.y);
+        acc.z = __builtin_fmaf(gj, v.z, acc.z);
+        acc.w = __builtin_fmaf(gj, v.w, acc.w);
+    }
+    if (has_shared) {
+        const float4 v = *(const float4*)(yp + ((size_t)T * k + t) * d + c);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    if constexpr (kBf16Out) {
+        uint2 o;
+        o.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
+        o.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
+        *(uint2*)((uint16_t*)y + (size_t)t * d + c) = o;
+    } else {
+        *(float4*)((float*)y + (size_t)t * d + c) = acc;
+    }
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_combine(const float* y_perm, const float* topk_w, const int32_t* inv_perm, int T,
+                                  int k, int d, int has_shared, void* y, moe_dtype out, moe_stream s) {
+    MOE_CHECK(T >= 0 && k >= 1 && d >= 4 && d % 4 == 0, MOE_ESHAPE, "moe_combine: bad shape T=%d k=%d d=%d", T, k, d);
+    if (T == 0) return MOE_OK;
+    MOE_CHECK(T <= 65535, MOE_ESHAPE, "moe_combine: T=%d too large", T);
+    MOE_CHECK(out == MOE_F32 || out == MOE_BF16, MOE_EDTYPE, "moe_combine: output must be F32 or BF16");
+    MOE_CHECK(y_perm && topk_w && inv_perm && y, MOE_EINVAL, "moe_combine: NULL pointer");
+    MOE_CHECK((uintptr_t)y_perm % 16 == 0 && (uintptr_t)y % 8 == 0, MOE_EINVAL, "moe_combine: misaligned buffers");
+    hipStream_t st = (hipStream_t)s;
+    dim3 grid((unsigned)((d / 4 + 255) / 256), (unsigned)T);
+    ProfScope p("combine", st);
+    if (out == MOE_BF16)
+        combine_kernel<true><<<grid, 256, 0, st>>>(y_perm, topk_w, inv_perm, T, k, d, has_shared, y);
+    else
+        combine_kernel<false><<<grid, 256, 0, st>>>(y_perm, topk_w, inv_perm, T, k, d, has_shared, y);
+    return check_launch("combine");
+}

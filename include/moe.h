@@ -1,0 +1,239 @@
+/*
+ * libmoe -- routed-expert MoE layer forward behind an expert-slot cache, for AMD
+ * Instinct MI355X (gfx950).  Plain C ABI: raw pointers, sizes and status codes.
+ *
+ * What the layer is (the pages describe an offloaded-MoE runtime; citations
+ * name the page and its section):
+ *   - a router picks a few experts per token (FreeToken linux guide, "MoE memory
+ *     handling": DeepSeek-V4-Flash activates 6 of 256 routed experts per layer);
+ *   - GPU memory holds expert slots, the whole routed pool stays in host RAM, and
+ *     one LRU over those slots is shared by all MoE layers (same section, memory
+ *     tier table and mechanism table; FreeToken GGUF page, "MoE backends",
+ *     offload backend);
+ *   - a missed expert is copied to GPU memory over PCIe and kept for reuse (same
+ *     places); prefill streams the next layer's experts while the current layer
+ *     runs (FreeToken linux guide, mechanism table, full-layer double buffering;
+ *     FreeToken RTX 5090 page, memory-hierarchy paragraph).
+ * Router form, expert form and the combine are not given on the pages; the
+ * plain readings used are stated at each call.
+ *
+ * Conventions for every call:
+ *   - OWNERSHIP: the caller owns every buffer passed in (device or host); the
+ *     library allocates no device memory.  It owns only cache objects, their HIP
+ *     events, pinned blocks returned by moe_pinned_alloc, and profiling events.
+ *   - ERRORS: arguments are checked on the host before anything is enqueued; a
+ *     call that returns non-OK has enqueued nothing.  moe_last_error() gives a
+ *     thread-local message for the last non-OK status.  Asynchronous device
+ *     faults surface at the caller's next synchronisation, as in HIP.
+ *   - STREAMS: moe_stream is a hipStream_t (NULL = the null stream).  Kernel
+ *     calls are asynchronous on their stream and run on the current device.
+ *   - T == 0 is a valid no-op that returns MOE_OK.
+ *   - DETERMINISM: identical inputs give bitwise identical outputs; no atomics
+ *     decide positions or the order of any floating-point sum.
+ *   - DTYPES: activations MOE_F32 or MOE_BF16 (bfloat16 bit patterns, uint16);
+ *     weights MOE_F32, MOE_BF16 or MOE_INT4_G128.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_API __attribute__((visibility("default")))
+
+typedef int32_t moe_status;
+enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,    /* bad pointer, range or flag */
+    MOE_ESHAPE = -2,    /* shape outside the supported set */
+    MOE_EDTYPE = -3,    /* dtype combination not supported */
+    MOE_ENOMEM = -4,    /* workspace too small or host allocation failed */
+    MOE_EHIP = -5,      /* a HIP runtime call failed; text in moe_last_error() */
+    MOE_ECAPACITY = -6, /* request set larger than the slot cache */
+    MOE_ESTATE = -7     /* call out of order, or an eviction would hit an unread slot */
+};
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_INT4_G128 = 2 } moe_dtype;
+typedef void* moe_stream;
+
+MOE_API const char* moe_last_error(void);
+MOE_API const char* moe_version(void);
+
+/* ------------------------------------------------------------------------------------------
+ * Expert slots.  One slot holds one SwiGLU expert (W_g, W_u: [f, d]; W_d: [d, f]; rows are
+ * outputs) in the kernel-ready layout below; the pinned host pool stores experts in the same
+ * layout so that a cache fill is one contiguous copy per expert (the pages' FTW format keeps
+ * expert banks in runtime layout for the same reason: FreeToken linux guide, setup section,
+ * model-weight preparation).
+ *
+ * Layout: matrices are cut into blocks of 16 rows.  Gate/up blocks alternate (gate rows
+ * 16b..16b+15, then up rows 16b..16b+15, for b = 0 .. f/16-1), followed by the W_d blocks.
+ *   F32/BF16: a 16-row block is K/32 consecutive fragments of 16 rows x 32 inputs; inside a
+ *     fragment, lane l (0..63) owns row l%16, inputs 8*(l/16) .. 8*(l/16)+7, stored as 8
+ *     consecutive elements at element offset 8*l.
+ *   INT4_G128: a 16-row block is K/128 fragments of 16 rows x 128 inputs (1024 bytes), then
+ *     the block's scales as bf16 [16 rows][K/128].  In a fragment lane l owns 16 bytes at
+ *     offset 16*l: row l%16, word s (0..3) holds inputs 32s + 8*(l/16) + (0..7); input pair
+ *     (2p, 2p+1) of a word sits in bits [4p, 4p+4) and [16+4p, 20+4p).  A stored nibble u is
+ *     the integer u - 8 in [-7, 7]; weight = (u - 8) * scale of its row and 128-group.
+ * ------------------------------------------------------------------------------------------ */
+
+/* Bytes of one packed expert (a multiple of 256).  0 if the shape/dtype is unsupported:
+ * d, f multiples of 32 (F32/BF16) or of 128 (INT4_G128), 64 <= d, f <= 16384. */
+MOE_API size_t moe_slot_bytes(int d, int f, moe_dtype w);
+
+/* Pack one expert from the canonical row-major layout into a slot image (host memory).
+ * F32/BF16: wg, wu [f][d], wd [d][f] in the weight dtype; sg, su, sd must be NULL.
+ * INT4_G128: wg, wu [f][d/2], wd [d][f/2] bytes (element 2i low nibble of byte i, offset
+ * binary); sg, su [f][d/128], sd [d][f/128] bf16 scale bits.  slot_out: moe_slot_bytes bytes. */
+MOE_API moe_status moe_pack_expert(moe_dtype w, int d, int f, const void* wg, const void* wu,
+                                   const void* wd, const void* sg, const void* su, const void* sd,
+                                   void* slot_out);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_route -- router scores, top-k and gates (FreeToken linux guide, "MoE memory handling":
+ * the router activates a subset of experts per token).
+ *   logits[t,e] = x[t,:] . w_router[e,:] (+ bias[e]) in binary32, in one fixed order: row
+ *     elements are split into 64 contiguous segments of d/64; each segment is summed from +0
+ *     in ascending index with every product and sum rounded to nearest even (no fused
+ *     multiply-add for F32 inputs; for BF16 inputs products are exact); the 64 segment sums
+ *     are joined pairwise, neighbours first (a tree of 6 levels); the bias is added last.
+ *   topk_idx[t,:]  the k largest logits, largest first, equal logits -> lower expert id first.
+ *   topk_w[t,j]    softmax over all E logits renormalised over the selected k, i.e.
+ *                  exp(l_j - l_max) / sum_{i in S} exp(l_i - l_max), formed in binary64 and
+ *                  rounded once to binary32.
+ * With forced_idx (a device [T,k] int32 array of distinct ids in [0,E), e.g. a replayed
+ * routing trace), the selection is skipped: topk_idx = forced_idx and the gates are computed
+ * at those ids in the given order.  Out-of-range forced ids give unspecified gates.
+ *   x [T,d] act dtype; w_router [E,d] act dtype; bias [E] f32 or NULL (device pointers).
+ *   logits [T,E] f32 (device, required: it is the selection's input as well as an output).
+ * Shapes: 1 <= k <= E <= 1024, d a multiple of 64, d <= 16384. */
+MOE_API moe_status moe_route(const void* x, moe_dtype act, int T, int d, const void* w_router,
+                             const float* bias, int E, int k, const int32_t* forced_idx,
+                             int32_t* topk_idx, float* topk_w, float* logits, moe_stream s);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_permute -- group the T*k (token, choice) pairs by expert (pages silent; the plain
+ * reading is a stable counting sort of the flat ids t*k + j):
+ *   counts[e] pairs routed to e; offsets[0..E] exclusive prefix sum (offsets[E] = T*k);
+ *   perm[p] flat pair index at sorted position p (stable: ascending flat index within an
+ *   expert); inv_perm[i] sorted position of flat pair i.  All int32, device.
+ * topk_idx must hold ids in [0, E).  T*k <= 2^24.  ws/ws_bytes unused (may be NULL/0). */
+MOE_API moe_status moe_permute(const int32_t* topk_idx, int T, int k, int E, int32_t* counts,
+                               int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws,
+                               size_t ws_bytes, moe_stream s);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_expert_ffn_grouped -- every expert with n_e > 0 runs once on its n_e rows (SwiGLU, the
+ * plain reading of the expert form: h = silu(x W_g^T) * (x W_u^T), y = h W_d^T, no biases).
+ * Expert e's weights are read from the slot slot_of_expert[e] of slot_pool (FreeToken GGUF
+ * page, offload backend: expert slots on the GPU), i.e. at slot_pool + slot * slot_stride.
+ *   x [T,d] act; perm, offsets, counts from moe_permute; slot_of_expert [E] int32 (a device
+ *   row of the slot table; a slot outside [0, n_slots) sets the workspace status word to 1
+ *   and that expert's rows to 0 -- it never reads outside the pool).
+ *   shared_w: an always-on shared expert packed like a slot (or NULL); it runs on all T tokens.
+ *   y_perm [T*k (+T if shared_w), d] f32: row p = expert output of sorted pair p; rows T*k+t
+ *   hold the shared expert's output for token t.
+ *   ws: device workspace of at least moe_workspace_bytes(...) bytes, zero-filled before its
+ *   first use.  Its first 4 bytes are a sticky int32 status word (0 = no error).
+ * Intermediate h is rounded to bf16 when act is BF16 (binary32 when act is F32). */
+MOE_API size_t moe_workspace_bytes(int T, int d, int f, int E, int k, int has_shared,
+                                   moe_dtype act, moe_dtype w);
+MOE_API moe_status moe_expert_ffn_grouped(const void* x, moe_dtype act, int T, int d, int f, int E,
+                                          int k, const int32_t* perm, const int32_t* offsets,
+                                          const int32_t* counts, const int32_t* slot_of_expert,
+                                          int n_slots, const void* slot_pool, size_t slot_stride,
+                                          moe_dtype w, const void* shared_w, float* y_perm,
+                                          void* ws, size_t ws_bytes, moe_stream s);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_combine -- gate-weighted sum (pages silent on the form; plain reading):
+ *   y[t,:] = sum_{j=0..k-1} topk_w[t,j] * y_perm[inv_perm[t*k+j], :]  (+ y_perm[T*k+t, :] if
+ *   has_shared), j ascending, binary32 accumulation, one final rounding to out (F32 or BF16,
+ *   round to nearest even). */
+MOE_API moe_status moe_combine(const float* y_perm, const float* topk_w, const int32_t* inv_perm,
+                               int T, int k, int d, int has_shared, void* y, moe_dtype out,
+                               moe_stream s);
+
+/* ------------------------------------------------------------------------------------------
+ * Expert-slot cache shared by all MoE layers (FreeToken linux guide, "MoE memory handling":
+ * one LRU over GPU expert slots across the MoE layers, full pool in host RAM; a missed expert
+ * is copied over PCIe from pinned memory and kept -- FreeToken GGUF page, offload backend;
+ * prefill double-buffers the next layer -- mechanism table).
+ * Keys are (layer, expert).  A request set S is processed as: resident members are hits and
+ * become most recent in ascending id; then each other member, ascending, is a miss that takes
+ * the lowest-numbered free slot, else evicts the least recently used entry and reuses its slot.
+ * |S| > n_slots -> MOE_ECAPACITY.  Slots handed out by a lookup/prefetch of layer l stay pinned
+ * until moe_cache_mark_read(l); evicting a pinned slot is refused with MOE_ESTATE (it never
+ * happens when n_slots >= 2E with the prefill order prefetch(l+1) -> mark_read(l)).
+ * Policy-only mode: slot_pool == NULL (then slot_table and host_expert must be NULL) keeps the
+ * bookkeeping and statistics and makes no HIP call at all (simulations, CPU tests).
+ * The cache object is not thread-safe; mark_read events must come from one compute stream. */
+typedef struct moe_cache moe_cache;
+
+/* slot_pool: device, n_slots * slot_stride bytes.  slot_table: device int32 [L*E]; this call
+ * sets it to -1 (synchronously) and the cache keeps it equal to its own table.
+ * host_expert: [L*E] host pointers to pinned slot images of slot_stride bytes (layer-major).
+ * The arrays pointed to must stay valid until moe_cache_destroy. */
+MOE_API moe_status moe_cache_create(int L, int E, int n_slots, size_t slot_stride, void* slot_pool,
+                                    int32_t* slot_table, const void* const* host_expert,
+                                    moe_cache** out);
+/* Decode lookup of layer `layer`: ids (host, n distinct ids in [0,E)).  slots_out[i] (host) is
+ * the slot of ids[i] once pending fills are done; *n_miss_out the number of misses.  Host only:
+ * the caller has the ids on the host (copy topk_idx back and synchronise first). */
+MOE_API moe_status moe_cache_lookup(moe_cache* c, int layer, const int32_t* ids, int n,
+                                    int32_t* slots_out, int32_t* n_miss_out);
+/* Enqueue the copies of all pending misses on `copy` (each waits for the last recorded read of
+ * the slot it overwrites), then the slot-table update; `compute` waits for them.  A failed copy
+ * enqueue leaves the failed entries non-resident (-1) and returns MOE_EHIP. */
+MOE_API moe_status moe_cache_fill(moe_cache* c, moe_stream copy, moe_stream compute);
+/* Prefill: request all E experts of `layer` (prefill statistics) and fill on `copy`; `compute`
+ * waits for the copies (enqueue the current layer's kernels on `compute` first, then prefetch
+ * the next layer, so that the copies overlap the current layer). */
+MOE_API moe_status moe_cache_prefetch_layer(moe_cache* c, int layer, moe_stream copy,
+                                            moe_stream compute);
+/* Record on `compute` the point after which layer `layer`'s pinned slots are no longer read
+ * (call after enqueueing the layer's kernels); unpins them. */
+MOE_API moe_status moe_cache_mark_read(moe_cache* c, int layer, moe_stream compute);
+/* out[0..5] = decode accesses, decode hits, decode misses, prefill accesses, prefill misses,
+ * bytes copied host -> device. */
+MOE_API moe_status moe_cache_stats(const moe_cache* c, int64_t out[6]);
+/* Hit (1) / miss (0) flag of every access so far, in request order, ascending id within a
+ * request; writes min(cap, total) flags and sets *n to the total. */
+MOE_API moe_status moe_cache_trace(const moe_cache* c, uint8_t* hitmiss, int64_t cap, int64_t* n);
+/* Host view of the slot table: *slot = slot of (layer, expert) or -1. */
+MOE_API moe_status moe_cache_slot_of(const moe_cache* c, int layer, int expert, int32_t* slot);
+/* Copy plan so far (test and tracing aid): for the i-th expert copy enqueued (or, in
+ * policy-only mode, simulated) out[3i..3i+2] = slot, key (layer*E + expert), and the read
+ * sequence number the copy waited for (-1 = none; sequence numbers count mark_read calls from 1).
+ * Writes min(cap, total) triples and sets *n to the total. */
+MOE_API moe_status moe_cache_copy_log(const moe_cache* c, int64_t* out, int64_t cap, int64_t* n);
+/* Fault injection for tests of the failure path: the next n expert copies are treated as failed
+ * enqueues (no HIP call is made for them), which leaves those entries non-resident. */
+MOE_API moe_status moe_cache_inject_copy_failures(moe_cache* c, int n);
+/* Waits for outstanding copies, releases events; the caller's buffers are untouched. */
+MOE_API void moe_cache_destroy(moe_cache* c);
+
+/* Page-locked host memory for the expert pool (hipHostMalloc). */
+MOE_API moe_status moe_pinned_alloc(size_t bytes, void** out);
+MOE_API void moe_pinned_free(void* p);
+
+/* ------------------------------------------------------------------------------------------
+ * Kernel timing.  While enabled, each kernel launch of the calls above is bracketed by two
+ * HIP events recorded on the launch stream; moe_profile_collect() waits for them and adds the
+ * elapsed times per kernel name.  moe_profile_get(i, ...) reads entry i (MOE_EINVAL past the
+ * end).  Adds event overhead: for measurement runs only. */
+MOE_API void moe_profile_enable(int on);
+MOE_API moe_status moe_profile_collect(void);
+MOE_API moe_status moe_profile_get(int i, char* name, int name_cap, double* total_ms,
+                                   int64_t* launches);
+MOE_API void moe_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

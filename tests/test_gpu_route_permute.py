@@ -1,0 +1,106 @@
+"""GPU router and permutation against the oracle: bit-exact logits, ids, counts, offsets,
+permutation; gates within 1e-6 relative.  Sizes span several tiles with ragged tails, up to the
+full prefill batch (8192 tokens x 256 experts x d 4096)."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import need_gpu, to_dev
+from oracle.permute import permute as o_permute
+from oracle.router import renorm_gates, router_logits, topk_select
+
+pytestmark = pytest.mark.gpu
+
+ROUTE_CASES = [
+    # (act, d, E, k, T, bias)
+    ("f32", 64, 8, 2, 16, None),          # tiny fp32 layer
+    ("f32", 256, 40, 3, 77, 1.1),         # fp32, ragged T on the tiled path
+    ("bf16", 2048, 128, 8, 1, 1.1),       # Qwen-A3B shaped decode
+    ("bf16", 2048, 128, 8, 4, 1.1),
+    ("bf16", 2048, 128, 8, 16, 1.1),
+    ("bf16", 2048, 128, 8, 64, 1.1),
+    ("bf16", 4096, 256, 6, 1, 1.1),       # DeepSeek-V4-Flash shaped decode
+    ("bf16", 4096, 256, 6, 2, 1.1),
+    ("bf16", 4096, 256, 6, 8, 1.1),
+    ("bf16", 4096, 256, 6, 65, 1.1),      # just past the decode kernel
+    ("bf16", 4096, 256, 6, 333, 1.1),     # ragged tiles
+    ("bf16", 4096, 256, 6, 512, 1.1),     # prefill batches
+    ("bf16", 4096, 256, 6, 2048, 1.1),
+    ("bf16", 4096, 256, 6, 8192, 1.1),
+    ("bf16", 1024, 1024, 8, 70, None),    # maximum expert count
+    ("bf16", 512, 100, 100, 9, 1.1),      # k = E, ragged E
+]
+
+
+@pytest.mark.parametrize("act,d,E,k,T,bias", ROUTE_CASES)
+def test_route_bit_exact(act, d, E, k, T, bias):
+    need_gpu()
+    import expert_offload_cache_amd as moe
+
+    print(f"route act={act} d={d} E={E} k={k} T={T}", flush=True)
+    gen = synth.normal_bf16 if act == "bf16" else synth.normal_f32
+    x = gen(11, synth.stream_id(synth.KIND_X, 0, T), (T, d), 1.0)
+    w = gen(11, synth.stream_id(synth.KIND_ROUTER, 0, E), (E, d), 0.02)
+    b = synth.router_bias(11, E, bias) if bias else None
+    lg = router_logits(x, w, b, act)
+    idx = topk_select(lg, k)
+    g = renorm_gates(lg, idx)
+    xd, wd = to_dev(x, act), to_dev(w, act)
+    bd = None if b is None else to_dev(b, "f32")
+    gi, gw, gl = moe.route(xd, wd, bd, k)
+    gl = gl.cpu().numpy()
+    assert np.array_equal(gl.view(np.uint32), lg.view(np.uint32)), "logits differ"
+    assert np.array_equal(gi.cpu().numpy(), idx)
+    gw = gw.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(gw - g) / g) <= 1e-6
+    # near-ties: report the smallest k-th / (k+1)-th gap the case exercised
+    if k < E:
+        s = -np.sort(-lg, axis=1)
+        print(f"min top-k gap {np.min(s[:, k - 1] - s[:, k]):.3g}")
+
+
+def test_route_forced_ids():
+    need_gpu()
+    import expert_offload_cache_amd as moe
+
+    T, d, E, k = 37, 4096, 256, 6
+    x = synth.normal_bf16(2, 5, (T, d), 1.0)
+    w = synth.normal_bf16(2, 6, (E, d), 0.02)
+    b = synth.router_bias(2, E, 1.1)
+    forced = synth.forced_topk(2, T, E, k)
+    lg = router_logits(x, w, b, "bf16")
+    g = renorm_gates(lg, forced)
+    gi, gw, _ = moe.route(to_dev(x, "bf16"), to_dev(w, "bf16"), to_dev(b, "f32"), k, forced_idx=to_dev(forced, "i32"))
+    assert np.array_equal(gi.cpu().numpy(), forced)
+    assert np.max(np.abs(gw.cpu().numpy() - g) / g) <= 1e-6
+
+
+PERM_CASES = [
+    # (T, E, k, kind)
+    (1, 8, 2, "rand"), (16, 8, 2, "rand"), (64, 128, 8, "rand"), (1, 256, 6, "rand"), (333, 256, 6, "rand"),
+    (8192, 256, 6, "rand"), (1000, 1024, 8, "rand"), (4096, 64, 1, "one"), (700, 5, 5, "all"),
+    (8192, 256, 6, "zipf"),
+]
+
+
+@pytest.mark.parametrize("T,E,k,kind", PERM_CASES)
+def test_permute_bit_exact(T, E, k, kind):
+    need_gpu()
+    import expert_offload_cache_amd as moe
+
+    print(f"permute T={T} E={E} k={k} {kind}", flush=True)
+    if kind == "rand":
+        idx = synth.forced_topk(T, T, E, k)
+    elif kind == "one":
+        idx = np.full((T, k), 3, dtype=np.int32)  # every pair on one expert
+    elif kind == "all":
+        idx = np.tile(np.arange(E, dtype=np.int32)[::-1], (T, 1))
+    else:
+        tr = synth.routing_trace(0, T, 1, E, k, p_reuse=0.0)  # independent Zipf draws per token
+        idx = np.ascontiguousarray(tr[:, 0, :])
+    c, o, p, ip = o_permute(idx, E)
+    gc, go, gp, gip = moe.permute(to_dev(idx, "i32"), E)
+    assert np.array_equal(gc.cpu().numpy(), c)
+    assert np.array_equal(go.cpu().numpy(), o)
+    assert np.array_equal(gp.cpu().numpy(), p)
+    assert np.array_equal(gip.cpu().numpy(), ip)
