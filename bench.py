@@ -141,18 +141,22 @@ def main():
         kern = {name: ms / n * 1e3 for name, (ms, n) in prof.items()}  # average us per launch
         res[T] = dict(el=el, steps=steps, avg=avg, kern=kern)
 
+    def kname(kern, part):
+        names = [n for n in kern if n.startswith("ffn_") and part in n]
+        return names[0] if names else None
+
     m = res[Tmain]
     ms_per_step = m["el"] / m["steps"] * 1e3
-    gu_us = m["kern"].get("ffn_gemv_gateup_bf16")
-    dn_us = m["kern"].get("ffn_gemv_down_bf16")
+    gu_name = kname(m["kern"], "gateup")
+    gu_us = m["kern"].get(gu_name)
     achieved = m["avg"]["gateup"] / (gu_us * 1e-6) / 1e9 if gu_us else None
-    roofline = {"bound": "hbm", "kernel": "ffn_gemv_gateup_bf16", "achieved": achieved, "peak": HBM_PEAK_GBS,
+    roofline = {"bound": "hbm", "kernel": gu_name, "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": None,
                 "bytes_per_launch": m["avg"]["gateup"], "avg_launch_us": gu_us}
     sweep = {}
     for T, r in res.items():
-        gu = r["kern"].get("ffn_gemv_gateup_bf16")
-        dn = r["kern"].get("ffn_gemv_down_bf16")
+        gu = r["kern"].get(kname(r["kern"], "gateup"))
+        dn = r["kern"].get(kname(r["kern"], "down"))
         ffn_us = (gu or 0) + (dn or 0)
         sweep[str(T)] = {
             "tokens_per_s": T * r["steps"] / r["el"], "layer_us": r["el"] / r["steps"] * 1e6,

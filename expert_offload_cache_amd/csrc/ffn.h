@@ -25,8 +25,8 @@ struct FfnArgs {
 constexpr size_t kWsHeader = 256;
 constexpr size_t kPlanBytes = 1 << 16;
 
-// decode path: GEMV kernels (ffn_gemv.hip)
-moe_status ffn_gemv(const FfnArgs& a, moe_dtype act, moe_dtype w, int grid_experts, hipStream_t st);
+// decode path: grouped GEMV kernels (ffn_gemv.hip)
+moe_status ffn_gemv(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st);
 // prefill path: MFMA grouped GEMM (ffn_mfma.hip); returns MOE_EDTYPE when it does not apply
 moe_status ffn_mfma(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st);
 

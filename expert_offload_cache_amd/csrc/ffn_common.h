@@ -1,0 +1,143 @@
+// Device code shared by the grouped-GEMV kernels (one-shot and persistent).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "ffn.h"
+#include "slot_layout.h"
+
+namespace moe {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// streaming 16-byte load (weights are read once per call)
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+    u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+template <int W>
+struct Frag;
+template <>
+struct Frag<MOE_BF16> {
+    static constexpr int kIn = 32, kBytes = 1024, kLaneVec = 1;  // 16-byte vectors per lane
+};
+template <>
+struct Frag<MOE_F32> {
+    static constexpr int kIn = 32, kBytes = 2048, kLaneVec = 2;
+};
+template <>
+struct Frag<MOE_INT4_G128> {
+    static constexpr int kIn = 128, kBytes = 1024, kLaneVec = 1;
+};
+
+constexpr uint32_t kMagic = 0x43004300u;  // bf16 pair (128, 128)
+constexpr uint32_t kOnes = 0x3F803F80u;   // bf16 pair (1, 1)
+
+// int4 word (8 nibbles, input pair p at bits 4p and 16+4p) -> 4 bf16 pairs (128 + u)
+__device__ __forceinline__ void int4_word_to_bf16(uint32_t w, uint32_t* out) {
+    out[0] = (w & 0x000F000Fu) | kMagic;
+    out[1] = ((w >> 4) & 0x000F000Fu) | kMagic;
+    out[2] = ((w >> 8) & 0x000F000Fu) | kMagic;
+    out[3] = ((w >> 12) & 0x000F000Fu) | kMagic;
+}
+
+enum { kGateUp = 0, kDown = 1 };
+
+// One token group of one item: acc[i][m] = this lane's partial dot products of its weight share
+// (fragments f0 .. f0+nmine-1 of matrix m, already in registers) with token i's staged row.
+template <int W, bool kBf16Act, int FPW, int NTG, int NM>
+__device__ __forceinline__ void gemv_group(const uint4 (&wreg)[FPW][NM][Frag<W>::kLaneVec],
+                                           const float (&sc)[FPW][NM], const uint8_t* s_x, size_t row_bytes,
+                                           int f0, int nmine, int nt, int q, float (&acc)[NTG][NM]) {
+    constexpr int LV = Frag<W>::kLaneVec;
+#pragma unroll
+    for (int i = 0; i < NTG; ++i)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) acc[i][m] = 0.f;
+#pragma unroll
+    for (int c = 0; c < FPW; ++c) {
+        if (c < nmine) {
+            const int fr = f0 + c;
+            if constexpr (W == MOE_INT4_G128) {
+                uint32_t wb[NM][16];
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    int4_word_to_bf16(wreg[c][m][0].x, &wb[m][0]);
+                    int4_word_to_bf16(wreg[c][m][0].y, &wb[m][4]);
+                    int4_word_to_bf16(wreg[c][m][0].z, &wb[m][8]);
+                    int4_word_to_bf16(wreg[c][m][0].w, &wb[m][12]);
+                }
+#pragma unroll
+                for (int i = 0; i < NTG; ++i) {
+                    if (i < nt) {
+                        const uint16_t* xr = (const uint16_t*)(s_x + (size_t)i * row_bytes) + fr * 128 + 8 * q;
+                        float xs = 0.f, p[NM];
+#pragma unroll
+                        for (int m = 0; m < NM; ++m) p[m] = 0.f;
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            const uint4 xv = *(const uint4*)(xr + 32 * s);
+                            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                            for (int pp = 0; pp < 4; ++pp) {
+                                xs = dot2(kOnes, xw[pp], xs);
+#pragma unroll
+                                for (int m = 0; m < NM; ++m) p[m] = dot2(wb[m][4 * s + pp], xw[pp], p[m]);
+                            }
+                        }
+#pragma unroll
+                        for (int m = 0; m < NM; ++m)
+                            acc[i][m] = __builtin_fmaf(sc[c][m], __builtin_fmaf(-136.0f, xs, p[m]), acc[i][m]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NTG; ++i) {
+                    if (i < nt) {
+                        if constexpr (W == MOE_BF16) {
+                            const uint4 xv =
+                                *(const uint4*)((const uint16_t*)(s_x + (size_t)i * row_bytes) + fr * 32 + 8 * q);
+#pragma unroll
+                            for (int m = 0; m < NM; ++m) {
+                                float t = acc[i][m];
+                                t = dot2(wreg[c][m][0].x, xv.x, t);
+                                t = dot2(wreg[c][m][0].y, xv.y, t);
+                                t = dot2(wreg[c][m][0].z, xv.z, t);
+                                t = dot2(wreg[c][m][0].w, xv.w, t);
+                                acc[i][m] = t;
+                            }
+                        } else {  // f32 weights and activations
+                            const float* xr = (const float*)(s_x + (size_t)i * row_bytes) + fr * 32 + 8 * q;
+                            const float4 xa = *(const float4*)xr, xb = *(const float4*)(xr + 4);
+#pragma unroll
+                            for (int m = 0; m < NM; ++m) {
+                                float t = acc[i][m];
+                                const uint4 wa = wreg[c][m][0], wb2 = wreg[c][m][LV - 1];
+                                t = __builtin_fmaf(as_f32(wa.x), xa.x, t);
+                                t = __builtin_fmaf(as_f32(wa.y), xa.y, t);
+                                t = __builtin_fmaf(as_f32(wa.z), xa.z, t);
+                                t = __builtin_fmaf(as_f32(wa.w), xa.w, t);
+                                t = __builtin_fmaf(as_f32(wb2.x), xb.x, t);
+                                t = __builtin_fmaf(as_f32(wb2.y), xb.y, t);
+                                t = __builtin_fmaf(as_f32(wb2.z), xb.z, t);
+                                t = __builtin_fmaf(as_f32(wb2.w), xb.w, t);
+                                acc[i][m] = t;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace moe

@@ -77,9 +77,7 @@ moe_status moe_expert_ffn_grouped(const void* x, moe_dtype act, int T, int d, in
 
     moe_status r = ffn_mfma(a, act, w, st);
     if (r != MOE_EDTYPE) return r;
-    int grid_experts = (int)std::min<int64_t>(E, (int64_t)T * k) + has_shared;
-    MOE_CHECK(grid_experts <= 65535, MOE_ESHAPE, "moe_expert_ffn_grouped: too many experts for one launch");
-    return ffn_gemv(a, act, w, grid_experts, st);
+    return ffn_gemv(a, act, w, st);
 }
 
 }  // extern "C"

@@ -8,7 +8,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/moe.h"
+#include "moe.h"
 
 namespace moe {
 
@@ -62,6 +62,46 @@ __host__ __device__ inline uint16_t f32_to_bf16(float f) {
 }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---- cross-lane sums without LDS (gfx950) -------------------------------------------------------
+// Each returns v[lane] + v[lane ^ s] in every lane.  Floating-point addition is commutative, so the
+// two lanes of a pair hold identical bits afterwards, which the fixed-order reductions rely on.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float pair_sum1(float v) { return v + dpp_move<0xB1>(v); }  // quad_perm [1,0,3,2]
+__device__ __forceinline__ float pair_sum2(float v) { return v + dpp_move<0x4E>(v); }  // quad_perm [2,3,0,1]
+// lane i <-> 7-i within 8 lanes: the partner quad; valid when each quad is already uniform
+__device__ __forceinline__ float pair_sum4_uniform(float v) { return v + dpp_move<0x141>(v); }
+// lane i <-> 15-i within 16 lanes: the partner 8-lane group; valid when each group is uniform
+__device__ __forceinline__ float pair_sum8_uniform(float v) { return v + dpp_move<0x140>(v); }
+// v_permlane16/32_swap exchange rows of two registers.  Swapping v against a zero register
+// gives, in each result pair, v of a row and v of its partner row, so r0 + r1 is the pair sum in
+// the lanes that keep their own row: lanes 0-15 and 32-47 (stride 16), lanes 0-31 (stride 32).
+// (The two results are copied to scalars before reinterpreting: a bit cast applied directly to
+// a vector-element expression picked up element 0 for both.)
+__device__ __forceinline__ float pair_sum16_low(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), 0u, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    return as_f32(r0) + as_f32(r1);
+}
+__device__ __forceinline__ float pair_sum32_low(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), 0u, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    return as_f32(r0) + as_f32(r1);
+}
+// Sum of the four row quarters (lanes r, r+16, r+32, r+48), valid in lanes 0-15.
+__device__ __forceinline__ float quarter_sum_low(float v) { return pair_sum32_low(pair_sum16_low(v)); }
+// Pairwise sum of the 64 lane values, neighbours first (strides 1, 2, ..., 32), valid in
+// lanes 0-15: level m+1 of the tree adds the two level-m sums of adjacent 2^m-lane groups.
+__device__ __forceinline__ float wave_tree_sum(float v) {
+    v = pair_sum1(v);
+    v = pair_sum2(v);
+    v = pair_sum4_uniform(v);
+    v = pair_sum8_uniform(v);
+    return pair_sum32_low(pair_sum16_low(v));
+}
 
 constexpr int kWave = 64;
 

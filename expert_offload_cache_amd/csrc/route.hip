@@ -5,22 +5,22 @@
 // selected ids are reproducible bit for bit: 64 contiguous segments of d/64 elements, each
 // summed from +0 in ascending index, joined pairwise neighbours first, bias added last.
 //
-// Two logits kernels implement that one order:
-//   * few tokens (decode): one wave per (expert, group of 8 tokens); lane j owns segment j and
-//     the pairwise join is the xor butterfly with strides 1, 2, 4, ..., 32 (a + b == b + a, so
-//     every lane ends with the same bits);
+// Two logits paths implement that one order:
+//   * few tokens (decode): one wave per (token, expert); lane j owns segment j, and the pairwise
+//     join is a butterfly with strides 1, 2, 4, ..., 32 done in VALU (DPP and permlane swaps;
+//     a + b == b + a, so both lanes of a pair hold the same bits);
 //   * many tokens (prefill): an LDS-tiled VALU product, each thread owning 4 tokens x 4
 //     experts, running the segments one after another and joining segment sums with a
 //     binary-counter stack (the same neighbours-first tree).
-// The top-k kernel gives one wave to each token.
+// A second kernel selects and gates, one block per token.
+// Selection is by rank: expert e is chosen iff fewer than k experts beat it (larger logit, or
+// equal logit and lower id), and that count is its output position.
 #include <hip/hip_runtime.h>
 
 #include "moe_common.h"
 
 namespace moe {
 namespace {
-
-constexpr int kTokGroup = 8;
 
 // acc + a*b with two roundings (a*b exact for bf16 inputs, so a fused form gives the same bits)
 template <bool kBf16>
@@ -38,64 +38,6 @@ template <bool kBf16>
 __device__ __forceinline__ float load_elem(const void* base, size_t i) {
     if constexpr (kBf16) return bf16_to_f32(((const uint16_t*)base)[i]);
     else return ((const float*)base)[i];
-}
-
-// ---- decode logits: one wave per (expert, token group) --------------------------------------
-template <bool kBf16>
-__global__ __launch_bounds__(256) void route_logits_wave(const void* __restrict__ x,
-                                                          const void* __restrict__ w,
-                                                          const float* __restrict__ bias, int T,
-                                                          int d, int E, float* __restrict__ logits) {
-    const int lane = threadIdx.x & 63;
-    const long gw = (long)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-    const int e = (int)(gw % E);
-    const int t0 = (int)(gw / E) * kTokGroup;
-    if (t0 >= T) return;
-    const int nt = min(kTokGroup, T - t0);
-    const int S = d / 64;
-    const size_t seg = (size_t)lane * S;
-    float acc[kTokGroup];
-#pragma unroll
-    for (int t = 0; t < kTokGroup; ++t) acc[t] = 0.0f;
-
-    if (kBf16 && (S % 8) == 0) {
-        const uint4* wr = (const uint4*)((const uint16_t*)w + (size_t)e * d + seg);
-        for (int c = 0; c < S / 8; ++c) {
-            uint4 wv = wr[c];
-            float wf[8] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y),
-                           bf16_lo(wv.z), bf16_hi(wv.z), bf16_lo(wv.w), bf16_hi(wv.w)};
-#pragma unroll
-            for (int t = 0; t < kTokGroup; ++t) {
-                if (t < nt) {
-                    uint4 xv = ((const uint4*)((const uint16_t*)x + (size_t)(t0 + t) * d + seg))[c];
-                    float xf[8] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y),
-                                   bf16_lo(xv.z), bf16_hi(xv.z), bf16_lo(xv.w), bf16_hi(xv.w)};
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[t] = madd<true>(acc[t], xf[i], wf[i]);
-                }
-            }
-        }
-    } else {
-        for (int i = 0; i < S; ++i) {
-            float wf = load_elem<kBf16>(w, (size_t)e * d + seg + i);
-#pragma unroll
-            for (int t = 0; t < kTokGroup; ++t)
-                if (t < nt) acc[t] = madd<kBf16>(acc[t], load_elem<kBf16>(x, (size_t)(t0 + t) * d + seg + i), wf);
-        }
-    }
-    // neighbours-first pairwise join of the 64 segment sums
-#pragma unroll
-    for (int t = 0; t < kTokGroup; ++t) {
-#pragma unroll
-        for (int s = 1; s < 64; s <<= 1) acc[t] = acc[t] + __shfl_xor(acc[t], s, 64);
-    }
-    if (lane < nt) {
-        float v = acc[0];
-#pragma unroll
-        for (int t = 1; t < kTokGroup; ++t)
-            if (lane == t) v = acc[t];
-        logits[(size_t)(t0 + lane) * E + e] = bias ? v + bias[e] : v;
-    }
 }
 
 // ---- prefill logits: LDS tiles, 64 tokens x 64 experts per block ------------------------------
@@ -147,20 +89,23 @@ __global__ __launch_bounds__(256) void route_logits_tiled(const void* __restrict
             if (++seg_pos == S) {
                 // close segment seg_idx: binary-counter join (left sibling + right)
                 seg_pos = 0;
-                int n = seg_idx++;
+                const int n = seg_idx++;
+                bool carry = true;  // still joining upwards
 #pragma unroll
                 for (int lv = 0; lv < 6; ++lv) {
-                    if (n & (1 << lv)) {
+                    if (carry) {
+                        if (n & (1 << lv)) {
 #pragma unroll
-                        for (int a = 0; a < 4; ++a)
+                            for (int a = 0; a < 4; ++a)
 #pragma unroll
-                            for (int b = 0; b < 4; ++b) acc[a][b] = stk[lv][a][b] + acc[a][b];
-                    } else {
+                                for (int b = 0; b < 4; ++b) acc[a][b] = stk[lv][a][b] + acc[a][b];
+                        } else {
 #pragma unroll
-                        for (int a = 0; a < 4; ++a)
+                            for (int a = 0; a < 4; ++a)
 #pragma unroll
-                            for (int b = 0; b < 4; ++b) stk[lv][a][b] = acc[a][b];
-                        break;
+                                for (int b = 0; b < 4; ++b) stk[lv][a][b] = acc[a][b];
+                            carry = false;
+                        }
                     }
                 }
                 if (n != 63) {
@@ -186,78 +131,110 @@ __global__ __launch_bounds__(256) void route_logits_tiled(const void* __restrict
     }
 }
 
-// ---- top-k and gates: one wave per token -------------------------------------------------------
+// ---- top-k and gates: rank selection on one token's logits held in LDS ------------------------
+// rank(e) = number of experts that beat e (larger logit, or equal logit and lower id); the
+// selected experts are those with rank < k and rank is their output position, so every thread
+// finds its own answer without a chain of cross-lane reductions.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
 
+__device__ void select_and_gate(const float* s_logit, int E, int k, const int32_t* forced_row, int* s_sel,
+                                float* s_val, int32_t* idx_out, float* w_out) {
+    const int tid = threadIdx.x, nth = blockDim.x;
+    if (forced_row) {
+        for (int j = tid; j < k; j += nth) {
+            const int id = forced_row[j];
+            s_sel[j] = id;
+            s_val[j] = s_logit[min(max(id, 0), E - 1)];
+        }
+    } else {
+        for (int e = tid; e < E; e += nth) {
+            const float v = s_logit[e];
+            int r = 0;
+            int i = 0;
+            for (; i + 4 <= E; i += 4) {
+                const float4 o = *(const float4*)(s_logit + i);
+                r += better(o.x, i, v, e) + better(o.y, i + 1, v, e) + better(o.z, i + 2, v, e) +
+                     better(o.w, i + 3, v, e);
+            }
+            for (; i < E; ++i) r += better(s_logit[i], i, v, e);
+            if (r < k) {
+                s_sel[r] = e;
+                s_val[r] = v;
+            }
+        }
+    }
+    __syncthreads();
+    // gates: softmax over the selected logits in binary64, rounded once
+    for (int j = tid; j < k; j += nth) {
+        double m = -INFINITY;
+        for (int i = 0; i < k; ++i) m = fmax(m, (double)s_val[i]);
+        double den = 0.0;
+        for (int i = 0; i < k; ++i) den += exp((double)s_val[i] - m);
+        idx_out[j] = s_sel[j];
+        w_out[j] = (float)(exp((double)s_val[j] - m) / den);
+    }
+}
+
+// prefill: one block per token, logits already in global memory
 __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logits, int T, int E, int k,
                                                   const int32_t* __restrict__ forced,
                                                   int32_t* __restrict__ topk_idx,
                                                   float* __restrict__ topk_w) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const float* row = logits + (size_t)t * E;
-    __shared__ float sel_v_all[4][1024];
-    __shared__ int sel_i_all[4][1024];
-    float* sel_v = sel_v_all[threadIdx.x >> 6];
-    int* sel_i = sel_i_all[threadIdx.x >> 6];
+    __shared__ __align__(16) float s_logit[1024];
+    __shared__ int s_sel[1024];
+    __shared__ float s_val[1024];
+    const int t = blockIdx.x;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) s_logit[e] = logits[(size_t)t * E + e];
+    __syncthreads();
+    select_and_gate(s_logit, E, k, forced ? forced + (size_t)t * k : nullptr, s_sel, s_val,
+                    topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
+}
 
-    if (forced) {
-        for (int j = lane; j < k; j += 64) {
-            int id = forced[(size_t)t * k + j];
-            int safe = min(max(id, 0), E - 1);
-            sel_i[j] = id;
-            sel_v[j] = row[safe];
+// decode: one wave per (token, expert); lane j owns segment j of the row, issues all of its
+// loads first, sums its segment in ascending index, and the wave joins the 64 segment sums with
+// the neighbours-first butterfly.
+template <bool kBf16>
+__global__ __launch_bounds__(256) void route_logits_wave(const void* __restrict__ x, const void* __restrict__ w,
+                                                         const float* __restrict__ bias, int T, int d, int E,
+                                                         float* __restrict__ logits) {
+    const int lane = threadIdx.x & 63;
+    const long g = (long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (g >= (long)T * E) return;
+    const int t = (int)(g / E), e = (int)(g - (long)t * E);
+    const int S = d / 64;
+    const size_t seg = (size_t)lane * S;
+    float acc = 0.f;
+    if (kBf16 && S % 8 == 0 && S <= 128) {
+        const uint4* xr = (const uint4*)((const uint16_t*)x + (size_t)t * d + seg);
+        const uint4* wr = (const uint4*)((const uint16_t*)w + (size_t)e * d + seg);
+        const int nv = S / 8;
+        uint4 xv[16], wv[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            xv[c] = (c < nv) ? xr[c] : make_uint4(0, 0, 0, 0);
+            wv[c] = (c < nv) ? wr[c] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            if (c < nv) {
+                const uint32_t xs[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
+                const uint32_t ws[4] = {wv[c].x, wv[c].y, wv[c].z, wv[c].w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    acc = madd<true>(acc, bf16_lo(xs[h]), bf16_lo(ws[h]));
+                    acc = madd<true>(acc, bf16_hi(xs[h]), bf16_hi(ws[h]));
+                }
+            }
         }
     } else {
-        float v[16];
-        unsigned taken = 0;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            int e = lane + 64 * m;
-            v[m] = (e < E) ? row[e] : 0.f;
-            if (e >= E) taken |= 1u << m;
-        }
-        for (int j = 0; j < k; ++j) {
-            float bv = 0.f;
-            int bi = 0x7FFFFFFF;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                int e = lane + 64 * m;
-                if (!(taken & (1u << m)) && (bi == 0x7FFFFFFF || better(v[m], e, bv, bi))) {
-                    bv = v[m];
-                    bi = e;
-                }
-            }
-#pragma unroll
-            for (int s = 32; s >= 1; s >>= 1) {
-                float ov = __shfl_xor(bv, s, 64);
-                int oi = __shfl_xor(bi, s, 64);
-                if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || better(ov, oi, bv, bi))) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
-            if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-            if (lane == 0) {
-                sel_i[j] = bi;
-                sel_v[j] = bv;
-            }
-        }
+        for (int i = 0; i < S; ++i)
+            acc = madd<kBf16>(acc, load_elem<kBf16>(x, (size_t)t * d + seg + i),
+                              load_elem<kBf16>(w, (size_t)e * d + seg + i));
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    // gates: softmax over the selected logits in binary64, rounded once
-    double m = -INFINITY;
-    for (int j = 0; j < k; ++j) m = fmax(m, (double)sel_v[j]);
-    double den = 0.0;
-    for (int j = 0; j < k; ++j) den += exp((double)sel_v[j] - m);
-    for (int j = lane; j < k; j += 64) {
-        topk_idx[(size_t)t * k + j] = sel_i[j];
-        topk_w[(size_t)t * k + j] = (float)(exp((double)sel_v[j] - m) / den);
-    }
+    acc = wave_tree_sum(acc);
+    if (lane == 0) logits[(size_t)t * E + e] = bias ? acc + bias[e] : acc;
 }
 
 }  // namespace
@@ -277,14 +254,11 @@ extern "C" moe_status moe_route(const void* x, moe_dtype act, int T, int d, cons
     MOE_CHECK(T <= (1 << 24), MOE_ESHAPE, "moe_route: T=%d too large", T);
     hipStream_t st = (hipStream_t)s;
     const bool bf = act == MOE_BF16;
-    const int S = d / 64;
-    const bool vec_ok = !bf || (S % 8 == 0 && ((uintptr_t)x % 16 == 0) && ((uintptr_t)w_router % 16 == 0));
-    if (T <= 64 || !vec_ok) {
-        long waves = (long)E * ((T + kTokGroup - 1) / kTokGroup);
-        dim3 grid((unsigned)((waves + 3) / 4));
+    if (T <= 64) {
+        const long waves = (long)T * E;
         ProfScope p("route_logits_wave", st);
-        if (bf) route_logits_wave<true><<<grid, 256, 0, st>>>(x, w_router, bias, T, d, E, logits);
-        else route_logits_wave<false><<<grid, 256, 0, st>>>(x, w_router, bias, T, d, E, logits);
+        if (bf) route_logits_wave<true><<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(x, w_router, bias, T, d, E, logits);
+        else route_logits_wave<false><<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(x, w_router, bias, T, d, E, logits);
     } else {
         dim3 grid((unsigned)((E + kTE - 1) / kTE), (unsigned)((T + kTT - 1) / kTT));
         ProfScope p("route_logits_tiled", st);
@@ -295,7 +269,7 @@ extern "C" moe_status moe_route(const void* x, moe_dtype act, int T, int d, cons
     if (r != MOE_OK) return r;
     {
         ProfScope p("route_topk", st);
-        route_topk<<<(T + 3) / 4, 256, 0, st>>>(logits, T, E, k, forced_idx, topk_idx, topk_w);
+        route_topk<<<T, 256, 0, st>>>(logits, T, E, k, forced_idx, topk_idx, topk_w);
     }
     return check_launch("route_topk");
 }

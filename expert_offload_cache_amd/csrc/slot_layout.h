@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 
 namespace moe {
 
