@@ -1,4 +1,4 @@
-// Device code shared by the grouped-GEMV kernels (one-shot and persistent).
+// Device code shared by the grouped expert kernels (GEMV and MFMA).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,6 +23,55 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// Work item a of the launch -> (expert, token chunk).  Expert e contributes ceil(n_e / ntg)
+// chunks, in ascending expert id; the shared expert's ceil(T / ntg) chunks come last (e = -1).
+// Returns false when a is past the last item.  Every lane of the calling wave agrees.
+__device__ __forceinline__ bool find_work(const int32_t* __restrict__ counts, int E, int T, int ntg, bool has_shared, int a,
+                          int& e_out, int& chunk_out) {
+    const int lane = threadIdx.x & 63;
+    const int per = (E + 63) / 64;
+    int nz = 0;
+    for (int i = 0; i < per; ++i) {
+        int e = lane * per + i;
+        if (e < E) nz += (counts[e] + ntg - 1) / ntg;
+    }
+    int incl = nz;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+        int v = __shfl_up(incl, s, 64);
+        if (lane >= s) incl += v;
+    }
+    const int total = __shfl(incl, 63, 64);
+    if (a >= total) {
+        const int c = a - total;
+        if (!has_shared || c >= (T + ntg - 1) / ntg) return false;
+        e_out = -1;
+        chunk_out = __builtin_amdgcn_readfirstlane(c);
+        return true;
+    }
+    const int excl = incl - nz;
+    int found = -1, chunk = 0;
+    if (a >= excl && a < incl) {
+        int r = a - excl;
+        for (int i = 0; i < per; ++i) {
+            int e = lane * per + i;
+            if (e >= E) break;
+            int ce = (counts[e] + ntg - 1) / ntg;
+            if (r < ce) {
+                found = e;
+                chunk = r;
+                break;
+            }
+            r -= ce;
+        }
+    }
+    const int src = (int)__builtin_ctzll(__ballot(found >= 0));
+    // wave-uniform results, so the caller's loops branch on scalars
+    e_out = __builtin_amdgcn_readfirstlane(__shfl(found, src, 64));
+    chunk_out = __builtin_amdgcn_readfirstlane(__shfl(chunk, src, 64));
+    return true;
+}
 
 template <int W>
 struct Frag;

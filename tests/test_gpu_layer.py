@@ -38,6 +38,10 @@ SMALL = [
     ("bf16", "bf16", 128, 64, 4, 4, 1, True),
     ("bf16", "int4", 256, 128, 8, 2, 5, True),
     ("bf16", "int4", 512, 256, 16, 4, 67, False),
+    # many tokens per expert: the MFMA grouped GEMM (several 128-token tiles, ragged tails)
+    ("bf16", "bf16", 256, 128, 6, 2, 300, True),
+    ("bf16", "bf16", 512, 384, 16, 4, 257, False),
+    ("bf16", "bf16", 256, 256, 3, 1, 1000, True),
 ]
 
 
@@ -72,7 +76,7 @@ def qwen_layer():
     gc.collect()
 
 
-@pytest.mark.parametrize("T", [1, 4, 16, 64])
+@pytest.mark.parametrize("T", [1, 4, 16, 64, 256])
 def test_qwen_a3b_decode_layer(qwen_layer, T):
     wl, li64, layer = qwen_layer
     print(f"qwen-a3b decode bf16 T={T}", flush=True)
@@ -102,12 +106,12 @@ def test_determinism_and_slot_order_invariance(qwen_layer):
     del layer2
 
 
-def test_absent_slot_is_flagged_not_read(qwen_layer):
+@pytest.mark.parametrize("T", [16, 256])
+def test_absent_slot_is_flagged_not_read(qwen_layer, T):
     import torch
     import expert_offload_cache_amd as moe
 
     wl, li, layer = qwen_layer
-    T = 16
     lt = synth.layer_inputs(wl, T, seed=0, with_experts=False)
     x = layer.x_to_device(lt.x)
     out = layer.forward(x)
