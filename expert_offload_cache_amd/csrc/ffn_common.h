@@ -9,7 +9,6 @@
 namespace moe {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // streaming 16-byte load (weights are read once per call)
 __device__ __forceinline__ uint4 load_stream(const void* p) {

@@ -9,15 +9,18 @@
 // l%16 and weight rows 4(l/16)..+3.
 //
 // Tiling: a workgroup of 8 waves (4 along weight rows x 2 along tokens) computes 256 weight
-// rows x 128 tokens of one expert; each wave owns 64 rows x 64 tokens = 16 MFMA tiles.  In the
+// rows x NT tokens of one expert (NT = 128 or 256); each wave owns 64 rows x NT/2 tokens.  In the
 // gate/up launch a wave's 64 rows are 32 gate rows and the same 32 up rows, so SwiGLU is
 // applied in registers before one bf16 store of h.  Inputs advance 64 at a time through a
 // double-buffered LDS stage: weights are copied fragment for fragment (the global layout is the
 // LDS layout), token rows are gathered through the permutation into a padded [token][input]
-// tile.  Workgroup (m, n) follows (m, n-1) sixteen blocks later in dispatch order, i.e. on the
-// same XCD (blocks go round-robin over 8), so an expert's weight tile is reused from that XCD's
-// L2 across its token tiles.
+// tile.  Global loads run two stages ahead of the MFMAs in registers.
+// Workgroup (m, n) follows (m, n-1) sixteen blocks later in dispatch order, i.e. on the same
+// XCD (blocks go round-robin over 8), so an expert's weight tile is reused from that XCD's L2
+// across its token tiles.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "ffn.h"
 #include "ffn_common.h"
@@ -29,36 +32,42 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMT = 256;           // weight rows per workgroup
-constexpr int kNT = 128;           // tokens per workgroup
-constexpr int kKT = 64;            // inputs per LDS stage (two fragments)
+constexpr int kMT = 256;             // weight rows per workgroup
+constexpr int kKT = 64;              // inputs per LDS stage (two fragments)
 constexpr int kBRow = kKT * 2 + 16;  // padded LDS row of one token (bytes)
-constexpr int kAStage = kMT * kKT * 2;       // 32 KB
-constexpr int kBStage = kNT * kBRow;         // 18 KB
-constexpr int kStage = kAStage + kBStage;
-constexpr int kLds = 2 * kStage;             // 100 KB
+constexpr int kAStage = kMT * kKT * 2;  // 32 KB
 
-__device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
+template <int NT>
+struct Tile {
+    static constexpr int kNTW = NT / 32;           // 16-token blocks per wave
+    static constexpr int kBV = NT * 8 / 512;       // B vectors per thread per stage
+    static constexpr int kBStage = NT * kBRow;
+    static constexpr int kStage = kAStage + kBStage;
+    static constexpr int kLds = 2 * kStage;        // 100 KB (NT 128) or 136 KB (NT 256)
+};
+
+__device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                    0, 0, 0);
 }
 
-// Token tile n of expert item a -> same scheme as the GEMV work items (kNT tokens per chunk).
-template <int MODE>
+template <int MODE, int NT>
 __global__ __launch_bounds__(512) void ffn_mfma_kernel(FfnArgs a) {
+    using TL = Tile<NT>;
+    constexpr int NTW = TL::kNTW, BV = TL::kBV;
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv & 3, wn = wv >> 2;  // wave position: 4 along rows, 2 along tokens
     const int K = (MODE == kGateUp) ? a.d : a.f;
-    const int nkb = K / 32;  // fragments along the inputs
+    const int nks = K / kKT;  // stages (even)
 
     int e, chunk;
-    if (!find_work(a.counts, a.E, a.T, kNT, a.shared_w != nullptr, blockIdx.y, e, chunk)) return;
+    if (!find_work(a.counts, a.E, a.T, NT, a.shared_w != nullptr, blockIdx.y, e, chunk)) return;
     const bool shared = e == -1;
     const int n_all = __builtin_amdgcn_readfirstlane(shared ? a.T : a.counts[e]);
-    const int t0 = chunk * kNT;
-    const int nt = __builtin_amdgcn_readfirstlane(min(kNT, n_all - t0));
+    const int t0 = chunk * NT;
+    const int nt = __builtin_amdgcn_readfirstlane(min(NT, n_all - t0));
     const int p0 = __builtin_amdgcn_readfirstlane(shared ? a.T * a.k : a.offsets[e]);
     const uint8_t* base;
     if (shared) {
@@ -81,108 +90,110 @@ __global__ __launch_bounds__(512) void ffn_mfma_kernel(FfnArgs a) {
         base = a.pool + (size_t)slot * a.stride;
     }
 
-    // 16 row blocks of this workgroup: gate/up -> f blocks mb*8 .. +7, gate and up interleaved
-    // as (g0, u0, g1, u1, ...); down -> d blocks mb*16 .. +15
-    auto rowblock_src = [&](int j) -> const uint8_t* {
-        if constexpr (MODE == kGateUp) {
-            const int fb = blockIdx.x * 8 + (j >> 1);
-            return base + gu_block_offset(fb, j & 1, a.d, MOE_BF16);
-        } else {
-            return base + down_block_offset(blockIdx.x * 16 + j, a.d, a.f, MOE_BF16);
-        }
-    };
-
-    // token rows staged by this thread: 8 threads cover one token's 64 inputs (128 contiguous
-    // bytes), so thread tid stages inputs 8*(tid&7)..+7 of tokens (tid>>3) and 64+(tid>>3)
-    const int seg = tid & 7;
-    const uint8_t* tok_row[2];
-    bool tok_ok[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int tok = (tid >> 3) + u * 64;
-        tok_ok[u] = tok < nt;
-        int src = 0;
-        if (tok_ok[u]) {
-            if (MODE == kGateUp) src = shared ? (t0 + tok) : (a.perm[p0 + t0 + tok] / a.k);
-            else src = p0 + t0 + tok;
-        }
-        tok_row[u] = ((MODE == kGateUp) ? (const uint8_t*)a.x : (const uint8_t*)a.h) + (size_t)src * K * 2 +
-                     (size_t)seg * 16;
+    // A source of this thread: 16 row blocks x 2 fragments per stage = 2048 vectors, 4 per
+    // thread; vector v = tid + 512u is row block (tid>>7) + 4u (gate/up: g0,u0,g1,u1,...; down:
+    // d blocks), bytes 16*(tid&127) of its two fragments.  In both launches the row block's byte
+    // offset is linear in the block index, so the four sources are one pointer and a stride.
+    const size_t rbb = rowblock_bytes(K, MOE_BF16);
+    const uint8_t* a_src;
+    {
+        const int j = tid >> 7;
+        if constexpr (MODE == kGateUp) a_src = base + gu_block_offset(blockIdx.x * 8 + (j >> 1), j & 1, a.d, MOE_BF16);
+        else a_src = base + down_block_offset(blockIdx.x * 16 + j, a.d, a.f, MOE_BF16);
+        a_src += (size_t)(tid & 127) * 16;
     }
+    // B source: 8 threads cover one token's 64 inputs of a stage (128 contiguous bytes); thread
+    // tid stages inputs 8*(tid&7)..+7 of tokens (tid>>3) + 64u.  Tokens past the tile's end read
+    // the tile's first row instead: MFMA columns are independent and those columns are never
+    // stored.  Row offsets fit 32 bits (activation and h buffers are far below 4 GiB).
+    const int seg = tid & 7;
+    const uint8_t* b_base = (MODE == kGateUp) ? (const uint8_t*)a.x : (const uint8_t*)a.h;
+    uint32_t b_off[BV];
+#pragma unroll
+    for (int u = 0; u < BV; ++u) {
+        int tok = (tid >> 3) + u * 64;
+        tok = tok < nt ? tok : 0;
+        int src;
+        if (MODE == kGateUp) src = shared ? (t0 + tok) : (a.perm[p0 + t0 + tok] / a.k);
+        else src = p0 + t0 + tok;
+        b_off[u] = (uint32_t)src * (uint32_t)(K * 2) + (uint32_t)seg * 16;
+    }
+    const uint32_t s_off = (uint32_t)(tid >> 3) * kBRow + seg * 16;  // LDS B slot of u = 0
 
-    // global -> registers for one stage: A = 16 row blocks x 2 fragments (32 KB, 4 vectors per
-    // thread, the same byte order in LDS as in the slot); B = 128 tokens x 64 inputs (2 vectors)
-    uint4 ra[4], rbv[2];
-    auto gload = [&](int ks) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int v = tid + u * 512;              // 16-byte vector index in the A stage
-            const int j = v >> 7, within = v & 127;   // row block, vector inside its 2 KB
-            ra[u] = *(const uint4*)(rowblock_src(j) + (size_t)ks * 2048 + (size_t)within * 16);
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            rbv[u] = tok_ok[u] ? *(const uint4*)(tok_row[u] + (size_t)ks * kKT * 2) : make_uint4(0, 0, 0, 0);
-    };
-    auto sstore = [&](int buf) {
-        uint8_t* sa = smem + buf * kStage;
-        uint8_t* sb = sa + kAStage;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) *(uint4*)(sa + (size_t)(tid + u * 512) * 16) = ra[u];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) *(uint4*)(sb + ((tid >> 3) + u * 64) * kBRow + seg * 16) = rbv[u];
-    };
-
-    f32x4_t acc[4][4];  // [row block of the wave][token block of the wave]
+    f32x4_t acc[4][NTW];  // [row block of the wave][token block of the wave]
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NTW; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-    const int nks = nkb / 2;  // stages
-    gload(0);
-    sstore(0);
+    u32x4_t pa[4], pb[BV], qa[4], qb[BV];  // native vectors: registers, never memory
+#define MFMA_GLOAD(KS, RA, RB)                                                                         \
+    do {                                                                                               \
+        const int ks_ = (KS);                                                                          \
+        _Pragma("unroll") for (int u = 0; u < 4; ++u) RA[u] =                                          \
+            *(const u32x4_t*)(a_src + (size_t)u * 4 * rbb + (size_t)ks_ * 2048);                         \
+        _Pragma("unroll") for (int u = 0; u < BV; ++u) RB[u] =                                         \
+            *(const u32x4_t*)(b_base + b_off[u] + (size_t)ks_ * (kKT * 2));                              \
+        __builtin_amdgcn_sched_barrier(0); /* issue here, ahead of the MFMAs */                        \
+    } while (0)
+#define MFMA_SSTORE(BUF, RA, RB)                                                                       \
+    do {                                                                                               \
+        uint8_t* sa_ = smem + (BUF) * TL::kStage;                                                      \
+        _Pragma("unroll") for (int u = 0; u < 4; ++u) *(u32x4_t*)(sa_ + (size_t)(tid + u * 512) * 16) = RA[u]; \
+        _Pragma("unroll") for (int u = 0; u < BV; ++u) *(u32x4_t*)(sa_ + kAStage + s_off + u * 64 * kBRow) = RB[u]; \
+    } while (0)
+#define MFMA_COMPUTE(BUF)                                                                              \
+    do {                                                                                               \
+        const uint8_t* sa_ = smem + (BUF) * TL::kStage;                                                \
+        const uint8_t* sb_ = sa_ + kAStage;                                                            \
+        _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                             \
+            u32x4_t av[4];                                                                               \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i) av[i] =                                      \
+                *(const u32x4_t*)(sa_ + ((wm * 4 + i) * 2 + kk) * 1024 + lane * 16);                     \
+            _Pragma("unroll") for (int j = 0; j < NTW; ++j) {                                          \
+                const int tok = (wn * NTW + j) * 16 + (lane & 15);                                     \
+                const u32x4_t bv = *(const u32x4_t*)(sb_ + tok * kBRow + (kk * 32 + 8 * (lane >> 4)) * 2); \
+                _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i][j] = mfma(av[i], bv, acc[i][j]);  \
+            }                                                                                          \
+        }                                                                                              \
+    } while (0)
+
+    // stages ks and ks+1 per trip; the last two stages are peeled so that the loop body has no
+    // branch (a conditional store there makes the back edge wait for every load in flight)
+    MFMA_GLOAD(0, pa, pb);
+    MFMA_GLOAD(1, qa, qb);
+    MFMA_SSTORE(0, pa, pb);
     __syncthreads();
-    for (int ks = 0; ks < nks; ++ks) {
-        const int buf = ks & 1;
-        if (ks + 1 < nks) gload(ks + 1);  // next stage in flight during the MFMAs
-        const uint8_t* sa = smem + buf * kStage;
-        const uint8_t* sb = sa + kAStage;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {  // two 32-input steps per stage
-            uint4 av[4], bv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)  // wave's row blocks: wm*4 + i
-                av[i] = *(const uint4*)(sa + ((size_t)(wm * 4 + i) * 2 + kk) * 1024 + lane * 16);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {  // wave's token blocks: wn*4 + j
-                const int tok = (wn * 4 + j) * 16 + (lane & 15);
-                bv[j] = *(const uint4*)(sb + tok * kBRow + (kk * 32 + 8 * (lane >> 4)) * 2);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma(av[i], bv[j], acc[i][j]);
-        }
-        if (ks + 1 < nks) {
-            sstore(buf ^ 1);
-            __syncthreads();
-        }
+    for (int ks = 0; ks < nks - 2; ks += 2) {
+        MFMA_GLOAD(ks + 2, pa, pb);
+        MFMA_COMPUTE(0);
+        MFMA_SSTORE(1, qa, qb);
+        __syncthreads();
+        MFMA_GLOAD(ks + 3, qa, qb);
+        MFMA_COMPUTE(1);
+        MFMA_SSTORE(0, pa, pb);
+        __syncthreads();
     }
+    MFMA_COMPUTE(0);
+    MFMA_SSTORE(1, qa, qb);
+    __syncthreads();
+    MFMA_COMPUTE(1);
+#undef MFMA_GLOAD
+#undef MFMA_SSTORE
+#undef MFMA_COMPUTE
 
     // ---- epilogue --------------------------------------------------------------------------
     const int quad = lane >> 4;  // C rows 4*quad .. +3 of each 16-row tile
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int tok = (wn * 4 + j) * 16 + (lane & 15);
+    for (int j = 0; j < NTW; ++j) {
+        const int tok = (wn * NTW + j) * 16 + (lane & 15);
         if (tok >= nt) continue;
         const size_t row = (size_t)(p0 + t0 + tok);
         if constexpr (MODE == kGateUp) {
 #pragma unroll
             for (int i2 = 0; i2 < 2; ++i2) {  // wave row blocks (g, u) pairs: (i2*2, i2*2+1)
                 const f32x4_t g = acc[2 * i2][j], u = acc[2 * i2 + 1][j];
-                const int fb = blockIdx.x * 8 + (wm * 4 + 2 * i2) / 2;
-                const int col = fb * 16 + quad * 4;
+                const int col = (blockIdx.x * 8 + wm * 2 + i2) * 16 + quad * 4;
                 uint2 o;
                 o.x = (uint32_t)f32_to_bf16(silu_mul(g[0], u[0])) | ((uint32_t)f32_to_bf16(silu_mul(g[1], u[1])) << 16);
                 o.y = (uint32_t)f32_to_bf16(silu_mul(g[2], u[2])) | ((uint32_t)f32_to_bf16(silu_mul(g[3], u[3])) << 16);
@@ -198,17 +209,17 @@ __global__ __launch_bounds__(512) void ffn_mfma_kernel(FfnArgs a) {
     }
 }
 
-template <int MODE>
+template <int MODE, int NT>
 moe_status launch(const FfnArgs& a, hipStream_t st, const char* name) {
     const int M = (MODE == kGateUp) ? 2 * a.f : a.d;  // weight rows (gate and up together)
     const int64_t tk = (int64_t)a.T * a.k;
-    const int64_t items = (tk + kNT - 1) / kNT + std::min<int64_t>(a.E, tk) + (a.shared_w ? (a.T + kNT - 1) / kNT : 0);
+    const int64_t items = (tk + NT - 1) / NT + std::min<int64_t>(a.E, tk) + (a.shared_w ? (a.T + NT - 1) / NT : 0);
     if (items > 65535) return set_error(MOE_ESHAPE, "%s: %lld token tiles exceed one launch", name, (long long)items);
-    auto kern = ffn_mfma_kernel<MODE>;
-    MOE_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds));
+    auto kern = ffn_mfma_kernel<MODE, NT>;
+    MOE_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Tile<NT>::kLds));
     dim3 grid((unsigned)(M / kMT), (unsigned)items);
     ProfScope p(name, st);
-    kern<<<grid, 512, kLds, st>>>(a);
+    kern<<<grid, 512, Tile<NT>::kLds, st>>>(a);
     return check_launch(name);
 }
 
@@ -217,10 +228,10 @@ moe_status launch(const FfnArgs& a, hipStream_t st, const char* name) {
 // Many tokens per expert and bf16: the MFMA path.  Other cases report MOE_EDTYPE ("not mine").
 moe_status ffn_mfma(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st) {
     if (act != MOE_BF16 || w != MOE_BF16 || a.T <= 64) return MOE_EDTYPE;
-    if ((2 * a.f) % kMT || a.d % kMT || a.d % kKT || a.f % kKT) return MOE_EDTYPE;
-    moe_status r = launch<kGateUp>(a, st, "ffn_mfma_gateup_bf16");
+    if ((2 * a.f) % kMT || a.d % kMT || a.d % (2 * kKT) || a.f % (2 * kKT)) return MOE_EDTYPE;
+    moe_status r = launch<kGateUp, 128>(a, st, "ffn_mfma_gateup_bf16");
     if (r != MOE_OK) return r;
-    return launch<kDown>(a, st, "ffn_mfma_down_bf16");
+    return launch<kDown, 128>(a, st, "ffn_mfma_down_bf16");
 }
 
 }  // namespace moe

@@ -47,6 +47,8 @@ struct ProfScope {
 };
 
 // ---- number formats ----------------------------------------------------------------------------
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // native vector: stays in registers
+
 __host__ __device__ inline float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 __host__ __device__ inline uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
 __host__ __device__ inline float bf16_lo(uint32_t w) { return as_f32(w << 16); }

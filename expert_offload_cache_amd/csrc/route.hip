@@ -9,9 +9,12 @@
 //   * few tokens (decode): one wave per (token, expert); lane j owns segment j, and the pairwise
 //     join is a butterfly with strides 1, 2, 4, ..., 32 done in VALU (DPP and permlane swaps;
 //     a + b == b + a, so both lanes of a pair hold the same bits);
-//   * many tokens (prefill): an LDS-tiled VALU product, each thread owning 4 tokens x 4
-//     experts, running the segments one after another and joining segment sums with a
-//     binary-counter stack (the same neighbours-first tree).
+//   * many tokens (prefill), bf16 with d a multiple of 2048: 32 tokens x 32 experts per block;
+//     each of the four waves owns one quarter of the inputs, i.e. 16 consecutive segments = one
+//     depth-4 subtree of the join, which it runs segment after segment with a binary-counter
+//     stack; the four subtree roots are then joined (0+1)+(2+3) through LDS;
+//   * other prefill shapes: an LDS-tiled VALU product, each thread owning 4 tokens x 4
+//     experts, running all 64 segments with a 6-level binary-counter stack.
 // A second kernel selects and gates, one block per token.
 // Selection is by rank: expert e is chosen iff fewer than k experts beat it (larger logit, or
 // equal logit and lower id), and that count is its output position.
@@ -54,7 +57,7 @@ __global__ __launch_bounds__(256) void route_logits_tiled(const void* __restrict
     __shared__ float ws[kKT][kTE + 4];
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;  // tx -> experts, ty -> tokens
-    const int tb = blockIdx.y * kTT, eb = blockIdx.x * kTE;
+    const int tb = blockIdx.x * kTT, eb = blockIdx.y * kTE;
     const int S = d / 64;
 
     float acc[4][4], stk[6][4][4];
@@ -128,6 +131,141 @@ __global__ __launch_bounds__(256) void route_logits_tiled(const void* __restrict
             int e = eb + tx * 4 + b;
             if (e < E) logits[(size_t)t * E + e] = bias ? acc[a][b] + bias[e] : acc[a][b];
         }
+    }
+}
+
+// ---- prefill logits, bf16, d % 2048 == 0: four waves split the inputs by subtree -----------------
+// Block (bx, by): tokens 32*bx .. +31, experts 32*by .. +31.  Lane (tx = l&7, ty = l>>3) owns
+// tokens ty + 8a and experts tx + 8b (a, b < 4).  Inputs move in chunks of 32 per wave: global
+// 16-byte loads (the next chunk's are issued before the current chunk is multiplied), widened to
+// binary32 once while staged, then read back as float4 so one LDS read serves four steps.
+constexpr int kSplitRow = 36;  // padded LDS row (floats): the 8 rows one read touches hit distinct banks
+
+__device__ __forceinline__ void widen_store(float* dst, u32x4_t v) {
+    float4 lo = make_float4(as_f32(v.x << 16), as_f32(v.x & 0xFFFF0000u), as_f32(v.y << 16), as_f32(v.y & 0xFFFF0000u));
+    float4 hi = make_float4(as_f32(v.z << 16), as_f32(v.z & 0xFFFF0000u), as_f32(v.w << 16), as_f32(v.w & 0xFFFF0000u));
+    *(float4*)dst = lo;
+    *(float4*)(dst + 4) = hi;
+}
+
+__global__ __launch_bounds__(256) void route_logits_split(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ w,
+                                                          const float* __restrict__ bias, int T, int d,
+                                                          int E, float* __restrict__ logits) {
+    __shared__ __align__(16) float lds[4][2][32][kSplitRow];  // per wave: x rows, w rows
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tx = lane & 7, ty = lane >> 3;
+    const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+    const int quarter = d / 4, nch = quarter / 32, cps = d / 64 / 32;  // chunks; chunks per segment
+
+    // staging: vectors v = lane + 64u (u < 2) -> row v>>2, inputs 8*(v&3)..+7 of the chunk
+    const uint16_t* xsrc[2];
+    const uint16_t* wsrc[2];
+    int srow[2], spart[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int v = lane + 64 * u;
+        srow[u] = v >> 2;
+        spart[u] = v & 3;
+        const int t = min(t0 + srow[u], T - 1), e = min(e0 + srow[u], E - 1);  // tails: any valid row
+        xsrc[u] = x + (size_t)t * d + wv * quarter + spart[u] * 8;
+        wsrc[u] = w + (size_t)e * d + wv * quarter + spart[u] * 8;
+    }
+    float(*xs)[kSplitRow] = lds[wv][0];
+    float(*ws)[kSplitRow] = lds[wv][1];
+
+    u32x4_t gx[2], gw[2];
+    auto gload = [&](int ch) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            gx[u] = *(const u32x4_t*)(xsrc[u] + ch * 32);
+            gw[u] = *(const u32x4_t*)(wsrc[u] + ch * 32);
+        }
+    };
+    auto sstore = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            widen_store(&xs[srow[u]][spart[u] * 8], gx[u]);
+            widen_store(&ws[srow[u]][spart[u] * 8], gw[u]);
+        }
+    };
+
+    float acc[4][4], stk[4][4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
+
+    gload(0);
+    sstore();
+    __syncthreads();
+    for (int ch = 0; ch < nch; ++ch) {
+        gload(min(ch + 1, nch - 1));
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            float4 xv[4], wq[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) xv[a] = *(const float4*)&xs[ty + 8 * a][4 * g];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) wq[b] = *(const float4*)&ws[tx + 8 * b][4 * g];
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    float s = acc[a][b];
+                    s = madd<true>(s, xv[a].x, wq[b].x);
+                    s = madd<true>(s, xv[a].y, wq[b].y);
+                    s = madd<true>(s, xv[a].z, wq[b].z);
+                    s = madd<true>(s, xv[a].w, wq[b].w);
+                    acc[a][b] = s;
+                }
+        }
+        if ((ch + 1) % cps == 0) {
+            // close local segment n (0..15): binary-counter join, left sibling + right
+            const int n = (ch + 1) / cps - 1;
+            bool carry = true;
+#pragma unroll
+            for (int lv = 0; lv < 4; ++lv) {
+                if (carry) {
+                    if (n & (1 << lv)) {
+#pragma unroll
+                        for (int a = 0; a < 4; ++a)
+#pragma unroll
+                            for (int b = 0; b < 4; ++b) acc[a][b] = stk[lv][a][b] + acc[a][b];
+                    } else {
+#pragma unroll
+                        for (int a = 0; a < 4; ++a)
+#pragma unroll
+                            for (int b = 0; b < 4; ++b) stk[lv][a][b] = acc[a][b];
+                        carry = false;
+                    }
+                }
+            }
+            if (n != 15) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
+            }
+        }
+        __syncthreads();
+        sstore();
+        __syncthreads();
+    }
+    // acc = this wave's subtree root.  Join the four: (q0 + q1) + (q2 + q3), then the bias.
+    float* part = &lds[0][0][0][0];  // [4 waves][32 tokens][32 experts], staging no longer needed
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) part[(wv * 32 + ty + 8 * a) * 32 + tx + 8 * b] = acc[a][b];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int o = tid + 256 * i, tl = o >> 5, el = o & 31;
+        const int t = t0 + tl, e = e0 + el;
+        const float l = (part[o] + part[1024 + o]) + (part[2048 + o] + part[3072 + o]);
+        if (t < T && e < E) logits[(size_t)t * E + e] = bias ? l + bias[e] : l;
     }
 }
 
@@ -259,8 +397,12 @@ extern "C" moe_status moe_route(const void* x, moe_dtype act, int T, int d, cons
         ProfScope p("route_logits_wave", st);
         if (bf) route_logits_wave<true><<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(x, w_router, bias, T, d, E, logits);
         else route_logits_wave<false><<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(x, w_router, bias, T, d, E, logits);
+    } else if (bf && d % 2048 == 0 && (((uintptr_t)x | (uintptr_t)w_router) & 15) == 0) {
+        dim3 grid((unsigned)((T + 31) / 32), (unsigned)((E + 31) / 32));
+        ProfScope p("route_logits_split", st);
+        route_logits_split<<<grid, 256, 0, st>>>((const uint16_t*)x, (const uint16_t*)w_router, bias, T, d, E, logits);
     } else {
-        dim3 grid((unsigned)((E + kTE - 1) / kTE), (unsigned)((T + kTT - 1) / kTT));
+        dim3 grid((unsigned)((T + kTT - 1) / kTT), (unsigned)((E + kTE - 1) / kTE));
         ProfScope p("route_logits_tiled", st);
         if (bf) route_logits_tiled<true><<<grid, 256, 0, st>>>(x, w_router, bias, T, d, E, logits);
         else route_logits_tiled<false><<<grid, 256, 0, st>>>(x, w_router, bias, T, d, E, logits);

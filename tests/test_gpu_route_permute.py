@@ -29,6 +29,9 @@ ROUTE_CASES = [
     ("bf16", 4096, 256, 6, 8192, 1.1),
     ("bf16", 1024, 1024, 8, 70, None),    # maximum expert count
     ("bf16", 512, 100, 100, 9, 1.1),      # k = E, ragged E
+    ("bf16", 2048, 128, 8, 100, 1.1),     # subtree-split prefill kernel, ragged tokens
+    ("bf16", 2048, 100, 4, 97, None),     # ... ragged experts, no bias
+    ("bf16", 6144, 96, 4, 130, 1.1),      # ... three chunks per segment
 ]
 
 
