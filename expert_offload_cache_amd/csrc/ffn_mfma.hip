@@ -11,10 +11,11 @@
 // Tiling: a workgroup of 8 waves (4 along weight rows x 2 along tokens) computes 256 weight
 // rows x NT tokens of one expert (NT = 128 or 256); each wave owns 64 rows x NT/2 tokens.  In the
 // gate/up launch a wave's 64 rows are 32 gate rows and the same 32 up rows, so SwiGLU is
-// applied in registers before one bf16 store of h.  Inputs advance 64 at a time through a
-// double-buffered LDS stage: weights are copied fragment for fragment (the global layout is the
-// LDS layout), token rows are gathered through the permutation into a padded [token][input]
-// tile.  Global loads run two stages ahead of the MFMAs in registers.
+// applied in registers before one bf16 store of h.  Inputs advance 32 at a time through a ring
+// of LDS stages filled by direct-to-LDS loads (global_load_lds_dwordx4), several stages ahead of
+// the MFMAs and without passing through registers: weights are copied fragment for fragment (the
+// slot layout is the LDS layout), and token rows are gathered through the permutation straight
+// into B fragments, so every LDS read of the MFMA loop is a conflict-free 16-byte lane read.
 // Workgroup (m, n) follows (m, n-1) sixteen blocks later in dispatch order, i.e. on the same
 // XCD (blocks go round-robin over 8), so an expert's weight tile is reused from that XCD's L2
 // across its token tiles.
@@ -31,19 +32,26 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
-constexpr int kMT = 256;             // weight rows per workgroup
-constexpr int kKT = 64;              // inputs per LDS stage (two fragments)
-constexpr int kBRow = kKT * 2 + 16;  // padded LDS row of one token (bytes)
-constexpr int kAStage = kMT * kKT * 2;  // 32 KB
+constexpr int kKT = 32;  // inputs per stage (one fragment)
 
-template <int NT>
+// MT weight rows x NT tokens per workgroup; 8 waves as WM (rows) x 8/WM (tokens); R stages of the
+// ring in LDS.  Each stage holds the MT/16 row blocks' fragments, then the NT/16 token fragments.
+template <int MT, int NT, int WM, int R>
 struct Tile {
-    static constexpr int kNTW = NT / 32;           // 16-token blocks per wave
-    static constexpr int kBV = NT * 8 / 512;       // B vectors per thread per stage
-    static constexpr int kBStage = NT * kBRow;
-    static constexpr int kStage = kAStage + kBStage;
-    static constexpr int kLds = 2 * kStage;        // 100 KB (NT 128) or 136 KB (NT 256)
+    static constexpr int kWN = 8 / WM;
+    static constexpr int kRA = MT / 16 / WM;             // row blocks per wave
+    static constexpr int kRB = NT / 16 / kWN;            // token blocks per wave
+    static constexpr int kLA = MT / 128;                 // row-block fragments each wave loads per stage
+    static constexpr int kLB = NT / 128;                 // token fragments each wave loads per stage
+    static constexpr int kAStage = MT * kKT * 2;
+    static constexpr int kStage = kAStage + NT * kKT * 2;
+    static constexpr int kRing = R;
+    static constexpr int kLds = R * kStage;
+    static constexpr int kLoads = kLA + kLB;             // direct-to-LDS loads per wave per stage
+    static_assert(kRA % 2 == 0 && kRA * WM * 16 == MT && kRB * kWN * 16 == NT && R >= 3, "tile shape");
 };
 
 __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
@@ -51,16 +59,34 @@ __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                    0, 0, 0);
 }
 
-template <int MODE, int NT>
+// Wait until at most N of this wave's direct-to-LDS loads are in flight and its LDS reads are
+// done, then meet the other waves.  After it, the stage whose loads were issued before the last
+// N has landed for the whole workgroup, and no wave still reads the buffer the next loads fill.
+// The empty asm statements keep the compiler from moving LDS accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));  // vmcnt(N) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void load_to_lds(const uint8_t* src, uint8_t* lds_wave_base) {
+    // 16 bytes per lane; lane i's bytes land at lds_wave_base + 16 i whatever its source address
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)lds_wave_base, 16, 0, 0);
+}
+
+template <int MODE, int MT, int NT, int WM, int R>
 __global__ __launch_bounds__(512) void ffn_mfma_kernel(FfnArgs a) {
-    using TL = Tile<NT>;
-    constexpr int NTW = TL::kNTW, BV = TL::kBV;
+    using TL = Tile<MT, NT, WM, R>;
+    constexpr int RA = TL::kRA, RB = TL::kRB, LA = TL::kLA, LB = TL::kLB;
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wv & 3, wn = wv >> 2;  // wave position: 4 along rows, 2 along tokens
+    const int wm = wv % WM, wn = wv / WM;  // wave position along rows, along tokens
     const int K = (MODE == kGateUp) ? a.d : a.f;
-    const int nks = K / kKT;  // stages (even)
+    const int nks = K / kKT;  // stages
 
     int e, chunk;
     if (!find_work(a.counts, a.E, a.T, NT, a.shared_w != nullptr, blockIdx.y, e, chunk)) return;
@@ -77,8 +103,8 @@ __global__ __launch_bounds__(512) void ffn_mfma_kernel(FfnArgs a) {
         if (slot < 0 || slot >= a.n_slots) {
             if (tid == 0) *a.status = 1;
             // zeros for this tile's outputs; nothing is read from the pool
-            const int rows0 = (MODE == kGateUp) ? blockIdx.x * (kMT / 2) : blockIdx.x * kMT;
-            const int nr = (MODE == kGateUp) ? kMT / 2 : kMT;
+            const int rows0 = (MODE == kGateUp) ? blockIdx.x * (MT / 2) : blockIdx.x * MT;
+            const int nr = (MODE == kGateUp) ? MT / 2 : MT;
             for (int i = tid; i < nt * nr; i += blockDim.x) {
                 const size_t row = (size_t)(p0 + t0 + i / nr);
                 const int col = rows0 + i % nr;
@@ -90,110 +116,80 @@ __global__ __launch_bounds__(512) void ffn_mfma_kernel(FfnArgs a) {
         base = a.pool + (size_t)slot * a.stride;
     }
 
-    // A source of this thread: 16 row blocks x 2 fragments per stage = 2048 vectors, 4 per
-    // thread; vector v = tid + 512u is row block (tid>>7) + 4u (gate/up: g0,u0,g1,u1,...; down:
-    // d blocks), bytes 16*(tid&127) of its two fragments.  In both launches the row block's byte
-    // offset is linear in the block index, so the four sources are one pointer and a stride.
-    const size_t rbb = rowblock_bytes(K, MOE_BF16);
-    const uint8_t* a_src;
+    // Stage buffer layout (both operands in fragment order, 1 KB per fragment, lane l's 16 bytes
+    // at 16 l): A = the MT/16 row blocks (gate/up: g0,u0,g1,u1,...; down: d blocks), then B = the
+    // NT/16 token blocks.  Wave w fills row blocks LA*w .. +LA-1 and token blocks LB*w .. +LB-1.
+    const uint8_t* a_src[LA];
+#pragma unroll
+    for (int u = 0; u < LA; ++u) {
+        const int j = LA * wv + u;
+        if constexpr (MODE == kGateUp) a_src[u] = base + gu_block_offset(blockIdx.x * (MT / 32) + (j >> 1), j & 1, a.d, MOE_BF16);
+        else a_src[u] = base + down_block_offset(blockIdx.x * (MT / 16) + j, a.d, a.f, MOE_BF16);
+        a_src[u] += lane * 16;
+    }
+    // B fragment lane l: token 16 tb + l%16, inputs 8(l/16)..+7 of the stage.  Tokens past the
+    // tile's end read the tile's first row: MFMA columns are independent and are never stored.
+    const uint8_t* b_src[LB];
     {
-        const int j = tid >> 7;
-        if constexpr (MODE == kGateUp) a_src = base + gu_block_offset(blockIdx.x * 8 + (j >> 1), j & 1, a.d, MOE_BF16);
-        else a_src = base + down_block_offset(blockIdx.x * 16 + j, a.d, a.f, MOE_BF16);
-        a_src += (size_t)(tid & 127) * 16;
-    }
-    // B source: 8 threads cover one token's 64 inputs of a stage (128 contiguous bytes); thread
-    // tid stages inputs 8*(tid&7)..+7 of tokens (tid>>3) + 64u.  Tokens past the tile's end read
-    // the tile's first row instead: MFMA columns are independent and those columns are never
-    // stored.  Row offsets fit 32 bits (activation and h buffers are far below 4 GiB).
-    const int seg = tid & 7;
-    const uint8_t* b_base = (MODE == kGateUp) ? (const uint8_t*)a.x : (const uint8_t*)a.h;
-    uint32_t b_off[BV];
+        const uint8_t* b_base = (MODE == kGateUp) ? (const uint8_t*)a.x : (const uint8_t*)a.h;
 #pragma unroll
-    for (int u = 0; u < BV; ++u) {
-        int tok = (tid >> 3) + u * 64;
-        tok = tok < nt ? tok : 0;
-        int src;
-        if (MODE == kGateUp) src = shared ? (t0 + tok) : (a.perm[p0 + t0 + tok] / a.k);
-        else src = p0 + t0 + tok;
-        b_off[u] = (uint32_t)src * (uint32_t)(K * 2) + (uint32_t)seg * 16;
+        for (int u = 0; u < LB; ++u) {
+            int tok = (LB * wv + u) * 16 + (lane & 15);
+            tok = tok < nt ? tok : 0;
+            int src;
+            if (MODE == kGateUp) src = shared ? (t0 + tok) : (a.perm[p0 + t0 + tok] / a.k);
+            else src = p0 + t0 + tok;
+            b_src[u] = b_base + (size_t)src * K * 2 + (lane >> 4) * 16;
+        }
     }
-    const uint32_t s_off = (uint32_t)(tid >> 3) * kBRow + seg * 16;  // LDS B slot of u = 0
-
-    f32x4_t acc[4][NTW];  // [row block of the wave][token block of the wave]
+    auto issue = [&](int ks) __attribute__((always_inline)) {
+        ks = min(ks, nks - 1);  // past the end: reload the last stage into a buffer nobody reads
+        uint8_t* buf = smem + (ks % R) * TL::kStage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int u = 0; u < LA; ++u) load_to_lds(a_src[u] + (size_t)ks * 1024, buf + (LA * wv + u) * 1024);
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < LB; ++u)
+            load_to_lds(b_src[u] + (size_t)ks * (kKT * 2), buf + TL::kAStage + (LB * wv + u) * 1024);
+    };
 
-    u32x4_t pa[4], pb[BV], qa[4], qb[BV];  // native vectors: registers, never memory
-#define MFMA_GLOAD(KS, RA, RB)                                                                         \
-    do {                                                                                               \
-        const int ks_ = (KS);                                                                          \
-        _Pragma("unroll") for (int u = 0; u < 4; ++u) RA[u] =                                          \
-            *(const u32x4_t*)(a_src + (size_t)u * 4 * rbb + (size_t)ks_ * 2048);                         \
-        _Pragma("unroll") for (int u = 0; u < BV; ++u) RB[u] =                                         \
-            *(const u32x4_t*)(b_base + b_off[u] + (size_t)ks_ * (kKT * 2));                              \
-        __builtin_amdgcn_sched_barrier(0); /* issue here, ahead of the MFMAs */                        \
-    } while (0)
-#define MFMA_SSTORE(BUF, RA, RB)                                                                       \
-    do {                                                                                               \
-        uint8_t* sa_ = smem + (BUF) * TL::kStage;                                                      \
-        _Pragma("unroll") for (int u = 0; u < 4; ++u) *(u32x4_t*)(sa_ + (size_t)(tid + u * 512) * 16) = RA[u]; \
-        _Pragma("unroll") for (int u = 0; u < BV; ++u) *(u32x4_t*)(sa_ + kAStage + s_off + u * 64 * kBRow) = RB[u]; \
-    } while (0)
-#define MFMA_COMPUTE(BUF)                                                                              \
-    do {                                                                                               \
-        const uint8_t* sa_ = smem + (BUF) * TL::kStage;                                                \
-        const uint8_t* sb_ = sa_ + kAStage;                                                            \
-        _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                             \
-            u32x4_t av[4];                                                                               \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i) av[i] =                                      \
-                *(const u32x4_t*)(sa_ + ((wm * 4 + i) * 2 + kk) * 1024 + lane * 16);                     \
-            _Pragma("unroll") for (int j = 0; j < NTW; ++j) {                                          \
-                const int tok = (wn * NTW + j) * 16 + (lane & 15);                                     \
-                const u32x4_t bv = *(const u32x4_t*)(sb_ + tok * kBRow + (kk * 32 + 8 * (lane >> 4)) * 2); \
-                _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i][j] = mfma(av[i], bv, acc[i][j]);  \
-            }                                                                                          \
-        }                                                                                              \
-    } while (0)
+    f32x4_t acc[RA][RB];  // [row block of the wave][token block of the wave]
+#pragma unroll
+    for (int i = 0; i < RA; ++i)
+#pragma unroll
+        for (int j = 0; j < RB; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-    // stages ks and ks+1 per trip; the last two stages are peeled so that the loop body has no
-    // branch (a conditional store there makes the back edge wait for every load in flight)
-    MFMA_GLOAD(0, pa, pb);
-    MFMA_GLOAD(1, qa, qb);
-    MFMA_SSTORE(0, pa, pb);
-    __syncthreads();
-    for (int ks = 0; ks < nks - 2; ks += 2) {
-        MFMA_GLOAD(ks + 2, pa, pb);
-        MFMA_COMPUTE(0);
-        MFMA_SSTORE(1, qa, qb);
-        __syncthreads();
-        MFMA_GLOAD(ks + 3, qa, qb);
-        MFMA_COMPUTE(1);
-        MFMA_SSTORE(0, pa, pb);
-        __syncthreads();
+    // R-1 stages in flight ahead of the one being multiplied; past the last stage the loads
+    // repeat the last stage (branch-free, so every wait count stays exact)
+#pragma unroll
+    for (int s = 0; s < R - 1; ++s) issue(s);
+    for (int ks = 0; ks < nks; ++ks) {
+        stage_barrier<(R - 2) * TL::kLoads>();  // stage ks landed; buffer (ks-1)%R is free
+        issue(ks + R - 1);
+        const uint8_t* sa = smem + (ks % R) * TL::kStage;
+        u32x4_t av[RA], bv[RB];
+#pragma unroll
+        for (int i = 0; i < RA; ++i) av[i] = *(const u32x4_t*)(sa + (wm * RA + i) * 1024 + lane * 16);
+#pragma unroll
+        for (int j = 0; j < RB; ++j) bv[j] = *(const u32x4_t*)(sa + TL::kAStage + (wn * RB + j) * 1024 + lane * 16);
+#pragma unroll
+        for (int j = 0; j < RB; ++j)
+#pragma unroll
+            for (int i = 0; i < RA; ++i) acc[i][j] = mfma(av[i], bv[j], acc[i][j]);
     }
-    MFMA_COMPUTE(0);
-    MFMA_SSTORE(1, qa, qb);
-    __syncthreads();
-    MFMA_COMPUTE(1);
-#undef MFMA_GLOAD
-#undef MFMA_SSTORE
-#undef MFMA_COMPUTE
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));  // drain the tail reloads (vmcnt(0))
 
     // ---- epilogue --------------------------------------------------------------------------
     const int quad = lane >> 4;  // C rows 4*quad .. +3 of each 16-row tile
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-        const int tok = (wn * NTW + j) * 16 + (lane & 15);
+    for (int j = 0; j < RB; ++j) {
+        const int tok = (wn * RB + j) * 16 + (lane & 15);
         if (tok >= nt) continue;
         const size_t row = (size_t)(p0 + t0 + tok);
         if constexpr (MODE == kGateUp) {
 #pragma unroll
-            for (int i2 = 0; i2 < 2; ++i2) {  // wave row blocks (g, u) pairs: (i2*2, i2*2+1)
+            for (int i2 = 0; i2 < RA / 2; ++i2) {  // wave row blocks (g, u) pairs: (2 i2, 2 i2 + 1)
                 const f32x4_t g = acc[2 * i2][j], u = acc[2 * i2 + 1][j];
-                const int col = (blockIdx.x * 8 + wm * 2 + i2) * 16 + quad * 4;
+                const int col = (blockIdx.x * (MT / 32) + (wm * RA) / 2 + i2) * 16 + quad * 4;
                 uint2 o;
                 o.x = (uint32_t)f32_to_bf16(silu_mul(g[0], u[0])) | ((uint32_t)f32_to_bf16(silu_mul(g[1], u[1])) << 16);
                 o.y = (uint32_t)f32_to_bf16(silu_mul(g[2], u[2])) | ((uint32_t)f32_to_bf16(silu_mul(g[3], u[3])) << 16);
@@ -201,37 +197,52 @@ __global__ __launch_bounds__(512) void ffn_mfma_kernel(FfnArgs a) {
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int col = (blockIdx.x * 16 + wm * 4 + i) * 16 + quad * 4;
+            for (int i = 0; i < RA; ++i) {
+                const int col = (blockIdx.x * (MT / 16) + wm * RA + i) * 16 + quad * 4;
                 *(float4*)(a.y_perm + row * a.d + col) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
             }
         }
     }
 }
 
-template <int MODE, int NT>
+template <int MODE, int MT, int NT, int WM, int R>
 moe_status launch(const FfnArgs& a, hipStream_t st, const char* name) {
+    using TL = Tile<MT, NT, WM, R>;
     const int M = (MODE == kGateUp) ? 2 * a.f : a.d;  // weight rows (gate and up together)
     const int64_t tk = (int64_t)a.T * a.k;
     const int64_t items = (tk + NT - 1) / NT + std::min<int64_t>(a.E, tk) + (a.shared_w ? (a.T + NT - 1) / NT : 0);
     if (items > 65535) return set_error(MOE_ESHAPE, "%s: %lld token tiles exceed one launch", name, (long long)items);
-    auto kern = ffn_mfma_kernel<MODE, NT>;
-    MOE_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Tile<NT>::kLds));
-    dim3 grid((unsigned)(M / kMT), (unsigned)items);
+    auto kern = ffn_mfma_kernel<MODE, MT, NT, WM, R>;
+    MOE_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, TL::kLds));
+    dim3 grid((unsigned)(M / MT), (unsigned)items);
     ProfScope p(name, st);
-    kern<<<grid, 512, Tile<NT>::kLds, st>>>(a);
+    kern<<<grid, 512, TL::kLds, st>>>(a);
     return check_launch(name);
 }
 
 }  // namespace
 
+#ifndef MOE_MFMA_MT
+#define MOE_MFMA_MT 512
+#endif
+#ifndef MOE_MFMA_NT
+#define MOE_MFMA_NT 128
+#endif
+#ifndef MOE_MFMA_WM
+#define MOE_MFMA_WM 8
+#endif
+#ifndef MOE_MFMA_R
+#define MOE_MFMA_R 3
+#endif
+
 // Many tokens per expert and bf16: the MFMA path.  Other cases report MOE_EDTYPE ("not mine").
 moe_status ffn_mfma(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st) {
+    constexpr int MT = MOE_MFMA_MT, NT = MOE_MFMA_NT, WM = MOE_MFMA_WM, R = MOE_MFMA_R;
     if (act != MOE_BF16 || w != MOE_BF16 || a.T <= 64) return MOE_EDTYPE;
-    if ((2 * a.f) % kMT || a.d % kMT || a.d % (2 * kKT) || a.f % (2 * kKT)) return MOE_EDTYPE;
-    moe_status r = launch<kGateUp, 128>(a, st, "ffn_mfma_gateup_bf16");
+    if ((2 * a.f) % MT || a.d % MT) return MOE_EDTYPE;
+    moe_status r = launch<kGateUp, MT, NT, WM, R>(a, st, "ffn_mfma_gateup_bf16");
     if (r != MOE_OK) return r;
-    return launch<kDown, 128>(a, st, "ffn_mfma_down_bf16");
+    return launch<kDown, MT, NT, WM, R>(a, st, "ffn_mfma_down_bf16");
 }
 
 }  // namespace moe

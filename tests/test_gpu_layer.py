@@ -42,6 +42,9 @@ SMALL = [
     ("bf16", "bf16", 256, 128, 6, 2, 300, True),
     ("bf16", "bf16", 512, 384, 16, 4, 257, False),
     ("bf16", "bf16", 256, 256, 3, 1, 1000, True),
+    ("bf16", "bf16", 512, 256, 6, 2, 300, True),
+    ("bf16", "bf16", 1024, 768, 16, 4, 257, False),
+    ("bf16", "bf16", 512, 512, 3, 1, 1000, True),
 ]
 
 
