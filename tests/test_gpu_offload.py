@@ -1,0 +1,128 @@
+"""Offloaded stack on the GPU: pinned host pool -> LRU slot cache -> layer kernels, against the
+oracle (layer outputs) and the oracle's LRU simulator (hit/miss sequence, miss counts).
+
+Small int4 stack: 4 layers of E=8 experts (top-2, d=256, d_ff=128, shared expert), 16 distinct
+expert images; a 40-token prefill that prefetches each next layer, then a 25-step decode trace.
+"""
+import gc
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import need_gpu, rel_err_per_token, small_workload, y_to_f64
+from oracle.layer import moe_layer, moe_layer_tokens
+from oracle.lru import LRUSim
+
+pytestmark = pytest.mark.gpu
+
+L, E, K, D, F = 4, 8, 2, 256, 128
+T_PRE, STEPS, IMAGES = 40, 25, 16
+
+
+def _wl():
+    return small_workload("bf16", "int4", D, F, E, K, shared=True, bias=1.1)
+
+
+def _trace():
+    return synth.routing_trace(seed=3, steps=STEPS, L=L, E=E, k=K)
+
+
+def _layer_weights(stack, wl, l):
+    experts = []
+    for e in range(E):
+        i = stack.image_of(l, e)
+        experts.append(synth.expert_weights(wl, 0, i // E, i % E))
+    shared = synth.expert_weights(wl, 0, stack.shared_layer_of(l), 0, shared=True)
+    return experts, shared
+
+
+def _expected(trace, C):
+    """Simulator replay of the same request sequence -> (hit flags, [(slot, key)] of every copy)."""
+    sim = LRUSim(C)
+    flags, copies = [], []
+    reqs = [(l, list(range(E)), "prefill") for l in range(L)]
+    reqs += [(l, np.unique(trace[s, l]).tolist(), "decode") for s in range(STEPS) for l in range(L)]
+    for l, ids, phase in reqs:
+        slots, fl, _ = sim.request(l, ids, phase=phase)
+        flags += fl
+        copies += [(sl, l * E + e) for e, sl, h in zip(sorted(ids), slots, fl) if not h]
+    return np.array(flags, dtype=np.uint8), copies
+
+
+def _run(C):
+    from expert_offload_cache_amd.offload import OffloadStack
+
+    wl = _wl()
+    stack = OffloadStack(wl, L, C, seed=0, n_images=IMAGES, prefill_tokens=T_PRE)
+    _, pre = stack.prefill(keep_outputs=True)
+    _, dec = stack.decode(_trace(), keep_outputs=True)
+    res = dict(pre=[(i.cpu().numpy(), y_to_f64(y)) for i, y in pre], dec=[(s, l, y_to_f64(y)) for s, l, y in dec],
+               trace=stack.cache.trace(), stats=stack.cache.stats(), stack=stack)
+    return wl, res
+
+
+@pytest.fixture(scope="module")
+def runs():
+    need_gpu()
+    out = {}
+    for C in (16, 20, 32):
+        print(f"offload stack L={L} E={E} C={C}", flush=True)
+        out[C] = _run(C)
+    yield out
+    for _, r in out.values():
+        r["stack"].close()
+    gc.collect()
+
+
+@pytest.mark.parametrize("C", [16, 20, 32])
+def test_hit_miss_sequence_matches_simulator(runs, C):
+    _, r = runs[C]
+    want, copies = _expected(_trace(), C)
+    assert np.array_equal(r["trace"], want)
+    log = r["stack"].cache.copy_log()
+    assert [(int(a), int(b)) for a, b in log[:, :2]] == copies
+    st = r["stats"]
+    n_dec = STEPS * L * K
+    assert st["dec_acc"] == n_dec and st["pre_acc"] == L * E
+    assert st["dec_miss"] == int((want[L * E:] == 0).sum())
+    assert st["bytes_h2d"] == int((want == 0).sum()) * r["stack"].stride
+
+
+def test_decode_outputs_match_oracle(runs):
+    wl, r = runs[20]
+    stack, trace = r["stack"], _trace()
+    per_layer = {l: _layer_weights(stack, wl, l) for l in range(L)}
+    worst = 0.0
+    for s, l, y in r["dec"]:
+        li = synth.layer_inputs(wl, 8, 0, layer=l, batch=1, with_experts=False)
+        x = li.x[s % 8:s % 8 + 1]
+        experts, shared = per_layer[l]
+        ref = moe_layer(x, li.w_router, li.bias, "bf16", K, E, experts, shared, forced_idx=trace[s, l:l + 1])
+        worst = max(worst, float(rel_err_per_token(y, ref["y"]).max()))
+    print(f"decode max per-token rel err {worst:.3g}")
+    assert worst <= 2e-2
+
+
+def test_prefill_outputs_match_oracle(runs):
+    wl, r = runs[20]
+    stack = r["stack"]
+    for l, (idx, y) in enumerate(r["pre"]):
+        li = synth.layer_inputs(wl, T_PRE, 0, layer=l, batch=0, with_experts=False)
+        experts, shared = _layer_weights(stack, wl, l)
+        toks = [0, 7, T_PRE // 2, T_PRE - 1]
+        ref = moe_layer_tokens(toks, li.x, li.w_router, li.bias, "bf16", K, E, experts, shared)
+        assert np.array_equal(idx[toks], ref["topk_idx"])
+        err = rel_err_per_token(y[toks], ref["y"])
+        assert err.max() <= 2e-2, (l, err)
+
+
+def test_outputs_do_not_depend_on_capacity(runs):
+    """Cache capacity changes which copies happen, never the layer outputs (bitwise)."""
+    ref = runs[32][1]
+    for C in (16, 20):
+        r = runs[C][1]
+        for (s0, l0, y0), (s1, l1, y1) in zip(ref["dec"], r["dec"]):
+            assert (s0, l0) == (s1, l1) and np.array_equal(y0, y1)
+        for (i0, y0), (i1, y1) in zip(ref["pre"], r["pre"]):
+            assert np.array_equal(i0, i1) and np.array_equal(y0, y1)
