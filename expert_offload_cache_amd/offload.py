@@ -26,51 +26,34 @@ from .layer import _expert_arrays, _to_device
 
 
 class OffloadStack:
-    """L stacked MoE layers whose routed experts live in a pinned host pool behind an LRU slot cache."""
+    """L stacked MoE layers whose routed experts live in a pinned host pool behind an LRU slot cache.
+
+    Every device buffer is allocated before the pool is pinned: on the hosts this runs on, device
+    allocations made after a large pinned allocation can be refused."""
 
     def __init__(self, wl, n_layers: int, n_slots: int, seed: int = 0, n_images: Optional[int] = None,
-                 x_bank: int = 8, prefill_tokens: int = 0, device="cuda", log=None):
+                 x_bank: int = 8, prefill_tokens: int = 0, device="cuda", log=None, slot_pool=None,
+                 min_layers: Optional[int] = None):
         import torch
         import synth
 
         self.wl, self.L, self.E, self.k, self.d, self.f = wl, n_layers, wl.E, wl.k, wl.d, wl.f
         self.seed, self.device, self.log = seed, device, log or (lambda *a: None)
         self.stride = slot_bytes(wl.d, wl.f, wl.wdt)
-        L, E = self.L, self.E
+        L, E, k, d = self.L, self.E, self.k, self.d
         self.n_images = int(n_images or E)
         self.act_code = MOE_BF16 if wl.act == "bf16" else MOE_F32
-
-        # distinct routed images, packed once
-        t0 = time.perf_counter()
-        imgs = np.empty((self.n_images, self.stride), dtype=np.uint8)
-        for i in range(self.n_images):
-            ew = synth.expert_weights(wl, seed, i // E, i % E)
-            pack_expert(wl.wdt, wl.d, wl.f, *_expert_arrays(ew), out=imgs[i])
-        self.log(f"packed {self.n_images} expert images in {time.perf_counter() - t0:.1f} s")
-
-        # pinned host pool, one stride per key
-        t0 = time.perf_counter()
-        self.pool_bytes = L * E * self.stride
-        self.pinned = pinned_alloc(self.pool_bytes)
-        try:
-            view = np.ctypeslib.as_array((ctypes.c_uint8 * self.pool_bytes).from_address(self.pinned))
-            for key in range(L * E):
-                view[key * self.stride:(key + 1) * self.stride] = imgs[key % self.n_images]
-            del view
-        except Exception:
-            pinned_free(self.pinned)
-            raise
-        self.log(f"pinned pool {self.pool_bytes / 2**30:.1f} GiB filled in {time.perf_counter() - t0:.1f} s")
-        del imgs
-        host_ptrs = [self.pinned + key * self.stride for key in range(L * E)]
-
-        # HBM slots and the slot table the kernels read
         self.n_slots = int(n_slots)
-        self.slot_pool = torch.empty(self.n_slots * self.stride, dtype=torch.uint8, device=device)
-        self.slot_table = torch.empty(L * E, dtype=torch.int32, device=device)
-        self.cache = SlotCache(L, E, self.n_slots, self.stride, self.slot_pool, self.slot_table, host_ptrs)
+        self.pinned = []
+        self.cache = None
 
-        # resident per-layer state: router, bias, shared expert, activation banks
+        # ---- device memory: slots, slot table, per-layer state, call buffers ----
+        if slot_pool is None:
+            slot_pool = torch.empty(self.n_slots * self.stride, dtype=torch.uint8, device=device)
+        if slot_pool.numel() < self.n_slots * self.stride:
+            raise ValueError("slot_pool is smaller than n_slots * slot stride")
+        self.slot_pool = slot_pool
+        self.slot_table = torch.empty(L * E, dtype=torch.int32, device=device)
         self.w_router, self.bias, self.shared, self.x_dec, self.x_pre = [], [], [], [], []
         for l in range(L):
             li = synth.layer_inputs(wl, x_bank, seed, layer=l, batch=1, with_experts=False)
@@ -85,11 +68,64 @@ class OffloadStack:
             if prefill_tokens:
                 xp = synth.layer_inputs(wl, prefill_tokens, seed, layer=l, batch=0, with_experts=False).x
                 self.x_pre.append(_to_device(xp, wl.act, device))
+        self._ws = {}
+        self._bufs = {}
+        for T in ({1, prefill_tokens} - {0}):
+            self._workspace(T)
+            self._buffers(T)
         self.compute = torch.cuda.Stream(device=device)
         self.copy = torch.cuda.Stream(device=device)
-        self._ws = {}
+        self._host_idx = torch.empty((1, k), dtype=torch.int32, pin_memory=True)
+
+        # ---- distinct routed images, packed once ----
+        t0 = time.perf_counter()
+        imgs = np.empty((self.n_images, self.stride), dtype=np.uint8)
+        for i in range(self.n_images):
+            ew = synth.expert_weights(wl, seed, i // E, i % E)
+            pack_expert(wl.wdt, wl.d, wl.f, *_expert_arrays(ew), out=imgs[i])
+        self.log(f"packed {self.n_images} expert images in {time.perf_counter() - t0:.1f} s")
+
+        # ---- pinned host pool: one stride per key, one block (a refused attempt pins nothing) ----
+        t0 = time.perf_counter()
+        self.layer_bytes = E * self.stride
+        try:
+            self.pinned = [pinned_alloc(L * self.layer_bytes)]
+        except MoeError as err:
+            if min_layers is None or min_layers >= L:
+                raise
+            self.log(f"pinning {L} layers failed ({err}); running {min_layers} layers")
+            self.L = L = min_layers
+            self.pinned = [pinned_alloc(L * self.layer_bytes)]
+            for lst in (self.w_router, self.bias, self.shared, self.x_dec, self.x_pre):
+                del lst[L:]
+        view = np.ctypeslib.as_array((ctypes.c_uint8 * (L * self.layer_bytes)).from_address(self.pinned[0]))
+        for key in range(L * E):
+            view[key * self.stride:(key + 1) * self.stride] = imgs[self.image_of(key // E, key % E)]
+        del view, imgs
+        self.pool_bytes = L * self.layer_bytes
+        self.log(f"pinned pool {self.pool_bytes / 2**30:.1f} GiB filled in {time.perf_counter() - t0:.1f} s")
+        self.new_cache(self.n_slots)
 
     # ------------------------------------------------------------------------------------------
+    def new_cache(self, n_slots: int):
+        """A fresh, empty LRU cache of n_slots slots over this stack's pool and slot memory."""
+        if n_slots * self.stride > self.slot_pool.numel():
+            raise ValueError("not enough slot memory")
+        if self.cache is not None:
+            self.cache.close()
+        self.n_slots = int(n_slots)
+        self.cache = SlotCache(self.L, self.E, self.n_slots, self.stride, self.slot_pool, self.slot_table,
+                               self.host_ptrs())
+
+    def host_ptrs(self):
+        """Pinned address of every key (layer * E + expert)."""
+        return [self.pinned[0] + key * self.stride for key in range(self.L * self.E)]
+
+    def _free_pinned(self):
+        for p in self.pinned:
+            pinned_free(p)
+        self.pinned = []
+
     def image_of(self, layer: int, expert: int) -> int:
         """Image held by key (layer, expert); image i is synth.expert_weights(wl, seed, i // E, i % E)."""
         return (layer * self.E + expert) % self.n_images
@@ -106,36 +142,61 @@ class OffloadStack:
             self._ws[T] = torch.zeros(n, dtype=torch.uint8, device=self.device)
         return self._ws[T]
 
-    def _layer_kernels(self, l: int, x, idx, w, counts, offsets, perm, inv, y=None, y_perm=None):
+    def _buffers(self, T: int):
+        """Outputs of route, permute, the grouped experts and the combine for a T-token call."""
+        import torch
+
+        if T not in self._bufs:
+            dev, k, E, d = self.device, self.k, self.E, self.d
+            rows = T * k + (T if self.wl.shared else 0)
+            self._bufs[T] = dict(
+                route=(torch.empty((T, k), dtype=torch.int32, device=dev),
+                       torch.empty((T, k), dtype=torch.float32, device=dev),
+                       torch.empty((T, E), dtype=torch.float32, device=dev)),
+                perm=(torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
+                      torch.empty(T * k, dtype=torch.int32, device=dev),
+                      torch.empty(T * k, dtype=torch.int32, device=dev)),
+                y_perm=torch.empty((rows, d), dtype=torch.float32, device=dev),
+                y=torch.empty((T, d), dtype=torch.bfloat16 if self.wl.act == "bf16" else torch.float32, device=dev))
+        return self._bufs[T]
+
+    def _layer(self, l: int, x, forced=None):
+        """One layer on the compute stream up to the grouped experts' inputs: route + permute."""
+        T = x.shape[0]
+        b = self._buffers(T)
+        idx, w, _ = route(x, self.w_router[l], self.bias[l], self.k, forced_idx=forced, out=b["route"],
+                          stream=self.compute)
+        perm = permute(idx, self.E, out=b["perm"], stream=self.compute)
+        return idx, w, perm
+
+    def _experts(self, l: int, x, w, perm):
         """Grouped experts through layer l's slot-table row, then the combine (compute stream)."""
-        E = self.E
+        T, E = x.shape[0], self.E
+        b = self._buffers(T)
+        counts, offsets, p, inv = perm
         table = self.slot_table[l * E:(l + 1) * E]
-        y_perm, _ = expert_ffn_grouped(x, perm, offsets, counts, table, self.slot_pool, self.n_slots, self.stride,
-                                       self.wl.wdt, self.f, self.k, shared_w=self.shared[l], y_perm=y_perm,
-                                       ws=self._workspace(x.shape[0]), stream=self.compute)
-        return combine(y_perm, w, inv, self.k, self.shared[l] is not None, x.dtype, y=y, stream=self.compute)
+        y_perm, _ = expert_ffn_grouped(x, p, offsets, counts, table, self.slot_pool, self.n_slots, self.stride,
+                                       self.wl.wdt, self.f, self.k, shared_w=self.shared[l], y_perm=b["y_perm"],
+                                       ws=self._workspace(T), stream=self.compute)
+        return combine(y_perm, w, inv, self.k, self.shared[l] is not None, x.dtype, y=b["y"], stream=self.compute)
 
     # ------------------------------------------------------------------------------------------
-    def prefill(self, T: Optional[int] = None, keep_outputs: bool = False):
-        """All L layers over the prefill batch; layer l+1's experts stream in while layer l computes.
-
-        Returns wall seconds (and the per-layer outputs when keep_outputs)."""
+    def prefill(self, keep_outputs: bool = False):
+        """All L layers over the prefill batch; layer l+1's experts stream in on the copy stream
+        while layer l computes.  Returns wall seconds (and per-layer (ids, y) when keep_outputs)."""
         import torch
 
         outs = []
-        T = T or self.x_pre[0].shape[0]
-        self._workspace(T)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         self.cache.prefetch_layer(0, self.copy, self.compute)
         with torch.cuda.stream(self.compute):
             for l in range(self.L):
-                x = self.x_pre[l][:T]
-                idx, w, _ = route(x, self.w_router[l], self.bias[l], self.k, stream=self.compute)
-                counts, offsets, perm, inv = permute(idx, self.E, stream=self.compute)
-                y = self._layer_kernels(l, x, idx, w, counts, offsets, perm, inv)
+                x = self.x_pre[l]
+                idx, w, perm = self._layer(l, x)
+                y = self._experts(l, x, w, perm)
                 if keep_outputs:
-                    outs.append((idx, y))
+                    outs.append((idx.clone(), y.clone()))
                 if l + 1 < self.L:
                     self.cache.prefetch_layer(l + 1, self.copy, self.compute)
                 self.cache.mark_read(l, self.compute)
@@ -152,17 +213,10 @@ class OffloadStack:
         import torch
 
         steps = steps or trace.shape[0]
-        L, E, k = self.L, self.E, self.k
-        forced = torch.from_numpy(np.ascontiguousarray(trace[:steps], dtype=np.int32)).to(self.device)
-        host_idx = torch.empty((1, k), dtype=torch.int32, pin_memory=True)
+        L = self.L
+        forced = self._forced(trace[:steps])
+        host_idx = self._host_idx
         done = torch.cuda.Event()
-        dev = self.device
-        rbuf = (torch.empty((1, k), dtype=torch.int32, device=dev), torch.empty((1, k), dtype=torch.float32, device=dev),
-                torch.empty((1, E), dtype=torch.float32, device=dev))
-        pbuf = (torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
-                torch.empty(k, dtype=torch.int32, device=dev), torch.empty(k, dtype=torch.int32, device=dev))
-        y_perm = torch.empty((k + (1 if self.wl.shared else 0), self.d), dtype=torch.float32, device=dev)
-        y_buf = torch.empty((1, self.d), dtype=self.x_dec[0].dtype, device=dev)
         outs = []
         nb = self.x_dec[0].shape[0]
         torch.cuda.synchronize()
@@ -171,22 +225,31 @@ class OffloadStack:
             for s in range(steps):
                 for l in range(L):
                     x = self.x_dec[l][s % nb:s % nb + 1]
-                    idx, w, _ = route(x, self.w_router[l], self.bias[l], k, forced_idx=forced[s, l:l + 1],
-                                      out=rbuf, stream=self.compute)
-                    counts, offsets, perm, inv = permute(idx, E, out=pbuf, stream=self.compute)
+                    idx, w, perm = self._layer(l, x, forced[s, l:l + 1])
                     host_idx.copy_(idx, non_blocking=True)
                     done.record(self.compute)
                     done.synchronize()  # the ids cross to the host: the cache decides there
-                    ids = np.unique(host_idx.numpy())
-                    self.cache.lookup(l, ids)
+                    self.cache.lookup(l, np.unique(host_idx.numpy()))
                     self.cache.fill(self.copy, self.compute)
-                    y = self._layer_kernels(l, x, idx, w, counts, offsets, perm, inv, y=y_buf, y_perm=y_perm)
+                    y = self._experts(l, x, w, perm)
                     self.cache.mark_read(l, self.compute)
                     if keep_outputs:
                         outs.append((s, l, y.clone()))
         self.compute.synchronize()
         el = time.perf_counter() - t0
         return (el, outs) if keep_outputs else el
+
+    def _forced(self, trace):
+        """The routing trace on the device (its buffer is reused between calls of the same length)."""
+        import torch
+
+        t = np.ascontiguousarray(trace, dtype=np.int32)
+        key = ("forced",) + t.shape
+        if key not in self._bufs:
+            self._bufs[key] = torch.empty(t.shape, dtype=torch.int32, device=self.device)
+        buf = self._bufs[key]
+        buf.copy_(torch.from_numpy(t))
+        return buf
 
     def close(self):
         import torch
@@ -196,11 +259,71 @@ class OffloadStack:
             self.cache.close()
             self.cache = None
         if getattr(self, "pinned", None):
-            pinned_free(self.pinned)
-            self.pinned = None
+            self._free_pinned()
 
     def __del__(self):
         try:
             self.close()
         except Exception:
             pass
+
+
+def pinned_h2d_GBps(nbytes: int = 1 << 29, reps: int = 4) -> float:
+    """Plain pinned host -> device copy rate, the ceiling the cache fills are compared with."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    return nbytes * reps / (time.perf_counter() - t0) / 1e9
+
+
+def run_trace(wl, layers: int, capacity_fracs=(0.40, 0.58), steps: int = 2048, prefill_tokens: int = 2048,
+              seed: int = 0, n_images: Optional[int] = None, log=None, min_layers: Optional[int] = 12):
+    """The offload workload: a prefill of `prefill_tokens`, then a `steps`-step batch-1 decode over a
+    seeded routing trace, once per cache capacity (fraction of all L*E routed experts).  When the
+    host cannot pin L layers, `min_layers` layers run instead (and the capacities scale with them).
+
+    Returns a dict of the measured figures per capacity (tokens/s, miss rates, H2D traffic)."""
+    import torch
+    import synth
+
+    log = log or (lambda *a: None)
+    pcie = pinned_h2d_GBps()  # before the pool is pinned
+    n_caps = [int(round(fr * layers * wl.E)) for fr in capacity_fracs]
+    stack = OffloadStack(wl, layers, max(n_caps), seed=seed, n_images=n_images, prefill_tokens=prefill_tokens,
+                         log=log, min_layers=min_layers)
+    requested, layers = layers, stack.L
+    trace = synth.routing_trace(seed, steps, layers, wl.E, wl.k)
+    caps = [int(round(fr * layers * wl.E)) for fr in capacity_fracs]
+    out = {"layers": layers, "layers_requested": requested, "experts_per_layer": wl.E, "slot_bytes": stack.stride,
+           "pool_GiB": stack.pool_bytes / 2**30, "steps": steps, "prefill_tokens": prefill_tokens,
+           "pcie_h2d_GBps": pcie, "runs": []}
+    try:
+        for fr, C in zip(capacity_fracs, caps):
+            stack.new_cache(C)
+            t_pre = stack.prefill()
+            st0 = stack.cache.stats()
+            t_dec = stack.decode(trace)
+            st = stack.cache.stats()
+            dec_bytes = st["bytes_h2d"] - st0["bytes_h2d"]
+            r = {"capacity_frac": fr, "slots": C,
+                 "prefill_s": t_pre, "prefill_tokens_per_s": prefill_tokens / t_pre,
+                 "prefill_miss_rate": st["pre_miss"] / max(1, st["pre_acc"]),
+                 "prefill_h2d_GBps": st0["bytes_h2d"] / t_pre / 1e9,
+                 "decode_s": t_dec, "decode_tokens_per_s": steps / t_dec,
+                 "decode_miss_rate": st["dec_miss"] / max(1, st["dec_acc"]),
+                 "decode_h2d_GBps": dec_bytes / t_dec / 1e9,
+                 "decode_h2d_MB_per_token": dec_bytes / steps / 1e6}
+            log(f"capacity {fr:.0%} ({C} slots): " + ", ".join(f"{k}={v:.4g}" for k, v in r.items()
+                                                              if isinstance(v, float)))
+            out["runs"].append(r)
+    finally:
+        stack.close()
+        torch.cuda.empty_cache()
+    return out
