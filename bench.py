@@ -1,10 +1,16 @@
 """MoE-layer throughput on one MI355X.
 
-Workload: the Qwen3.6-35B-A3B shaped decode layer (d_model 2048, 128 routed experts, top-8,
-SwiGLU d_ff 768, bf16, Zipf(1.1) router bias, experts in HBM slots in a seeded order).  A step
-is one whole layer forward -- route, permute, slot-indirected grouped SwiGLU, combine -- on one
-batch of T tokens (default 64).  Steps rotate over R distinct HBM copies of the layer's weights
-and R distinct input batches so that the 256 MB last-level cache cannot hold the working set.
+Headline workload: the Qwen3.6-35B-A3B shaped decode layer (d_model 2048, 128 routed experts,
+top-8, SwiGLU d_ff 768, bf16, Zipf(1.1) router bias, experts in HBM slots in a seeded order).  A
+step is one whole layer forward -- route, permute, slot-indirected grouped SwiGLU, combine -- on
+one batch of T tokens (default 64).  Steps rotate over R distinct HBM copies of the layer's
+weights and R distinct input batches so that the 256 MB last-level cache cannot hold the working
+set.
+
+Besides the headline it measures, on the same GPU: the DeepSeek-V4-Flash shaped bf16 prefill layer
+(MFMA grouped GEMM, T = 512/2048/8192), the same layer in int4 decode (T = 1/2/8), and the offload
+trace (stacked int4 layers in a pinned host pool behind the shared LRU slot cache: a 2048-token
+prefill that double-buffers the next layer, then a batch-1 decode trace, at 40 % and 58 % cache).
 
 Prints one JSON line: tokens/s, the HBM roofline of the dominant kernel (algorithmic bytes per
 launch over its event-timed duration), and the oracle timed on the host cores as a baseline.
@@ -12,6 +18,7 @@ launch over its event-timed duration), and the oracle timed on the host cores as
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -22,7 +29,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_gemv_gateup_bf16_qwen_a3b_T64_traffic.json")
 
 
 def parse():
@@ -35,15 +44,27 @@ def parse():
     ap.add_argument("--sweep", default="1,4,16,64", help="extra token counts timed for the sweep field")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-int4", action="store_true")
+    ap.add_argument("--no-offload", action="store_true")
+    ap.add_argument("--offload-layers", type=int, default=12,
+                    help="stacked layers in the pinned pool (24 need ~80 GB of pinned host memory)")
+    ap.add_argument("--offload-steps", type=int, default=2048)
     return ap.parse_args()
 
 
-def algorithmic_bytes(counts: np.ndarray, T: int, d: int, f: int, k: int, E: int, act_bytes=2, w_bytes=2):
-    """Bytes the layer must move: touched experts' weights, router weights, x in, y out,
-    plus the gate/up kernel's own share (its weights, its x rows, its h rows)."""
-    U = int((counts > 0).sum())
-    gateup = U * 2 * f * d * w_bytes + T * k * d * act_bytes + T * k * f * act_bytes
-    down = U * d * f * w_bytes + T * k * f * act_bytes + T * k * d * 4
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(counts: np.ndarray, T: int, d: int, f: int, k: int, E: int, act_bytes=2, w_bytes=2.0,
+                      shared=False):
+    """Bytes the layer must move: touched experts' weights, router weights, x in, y out, plus the
+    gate/up kernel's own share (its weights, its x rows, its h rows)."""
+    U = int((counts > 0).sum()) + (1 if shared else 0)
+    rows = T * k + (T if shared else 0)
+    gateup = U * 2 * f * d * w_bytes + rows * d * act_bytes + rows * f * act_bytes
+    down = U * d * f * w_bytes + rows * f * act_bytes + rows * d * 4
     layer = U * 3 * d * f * w_bytes + E * d * act_bytes + 2 * T * d * act_bytes
     return dict(U=U, gateup=gateup, down=down, layer=layer)
 
@@ -69,89 +90,221 @@ def cpu_baseline(wl, li, T, budget_s):
         if el >= budget_s or calls >= 50:
             break
     return {"value": calls * T / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{calls} layer calls of {T} tokens (float64 numpy/BLAS oracle, {el:.1f} s)"}
+            "sample": f"{calls} layer calls of {T} tokens of the headline layer (float64 numpy/BLAS oracle, {el:.1f} s)"}
+
+
+def replicate(base, R):
+    """R distinct HBM copies of one layer's slot pool (same slot order)."""
+    from expert_offload_cache_amd.layer import DeviceLayer
+
+    layers = [base]
+    for _ in range(1, R):
+        cp = DeviceLayer.__new__(DeviceLayer)
+        cp.__dict__.update(base.__dict__)
+        cp.pool = base.pool.clone()
+        layers.append(cp)
+    return layers
+
+
+def time_layer(moe, wl, layers, T, steps, warmup, stream, forced=None):
+    """Wall time of `steps` layer forwards rotating over the replicas, then a second pass with
+    the library's per-kernel HIP-event timing.  -> (seconds, {kernel: avg us}, per-replica counts)."""
+    import torch
+    import synth
+
+    R = len(layers)
+    base = layers[0]
+    xs = [base.x_to_device(synth.layer_inputs(wl, T, seed=0, batch=b, with_experts=False).x) for b in range(R)]
+    wss = [base.workspace(T) for _ in range(R)]
+    outs = []
+
+    def run(n, keep=False):
+        for i in range(n):
+            o = layers[i % R].forward(xs[i % R], ws=wss[i % R], stream=stream, forced_idx=forced)
+            if keep and i < R:
+                outs.append(o["counts"])
+
+    with torch.cuda.stream(stream):
+        run(warmup)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run(steps, keep=True)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        moe.profile_reset()
+        moe.profile_enable(True)
+        run(steps)
+        torch.cuda.synchronize()
+        moe.profile_collect()
+        moe.profile_enable(False)
+    kern = {name: ms / n * 1e3 for name, (ms, n) in moe.profile_results().items()}
+    return el, kern, [c.cpu().numpy() for c in outs]
+
+
+def kname(kern, part):
+    names = [n for n in kern if n.startswith("ffn_") and part in n]
+    return names[0] if names else None
+
+
+def traffic_for(kernel_source: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, when that
+    summary was taken on the kernel source as it stands (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+        with open(os.path.join(ROOT, kernel_source), "rb") as fh:
+            digest = hashlib.sha256(fh.read()).hexdigest()
+        return rec["hbm_bytes_per_launch"] if rec.get("kernel_source_sha256") == digest else None
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def bench_decode(args, moe, stream):
+    import synth
+    from expert_offload_cache_amd.layer import DeviceLayer
+
+    wl = synth.WORKLOADS["qwen_a3b_decode_bf16"]
+    Tmain = args.tokens
+    tlist = sorted({Tmain, *[int(t) for t in args.sweep.split(",") if t]})
+    log(f"generating {wl.name} weights")
+    li = synth.layer_inputs(wl, max(tlist), seed=0)
+    layers = replicate(DeviceLayer.from_inputs(li), args.replicas)
+    res = {}
+    for T in tlist:
+        steps = args.steps if T == Tmain else max(20, args.steps // 4)
+        log(f"decode T={T}: {steps} timed steps")
+        el, kern, counts = time_layer(moe, wl, layers, T, steps, args.warmup, stream)
+        byts = [algorithmic_bytes(c, T, wl.d, wl.f, wl.k, wl.E) for c in counts]
+        avg = {key: float(np.mean([b[key] for b in byts])) for key in ("U", "gateup", "down", "layer")}
+        res[T] = dict(el=el, steps=steps, avg=avg, kern=kern)
+    del layers
+    return wl, li, res
+
+
+def bench_prefill(moe, stream):
+    import torch
+    import synth
+    from expert_offload_cache_amd.layer import DeviceLayer
+
+    wl = synth.WORKLOADS["dsv4_prefill_bf16"]
+    log(f"generating {wl.name} weights")
+    li = synth.layer_inputs(wl, 1, seed=0)
+    layer = DeviceLayer.from_inputs(li)
+    out = {}
+    for T in wl.T_list:
+        steps = 10
+        el, kern, counts = time_layer(moe, wl, [layer], T, steps, 2, stream)
+        c = counts[0]
+        rows = T * wl.k + T
+        U = int((c > 0).sum()) + 1
+        fl_gu, fl_dn = 2.0 * rows * 2 * wl.f * wl.d, 2.0 * rows * wl.d * wl.f
+        b = algorithmic_bytes(c, T, wl.d, wl.f, wl.k, wl.E, shared=True)
+        gu, dn = kern.get(kname(kern, "gateup")), kern.get(kname(kern, "down"))
+        ffn_us = gu + dn
+        roof_us = max((b["gateup"] + b["down"]) / HBM_PEAK_GBS / 1e3, (fl_gu + fl_dn) / MFMA_BF16_PEAK_TFS / 1e6)
+        out[str(T)] = {
+            "tokens_per_s": T * steps / el, "layer_us": el / steps * 1e6, "touched_experts": U,
+            "max_tokens_per_expert": int(c.max()),
+            "gateup_us": gu, "down_us": dn, "gateup_TFLOPs": fl_gu / gu / 1e6, "down_TFLOPs": fl_dn / dn / 1e6,
+            "ffn_TFLOPs": (fl_gu + fl_dn) / ffn_us / 1e6,
+            "ffn_mfma_frac": (fl_gu + fl_dn) / ffn_us / 1e6 / MFMA_BF16_PEAK_TFS,
+            "ffn_weights_GBps": U * 3 * wl.d * wl.f * 2 / ffn_us / 1e3,
+            "ffn_frac_of_attainable_roof": roof_us / ffn_us,
+            "kernels_us": kern,
+        }
+        log(f"prefill T={T}: {out[str(T)]['tokens_per_s']:.0f} tok/s, FFN {out[str(T)]['ffn_TFLOPs']:.0f} TF/s")
+    # the dense contraction alone: every token routed to the same k experts (n_e = T for k experts)
+    T = wl.T_list[-1]
+    forced = torch.from_numpy(np.tile(np.arange(wl.k, dtype=np.int32), (T, 1))).to("cuda")
+    el, kern, _ = time_layer(moe, wl, [layer], T, 10, 2, stream, forced=forced)
+    rows = T * wl.k + T
+    fl_gu, fl_dn = 2.0 * rows * 2 * wl.f * wl.d, 2.0 * rows * wl.d * wl.f
+    gu, dn = kern.get(kname(kern, "gateup")), kern.get(kname(kern, "down"))
+    out["dense_contraction"] = {
+        "routing": f"every token to experts 0..{wl.k - 1} (+ shared): {T} tokens per expert",
+        "gateup_TFLOPs": fl_gu / gu / 1e6, "down_TFLOPs": fl_dn / dn / 1e6,
+        "gateup_mfma_frac": fl_gu / gu / 1e6 / MFMA_BF16_PEAK_TFS, "down_mfma_frac": fl_dn / dn / 1e6 / MFMA_BF16_PEAK_TFS,
+    }
+    del layer
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_int4(moe, stream, replicas=4):
+    import torch
+    import synth
+    from expert_offload_cache_amd.layer import DeviceLayer
+
+    wl = synth.WORKLOADS["dsv4_decode_int4"]
+    log(f"generating {wl.name} weights")
+    li = synth.layer_inputs(wl, 1, seed=0)
+    layers = replicate(DeviceLayer.from_inputs(li), replicas)
+    out = {}
+    wb = 0.5 + 2.0 / 128  # int4 weight bytes per element, with its bf16 group scale
+    for T in wl.T_list:
+        steps = 100
+        el, kern, counts = time_layer(moe, wl, layers, T, steps, 10, stream)
+        b = [algorithmic_bytes(c, T, wl.d, wl.f, wl.k, wl.E, w_bytes=wb, shared=True) for c in counts]
+        gu_b = float(np.mean([x["gateup"] for x in b]))
+        dn_b = float(np.mean([x["down"] for x in b]))
+        gu, dn = kern.get(kname(kern, "gateup")), kern.get(kname(kern, "down"))
+        out[str(T)] = {"tokens_per_s": T * steps / el, "layer_us": el / steps * 1e6,
+                       "gateup_us": gu, "down_us": dn, "gateup_GBps": gu_b / gu / 1e3,
+                       "ffn_GBps": (gu_b + dn_b) / (gu + dn) / 1e3, "kernels_us": kern}
+        log(f"int4 decode T={T}: {out[str(T)]['tokens_per_s']:.0f} tok/s, FFN {out[str(T)]['ffn_GBps']:.0f} GB/s")
+    del layers
+    torch.cuda.empty_cache()
+    return out
+
+
+def miss_rates_policy(layers, steps, fracs=(0.40, 0.58), prefill=True):
+    """Miss rates of the full-depth trace from the library's cache in policy-only mode (no weights)."""
+    import synth
+    import expert_offload_cache_amd as moe
+
+    wl = synth.WORKLOADS["dsv4_offload_int4"]
+    trace = synth.routing_trace(0, steps, layers, wl.E, wl.k)
+    out = {}
+    for fr in fracs:
+        c = moe.SlotCache(layers, wl.E, int(round(fr * layers * wl.E)))
+        if prefill:
+            for l in range(layers):
+                c.policy_prefetch(l)
+                if l > 0:
+                    c.policy_mark_read(l - 1)
+            c.policy_mark_read(layers - 1)
+        for s in range(steps):
+            for l in range(layers):
+                c.lookup(l, trace[s, l])
+                c.policy_fill()
+                c.policy_mark_read(l)
+        st = c.stats()
+        out[f"{fr:.2f}"] = st["dec_miss"] / st["dec_acc"]
+        c.close()
+    return out
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
-                          "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
 
     import expert_offload_cache_amd as moe
-    import synth
-    from expert_offload_cache_amd.layer import DeviceLayer
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    wl = synth.WORKLOADS["qwen_a3b_decode_bf16"]
-    Tmain = args.tokens
-    R = args.replicas
-    tlist = sorted({Tmain, *[int(t) for t in args.sweep.split(",") if t]})
-    Tmax = max(tlist)
-
-    print(f"[bench] generating {wl.name} weights", file=sys.stderr, flush=True)
-    li = synth.layer_inputs(wl, Tmax, seed=0)
-    base = DeviceLayer.from_inputs(li, device=dev)
-    layers = [base]
-    for r in range(1, R):  # distinct HBM copies of the same layer (same slot order)
-        cp = DeviceLayer.__new__(DeviceLayer)
-        cp.__dict__.update(base.__dict__)
-        cp.pool = base.pool.clone()
-        layers.append(cp)
+    torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
 
-    def run_T(T, steps, warmup, profile=False):
-        xs = [base.x_to_device(synth.layer_inputs(wl, T, seed=0, batch=b, with_experts=False).x) for b in range(R)]
-        wss = [base.workspace(T) for _ in range(R)]
-        outs = []
-        with torch.cuda.stream(stream):
-            for i in range(warmup):
-                layers[i % R].forward(xs[i % R], ws=wss[i % R], stream=stream)
-            stream.synchronize()
-            if profile:
-                moe.profile_reset()
-                moe.profile_enable(True)
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for i in range(steps):
-                o = layers[i % R].forward(xs[i % R], ws=wss[i % R], stream=stream)
-                if i < R:
-                    outs.append(o["counts"])
-            stream.synchronize()
-            torch.cuda.synchronize()
-            el = time.perf_counter() - t0
-            if profile:
-                moe.profile_collect()
-                moe.profile_enable(False)
-        counts = [c.cpu().numpy() for c in outs]
-        return el, counts
-
-    res = {}
-    for T in tlist:
-        steps = args.steps if T == Tmain else max(20, args.steps // 4)
-        print(f"[bench] T={T}: {steps} timed steps", file=sys.stderr, flush=True)
-        el, counts = run_T(T, steps, args.warmup)
-        _, _ = run_T(T, steps, 2, profile=True)
-        prof = moe.profile_results()
-        byts = [algorithmic_bytes(c, T, wl.d, wl.f, wl.k, wl.E) for c in counts]
-        avg = {key: float(np.mean([b[key] for b in byts])) for key in ("U", "gateup", "down", "layer")}
-        kern = {name: ms / n * 1e3 for name, (ms, n) in prof.items()}  # average us per launch
-        res[T] = dict(el=el, steps=steps, avg=avg, kern=kern)
-
-    def kname(kern, part):
-        names = [n for n in kern if n.startswith("ffn_") and part in n]
-        return names[0] if names else None
-
+    wl, li, res = bench_decode(args, moe, stream)
+    Tmain = args.tokens
     m = res[Tmain]
-    ms_per_step = m["el"] / m["steps"] * 1e3
     gu_name = kname(m["kern"], "gateup")
     gu_us = m["kern"].get(gu_name)
     achieved = m["avg"]["gateup"] / (gu_us * 1e-6) / 1e9 if gu_us else None
-    roofline = {"bound": "hbm", "kernel": gu_name, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": None,
+    traffic = traffic_for("expert_offload_cache_amd/csrc/ffn_gemv.hip")
+    roofline = {"bound": "hbm", "kernel": gu_name, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": traffic,
                 "bytes_per_launch": m["avg"]["gateup"], "avg_launch_us": gu_us}
     sweep = {}
     for T, r in res.items():
@@ -160,26 +313,48 @@ def main():
         ffn_us = (gu or 0) + (dn or 0)
         sweep[str(T)] = {
             "tokens_per_s": T * r["steps"] / r["el"], "layer_us": r["el"] / r["steps"] * 1e6,
-            "touched_experts": r["avg"]["U"],
-            "gateup_us": gu, "down_us": dn,
+            "touched_experts": r["avg"]["U"], "gateup_us": gu, "down_us": dn,
             "gateup_GBps": r["avg"]["gateup"] / (gu * 1e-6) / 1e9 if gu else None,
             "ffn_GBps": (r["avg"]["gateup"] + r["avg"]["down"]) / (ffn_us * 1e-6) / 1e9 if ffn_us else None,
             "layer_GBps": r["avg"]["layer"] / (r["el"] / r["steps"]) / 1e9,
             "kernels_us": r["kern"],
         }
+    torch.cuda.empty_cache()
+
+    extra = {}
+    for name, enabled, fn in (("prefill_bf16", not args.no_prefill, lambda: bench_prefill(moe, stream)),
+                              ("decode_int4", not args.no_int4, lambda: bench_int4(moe, stream))):
+        if enabled:
+            try:
+                extra[name] = fn()
+            except Exception as err:  # a failure here must not cost the headline line
+                extra[name] = {"error": f"{type(err).__name__}: {err}"}
+    if not args.no_offload:
+        try:
+            import synth
+            from expert_offload_cache_amd.offload import run_trace
+
+            log(f"offload trace: {args.offload_layers} layers, {args.offload_steps} steps")
+            off = run_trace(synth.WORKLOADS["dsv4_offload_int4"], args.offload_layers, steps=args.offload_steps,
+                            prefill_tokens=2048, log=log)
+            off["miss_rate_24_layers_policy"] = miss_rates_policy(24, args.offload_steps)
+            extra["offload_int4"] = off
+        except Exception as err:
+            extra["offload_int4"] = {"error": f"{type(err).__name__}: {err}"}
+
     cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] timing the oracle on the host cores", file=sys.stderr, flush=True)
+        log("timing the oracle on the host cores")
         cpu = cpu_baseline(wl, li, Tmain, args.cpu_seconds)
     line = {
         "metric": "MoE-layer tokens/s (decode, grouped GEMV HBM roofline)",
         "value": Tmain * m["steps"] / m["el"], "unit": "tokens/s", "n_gpus": 1, "steps": m["steps"],
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "warmup": args.warmup, "ms_per_step": m["el"] / m["steps"] * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "qwen3.6-35b-a3b shaped decode MoE layer", "tokens": Tmain, "d_model": wl.d,
                    "experts": wl.E, "top_k": wl.k, "d_ff": wl.f, "weights": "bf16", "router_bias": "zipf(1.1)",
-                   "hbm_replicas": R, "parallelism": "single gpu"},
-        "roofline": roofline, "cpu_baseline": cpu, "sweep": sweep,
+                   "hbm_replicas": args.replicas, "parallelism": "single gpu"},
+        "roofline": roofline, "cpu_baseline": cpu, "sweep": sweep, **extra,
     }
     print(json.dumps(line))
 
