@@ -33,8 +33,11 @@
 namespace moe {
 namespace {
 
-// LDS layout: [NTG][K] activations, then [KS][NTG][NM][16] partial sums
-template <int MODE, int W, bool kBf16Act, int FPW, int NTG>
+// LDS layout: [NTG][K] activations, then [waves][NTG][NM][16] partial sums.
+// A workgroup owns RB consecutive 16-row blocks (RB > 1 only where one block is small: the down
+// projection's rows hold only f inputs); its waves are RB groups of KSW waves, each group splitting
+// its row block's inputs.
+template <int MODE, int W, bool kBf16Act, int FPW, int NTG, int RB>
 __global__ __launch_bounds__(512) void ffn_gemv_kernel(FfnArgs a) {
     constexpr int NM = (MODE == kGateUp) ? 2 : 1;
     constexpr int LV = Frag<W>::kLaneVec;
@@ -42,10 +45,12 @@ __global__ __launch_bounds__(512) void ffn_gemv_kernel(FfnArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
-    const int KS = blockDim.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int KS = blockDim.x >> 6;   // waves in the workgroup
+    const int KSW = KS / RB;          // waves per row block
     const int q = lane >> 4, r16 = lane & 15;
-    const int rb = blockIdx.x;
+    const int rbi = wv / KSW;         // this wave's row block within the workgroup
+    const int rb = blockIdx.x * RB + rbi;
     const int K = (MODE == kGateUp) ? a.d : a.f;
     const int nfrag = K / Frag<W>::kIn;
     uint8_t* s_x = smem;
@@ -66,9 +71,9 @@ __global__ __launch_bounds__(512) void ffn_gemv_kernel(FfnArgs a) {
         if (slot < 0 || slot >= a.n_slots) {
             // absent or invalid slot: flag it and give the expert's rows zeros; nothing is read
             if (threadIdx.x == 0) *a.status = 1;
-            for (int i = threadIdx.x; i < nt * 16; i += blockDim.x) {
-                const size_t row = (size_t)(p0 + i0 + i / 16);
-                const int c = rb * 16 + i % 16;
+            for (int i = threadIdx.x; i < nt * 16 * RB; i += blockDim.x) {
+                const size_t row = (size_t)(p0 + i0 + i / (16 * RB));
+                const int c = blockIdx.x * RB * 16 + i % (16 * RB);
                 if (MODE == kGateUp) {
                     if (kBf16Act) ((uint16_t*)a.h)[row * a.f + c] = 0;
                     else ((float*)a.h)[row * a.f + c] = 0.f;
@@ -82,8 +87,8 @@ __global__ __launch_bounds__(512) void ffn_gemv_kernel(FfnArgs a) {
     }
 
     // ---- this wave's fragments: issue every load now ---------------------------------------
-    const int per = (nfrag + KS - 1) / KS;
-    const int f0 = __builtin_amdgcn_readfirstlane(wv * per);
+    const int per = (nfrag + KSW - 1) / KSW;
+    const int f0 = __builtin_amdgcn_readfirstlane((wv - rbi * KSW) * per);
     const int nmine = __builtin_amdgcn_readfirstlane(max(0, min(per, nfrag - f0)));
     const uint8_t* mats[NM];
     if constexpr (MODE == kGateUp) {
@@ -146,43 +151,56 @@ __global__ __launch_bounds__(512) void ffn_gemv_kernel(FfnArgs a) {
             }
         }
         __syncthreads();
-        for (int idx = threadIdx.x; idx < nt * 16; idx += blockDim.x) {
-            const int i = idx >> 4, r = idx & 15;
+        for (int idx = threadIdx.x; idx < nt * 16 * RB; idx += blockDim.x) {
+            const int bi = idx / (nt * 16), rem = idx - bi * nt * 16;
+            const int i = rem >> 4, r = rem & 15;
             float v[NM];
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
                 float s = 0.f;
-                for (int w2 = 0; w2 < KS; ++w2) s += s_red[((w2 * NTG + i) * NM + m) * 16 + r];
+                for (int w2 = bi * KSW; w2 < (bi + 1) * KSW; ++w2) s += s_red[((w2 * NTG + i) * NM + m) * 16 + r];
                 v[m] = s;
             }
             const size_t row = (size_t)(p0 + i0 + i);
+            const int col = (blockIdx.x * RB + bi) * 16 + r;
             if constexpr (MODE == kGateUp) {
                 const float h = silu_mul(v[0], v[NM - 1]);
-                if (kBf16Act) ((uint16_t*)a.h)[row * a.f + rb * 16 + r] = f32_to_bf16(h);
-                else ((float*)a.h)[row * a.f + rb * 16 + r] = h;
+                if (kBf16Act) ((uint16_t*)a.h)[row * a.f + col] = f32_to_bf16(h);
+                else ((float*)a.h)[row * a.f + col] = h;
             } else {
-                a.y_perm[row * a.d + rb * 16 + r] = v[0];
+                a.y_perm[row * a.d + col] = v[0];
             }
         }
     }
 }
 
 struct Plan {
-    int fpw, ks, ntg;
+    int fpw, ksw, rb, ntg;
     size_t lds;
 };
 
-// fragments per wave: the smallest of 4/8/16 that needs at most 8 waves
-Plan plan_for(int K, int kin, int esz, int T) {
+// Shape of one launch.  Fragments per wave: the smallest of the allowed counts with at most 8 waves
+// per workgroup.  The down projection groups up to 4 row blocks per workgroup when one row block is
+// small (K = f inputs), so that a workgroup still streams tens of KB of weights.
+Plan plan_for(int MODE, int W, int M, int K, int kin, int esz, int T) {
     const int nfrag = K / kin;
-    Plan p{4, 1, 1, 0};
-    for (int f : {4, 8, 16}) {
-        p.fpw = f;
-        p.ks = (nfrag + f - 1) / f;
-        if (p.ks <= 8) break;
+    const int fpws_dense[] = {4, 8, 12, 16}, fpws_int4[] = {4, 8};
+    const int* fpws = W == MOE_INT4_G128 ? fpws_int4 : fpws_dense;
+    const int nf = W == MOE_INT4_G128 ? 2 : 4;
+    Plan p{0, 0, 1, 1, 0};
+    const int rbs[] = {4, 2, 1};
+    for (int rb : rbs) {
+        if (rb > 1 && (MODE != kDown || (M / 16) % rb != 0 || nfrag * rb > 128)) continue;
+        for (int i = 0; i < nf && !p.fpw; ++i) {
+            const int ksw = (nfrag + fpws[i] - 1) / fpws[i];
+            if (rb * ksw <= 8) p = Plan{fpws[i], ksw, rb, 1, 0};
+        }
+        if (p.fpw) break;
     }
     // tokens per LDS group: up to 16, with activations + partial sums within 64 KB
-    auto lds = [&](int g) { return (size_t)g * K * esz + (size_t)p.ks * g * 2 * 16 * 4; };
+    const int waves = p.ksw * p.rb;
+    const int nm = MODE == kGateUp ? 2 : 1;
+    auto lds = [&](int g) { return (size_t)g * K * esz + (size_t)waves * g * nm * 16 * 4; };
     int ntg = 1;
     while (ntg < 16 && ntg < T && lds(2 * ntg) <= 65536) ntg <<= 1;
     p.ntg = ntg;
@@ -190,45 +208,52 @@ Plan plan_for(int K, int kin, int esz, int T) {
     return p;
 }
 
-template <int MODE, int W, bool kBf16Act, int FPW>
+template <int MODE, int W, bool kBf16Act, int FPW, int RB>
 moe_status launch_ntg(const FfnArgs& a, const Plan& p, dim3 grid, hipStream_t st, const char* name) {
-    dim3 block(64 * p.ks);
+    dim3 block(64 * p.ksw * RB);
     ProfScope ps(name, st);
     switch (p.ntg) {
-        case 1: ffn_gemv_kernel<MODE, W, kBf16Act, FPW, 1><<<grid, block, p.lds, st>>>(a); break;
-        case 2: ffn_gemv_kernel<MODE, W, kBf16Act, FPW, 2><<<grid, block, p.lds, st>>>(a); break;
-        case 4: ffn_gemv_kernel<MODE, W, kBf16Act, FPW, 4><<<grid, block, p.lds, st>>>(a); break;
-        case 8: ffn_gemv_kernel<MODE, W, kBf16Act, FPW, 8><<<grid, block, p.lds, st>>>(a); break;
-        default: ffn_gemv_kernel<MODE, W, kBf16Act, FPW, 16><<<grid, block, p.lds, st>>>(a); break;
+        case 1: ffn_gemv_kernel<MODE, W, kBf16Act, FPW, 1, RB><<<grid, block, p.lds, st>>>(a); break;
+        case 2: ffn_gemv_kernel<MODE, W, kBf16Act, FPW, 2, RB><<<grid, block, p.lds, st>>>(a); break;
+        case 4: ffn_gemv_kernel<MODE, W, kBf16Act, FPW, 4, RB><<<grid, block, p.lds, st>>>(a); break;
+        case 8: ffn_gemv_kernel<MODE, W, kBf16Act, FPW, 8, RB><<<grid, block, p.lds, st>>>(a); break;
+        default: ffn_gemv_kernel<MODE, W, kBf16Act, FPW, 16, RB><<<grid, block, p.lds, st>>>(a); break;
     }
     return check_launch(name);
+}
+
+template <int MODE, int W, bool kBf16Act, int RB>
+moe_status launch_fpw(const FfnArgs& a, const Plan& p, dim3 grid, hipStream_t st, const char* name) {
+    if constexpr (W == MOE_INT4_G128) {
+        if (p.fpw == 4) return launch_ntg<MODE, W, kBf16Act, 4, RB>(a, p, grid, st, name);
+        return launch_ntg<MODE, W, kBf16Act, 8, RB>(a, p, grid, st, name);
+    } else {
+        switch (p.fpw) {
+            case 4: return launch_ntg<MODE, W, kBf16Act, 4, RB>(a, p, grid, st, name);
+            case 8: return launch_ntg<MODE, W, kBf16Act, 8, RB>(a, p, grid, st, name);
+            case 12: return launch_ntg<MODE, W, kBf16Act, 12, RB>(a, p, grid, st, name);
+            default: return launch_ntg<MODE, W, kBf16Act, 16, RB>(a, p, grid, st, name);
+        }
+    }
 }
 
 template <int MODE, int W, bool kBf16Act>
 moe_status launch(const FfnArgs& a, hipStream_t st, const char* name) {
     const int K = (MODE == kGateUp) ? a.d : a.f;
-    const Plan p = plan_for(K, Frag<W>::kIn, kBf16Act ? 2 : 4, a.T);
+    const int M = (MODE == kGateUp) ? a.f : a.d;  // output rows (gate/up: pairs of rows)
+    const Plan p = plan_for(MODE, W, M, K, Frag<W>::kIn, kBf16Act ? 2 : 4, a.T);
+    if (!p.fpw || p.lds > 65536) return set_error(MOE_ESHAPE, "%s: K=%d too large for this kernel", name, K);
     // work items: sum over experts of ceil(n_e / ntg) <= T*k/ntg + min(E, T*k), plus the shared chunks
     const int64_t tk = (int64_t)a.T * a.k;
     const int64_t items = (tk + p.ntg - 1) / p.ntg + std::min<int64_t>(a.E, tk) +
                           (a.shared_w ? (a.T + p.ntg - 1) / p.ntg : 0);
     if (items > 65535) return set_error(MOE_ESHAPE, "%s: %lld work items exceed one launch", name, (long long)items);
-    dim3 grid((unsigned)((MODE == kGateUp ? a.f : a.d) / 16), (unsigned)items);
-    if constexpr (W == MOE_INT4_G128) {  // dequantised fragments are 4x larger: at most 8 per wave
-        if (p.fpw == 4) return launch_ntg<MODE, W, kBf16Act, 4>(a, p, grid, st, name);
-        Plan q = p;
-        q.fpw = 8;
-        q.ks = (K / 128 + 7) / 8;
-        q.lds = (size_t)q.ntg * K * 2 + (size_t)q.ks * q.ntg * 2 * 16 * 4 + 16 * sizeof(int);
-        if (q.ks > 8 || q.lds > 65536) return set_error(MOE_ESHAPE, "%s: K=%d too large for int4 weights", name, K);
-        return launch_ntg<MODE, W, kBf16Act, 8>(a, q, grid, st, name);
-    } else {
-        switch (p.fpw) {
-            case 4: return launch_ntg<MODE, W, kBf16Act, 4>(a, p, grid, st, name);
-            case 8: return launch_ntg<MODE, W, kBf16Act, 8>(a, p, grid, st, name);
-            default: return launch_ntg<MODE, W, kBf16Act, 16>(a, p, grid, st, name);
-        }
+    dim3 grid((unsigned)(M / 16 / p.rb), (unsigned)items);
+    if constexpr (MODE == kDown) {
+        if (p.rb == 4) return launch_fpw<MODE, W, kBf16Act, 4>(a, p, grid, st, name);
+        if (p.rb == 2) return launch_fpw<MODE, W, kBf16Act, 2>(a, p, grid, st, name);
     }
+    return launch_fpw<MODE, W, kBf16Act, 1>(a, p, grid, st, name);
 }
 
 }  // namespace
