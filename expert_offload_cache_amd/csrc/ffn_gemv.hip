@@ -37,8 +37,11 @@ namespace {
 // A workgroup owns RB consecutive 16-row blocks (RB > 1 only where one block is small: the down
 // projection's rows hold only f inputs); its waves are RB groups of KSW waves, each group splitting
 // its row block's inputs.
+// Largest workgroup of a launch shape (bounds the registers the compiler may give each lane).
+constexpr int max_threads(int mode, int w) { return (mode == kDown && w != MOE_INT4_G128) ? 1024 : 512; }
+
 template <int MODE, int W, bool kBf16Act, int FPW, int NTG, int RB>
-__global__ __launch_bounds__(512) void ffn_gemv_kernel(FfnArgs a) {
+__global__ __launch_bounds__(max_threads(MODE, W)) void ffn_gemv_kernel(FfnArgs a) {
     constexpr int NM = (MODE == kGateUp) ? 2 : 1;
     constexpr int LV = Frag<W>::kLaneVec;
     constexpr int ESZ = kBf16Act ? 2 : 4;
@@ -180,20 +183,23 @@ struct Plan {
 };
 
 // Shape of one launch.  Fragments per wave: the smallest of the allowed counts with at most 8 waves
-// per workgroup.  The down projection groups up to 4 row blocks per workgroup when one row block is
-// small (K = f inputs), so that a workgroup still streams tens of KB of weights.
+// per workgroup (16 for the dense down projection, measured faster there).  The down projection
+// groups up to 4 row blocks per workgroup when one row block is small (K = f inputs), so that a
+// workgroup still streams tens of KB of weights.
 Plan plan_for(int MODE, int W, int M, int K, int kin, int esz, int T) {
     const int nfrag = K / kin;
-    const int fpws_dense[] = {4, 8, 12, 16}, fpws_int4[] = {4, 8};
-    const int* fpws = W == MOE_INT4_G128 ? fpws_int4 : fpws_dense;
-    const int nf = W == MOE_INT4_G128 ? 2 : 4;
+    // binary32 fragments are twice as large: at most 8 per wave, like dequantised int4 ones
+    const int fpws_bf16[] = {4, 8, 12, 16}, fpws_small[] = {4, 8};
+    const int* fpws = W == MOE_BF16 ? fpws_bf16 : fpws_small;
+    const int nf = W == MOE_BF16 ? 4 : 2;
     Plan p{0, 0, 1, 1, 0};
     const int rbs[] = {4, 2, 1};
     for (int rb : rbs) {
         if (rb > 1 && (MODE != kDown || (M / 16) % rb != 0 || nfrag * rb > 128)) continue;
         for (int i = 0; i < nf && !p.fpw; ++i) {
             const int ksw = (nfrag + fpws[i] - 1) / fpws[i];
-            if (rb * ksw <= 8) p = Plan{fpws[i], ksw, rb, 1, 0};
+            const int max_waves = max_threads(MODE, W) / 64;
+            if (rb * ksw <= max_waves) p = Plan{fpws[i], ksw, rb, 1, 0};
         }
         if (p.fpw) break;
     }
@@ -224,7 +230,7 @@ moe_status launch_ntg(const FfnArgs& a, const Plan& p, dim3 grid, hipStream_t st
 
 template <int MODE, int W, bool kBf16Act, int RB>
 moe_status launch_fpw(const FfnArgs& a, const Plan& p, dim3 grid, hipStream_t st, const char* name) {
-    if constexpr (W == MOE_INT4_G128) {
+    if constexpr (W != MOE_BF16) {
         if (p.fpw == 4) return launch_ntg<MODE, W, kBf16Act, 4, RB>(a, p, grid, st, name);
         return launch_ntg<MODE, W, kBf16Act, 8, RB>(a, p, grid, st, name);
     } else {
