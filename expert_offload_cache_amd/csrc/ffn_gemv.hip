@@ -89,6 +89,30 @@ __global__ __launch_bounds__(max_threads(MODE, W)) void ffn_gemv_kernel(FfnArgs 
         base = a.pool + (size_t)slot * a.stride;
     }
 
+    // ---- the group's activation rows: issue their loads first ---------------------------------
+    // Loads complete in issue order, so activation loads issued after the weight loads could only
+    // be used once every weight had arrived.  Lane i < nt of each wave reads token i's source row
+    // (its activation row, or its h row in the down projection); each thread then loads up to XV
+    // 16-byte vectors of the group's rows into registers, before any weight load.
+    const uint8_t* in_base = (MODE == kGateUp) ? (const uint8_t*)a.x : (const uint8_t*)a.h;
+    const size_t row_bytes = (size_t)K * ESZ;
+    constexpr int XV = 4;
+    const int vpr = (int)(row_bytes / 16);
+    const int total = nt * vpr;
+    int my_row = 0;
+    if (lane < nt)
+        my_row = (MODE == kGateUp) ? (shared ? (i0 + lane) : (a.perm[p0 + i0 + lane] / a.k)) : (p0 + i0 + lane);
+    u32x4_t xr[XV];
+#pragma unroll
+    for (int u = 0; u < XV; ++u) {
+        // unconditional (clamped) loads: no branch, so they stay in flight together
+        const int v = min((int)threadIdx.x + u * (int)blockDim.x, total - 1);
+        const int i = v / vpr;
+        const int row = __shfl(my_row, i, 64);
+        xr[u] = *(const u32x4_t*)(in_base + (size_t)row * row_bytes + (size_t)(v - i * vpr) * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the weight loads
+
     // ---- this wave's fragments: issue every load now ---------------------------------------
     const int per = (nfrag + KSW - 1) / KSW;
     const int f0 = __builtin_amdgcn_readfirstlane((wv - rbi * KSW) * per);
@@ -117,24 +141,19 @@ __global__ __launch_bounds__(max_threads(MODE, W)) void ffn_gemv_kernel(FfnArgs 
         }
     }
 
-    const uint8_t* in_base = (MODE == kGateUp) ? (const uint8_t*)a.x : (const uint8_t*)a.h;
-    const size_t row_bytes = (size_t)K * ESZ;
-
     {
         // ---- stage the group's activation rows in LDS (16-byte vectors) ----------------------
         {
-            // source row of each token: its activation row (gate/up) or its h row (down)
-            int* s_row = (int*)(s_red + (size_t)KS * NTG * NM * 16);
-            if ((int)threadIdx.x < nt) {
-                const int i = threadIdx.x;
-                s_row[i] = (MODE == kGateUp) ? (shared ? (i0 + i) : (a.perm[p0 + i0 + i] / a.k)) : (p0 + i0 + i);
+#pragma unroll
+            for (int u = 0; u < XV; ++u) {
+                const int v = (int)threadIdx.x + u * (int)blockDim.x;
+                if (v < total) ((u32x4_t*)s_x)[v] = xr[u];
             }
-            __syncthreads();
-            const int vec_per_row = (int)(row_bytes / 16);
-            for (int v = threadIdx.x; v < nt * vec_per_row; v += blockDim.x) {
-                const int i = v / vec_per_row, c = v - i * vec_per_row;
-                ((uint4*)(s_x + (size_t)i * row_bytes))[c] =
-                    ((const uint4*)(in_base + (size_t)s_row[i] * row_bytes))[c];
+            // rows beyond XV vectors per thread (large K with many tokens): plain copies
+            for (int v = (int)threadIdx.x + XV * (int)blockDim.x; v < total; v += blockDim.x) {
+                const int i = v / vpr;
+                const int row = (MODE == kGateUp) ? (shared ? (i0 + i) : (a.perm[p0 + i0 + i] / a.k)) : (p0 + i0 + i);
+                ((u32x4_t*)s_x)[v] = *(const u32x4_t*)(in_base + (size_t)row * row_bytes + (size_t)(v - i * vpr) * 16);
             }
         }
         __syncthreads();
@@ -210,7 +229,7 @@ Plan plan_for(int MODE, int W, int M, int K, int kin, int esz, int T) {
     int ntg = 1;
     while (ntg < 16 && ntg < T && lds(2 * ntg) <= 65536) ntg <<= 1;
     p.ntg = ntg;
-    p.lds = lds(ntg) + 16 * sizeof(int);  // + source-row table
+    p.lds = lds(ntg);
     return p;
 }
 
