@@ -181,6 +181,16 @@ class SlotCache:
     def mark_read(self, layer: int, compute_stream=None):
         check(lib().moe_cache_mark_read(self.h, layer, _s(compute_stream)))
 
+    def resize(self, n_slots: int, copy_stream=None, compute_stream=None):
+        """Change the capacity at a safe point (every layer marked read, no fill pending)."""
+        check(lib().moe_cache_resize(self.h, n_slots, _s(copy_stream), _s(compute_stream)))
+        self.C = n_slots
+
+    def policy_resize(self, n_slots: int):
+        """resize() of a policy-only cache (no streams involved)."""
+        check(lib().moe_cache_resize(self.h, n_slots, None, None))
+        self.C = n_slots
+
     def policy_fill(self):
         """fill() of a policy-only cache (no streams involved)."""
         check(lib().moe_cache_fill(self.h, None, None))

@@ -59,6 +59,7 @@ struct moe_cache {
     int inject_failures = 0;
 
     int64_t read_seq = 0;
+    int64_t shrink_seq = -1;  // reads up to this one may still touch slots removed by a shrink
     hipEvent_t read_ev[kReadRing] = {};
     hipEvent_t fill_ev = nullptr;
     int32_t* stage[kStage] = {};
@@ -329,6 +330,90 @@ moe_status moe_cache_mark_read(moe_cache* c, int layer, moe_stream compute) {
         c->slots[s].pinned = false;
     }
     c->pinned_by_layer[layer].clear();
+    return MOE_OK;
+}
+
+moe_status moe_cache_resize(moe_cache* c, int n_slots, moe_stream copy, moe_stream compute) {
+    MOE_CHECK(c, MOE_EINVAL, "moe_cache_resize: NULL cache");
+    MOE_CHECK(n_slots >= 1, MOE_ECAPACITY, "moe_cache_resize: n_slots must be >= 1");
+    MOE_CHECK(c->pending.empty(), MOE_ESTATE, "moe_cache_resize: call moe_cache_fill for the pending misses first");
+    for (int l = 0; l < c->L; ++l)
+        MOE_CHECK(c->pinned_by_layer[l].empty(), MOE_ESTATE,
+                  "moe_cache_resize: layer %d is not marked read (resize only at a safe point)", l);
+    if (n_slots >= c->C) {
+        // grow: new slots are free
+        for (int s = c->C; s < n_slots; ++s) {
+            SlotInfo fresh;
+            fresh.read_seq = c->shrink_seq;  // a regrown slot may still be read by older kernels
+            c->slots.push_back(fresh);
+            c->free_slots.push(s);
+        }
+        c->C = n_slots;
+        return MOE_OK;
+    }
+    // shrink: keep the n_slots most recently used entries
+    c->shrink_seq = c->read_seq;
+    int resident = 0;
+    for (const SlotInfo& x : c->slots) resident += x.key >= 0;
+    while (resident > n_slots) {
+        const int32_t s = c->lru_head;
+        c->unlink(s);
+        c->table[c->slots[s].key] = -1;
+        c->slots[s].key = -1;
+        --resident;
+        c->table_dirty = true;
+    }
+    // kept entries in removed slots move to the lowest free slots below n_slots, taken in
+    // ascending old-slot order; each copy waits for the last read of the slot it overwrites
+    std::vector<int32_t> free_low;
+    for (int s = 0; s < n_slots; ++s)
+        if (c->slots[s].key < 0) free_low.push_back(s);
+    size_t next_free = 0;
+    std::vector<std::pair<int32_t, int32_t>> moves;  // (old, new)
+    for (int s = n_slots; s < c->C; ++s)
+        if (c->slots[s].key >= 0) moves.push_back({s, free_low[next_free++]});
+    hipStream_t cs = (hipStream_t)copy;
+    for (auto [from, to] : moves) {
+        if (!c->policy_only) {
+            hipEvent_t w = read_event_for(c, c->slots[to].read_seq);
+            if (w) MOE_HIP(hipStreamWaitEvent(cs, w, 0));
+            MOE_HIP(hipMemcpyAsync(c->pool + (size_t)to * c->stride, c->pool + (size_t)from * c->stride, c->stride,
+                                   hipMemcpyDeviceToDevice, cs));
+        }
+        // the moved entry takes the old slot's place in the LRU list
+        SlotInfo& dst = c->slots[to];
+        SlotInfo& src = c->slots[from];
+        dst.key = src.key;
+        dst.read_seq = src.read_seq;
+        dst.pinned = false;
+        dst.prev = src.prev;
+        dst.next = src.next;
+        if (src.prev >= 0) c->slots[src.prev].next = to; else c->lru_head = to;
+        if (src.next >= 0) c->slots[src.next].prev = to; else c->lru_tail = to;
+        c->table[dst.key] = to;
+        src = SlotInfo();
+        c->copy_log.push_back(to);
+        c->copy_log.push_back(dst.key);
+        c->copy_log.push_back(-2 - (int64_t)from);  // a move: -2 - source slot
+        c->table_dirty = true;
+    }
+    c->slots.resize(n_slots);
+    c->C = n_slots;
+    decltype(c->free_slots) fresh;
+    for (int s = 0; s < n_slots; ++s)
+        if (c->slots[s].key < 0) fresh.push(s);
+    c->free_slots.swap(fresh);
+    if (c->policy_only || !c->table_dirty) return MOE_OK;
+    int i = c->stage_next;
+    c->stage_next = (i + 1) % kStage;
+    if (c->stage_used[i]) MOE_HIP(hipEventSynchronize(c->stage_ev[i]));
+    memcpy(c->stage[i], c->table.data(), c->table.size() * 4);
+    MOE_HIP(hipMemcpyAsync(c->dtable, c->stage[i], c->table.size() * 4, hipMemcpyHostToDevice, cs));
+    MOE_HIP(hipEventRecord(c->stage_ev[i], cs));
+    c->stage_used[i] = true;
+    c->table_dirty = false;
+    MOE_HIP(hipEventRecord(c->fill_ev, cs));
+    MOE_HIP(hipStreamWaitEvent((hipStream_t)compute, c->fill_ev, 0));
     return MOE_OK;
 }
 

@@ -117,6 +117,13 @@ class OffloadStack:
         self.cache = SlotCache(self.L, self.E, self.n_slots, self.stride, self.slot_pool, self.slot_table,
                                self.host_ptrs())
 
+    def resize(self, n_slots: int):
+        """Change the cache capacity between layers (a safe point); moves run on the copy stream."""
+        if n_slots * self.stride > self.slot_pool.numel():
+            raise ValueError("not enough slot memory")
+        self.cache.resize(n_slots, self.copy, self.compute)
+        self.n_slots = int(n_slots)
+
     def host_ptrs(self):
         """Pinned address of every key (layer * E + expert)."""
         return [self.pinned[0] + key * self.stride for key in range(self.L * self.E)]
@@ -204,10 +211,13 @@ class OffloadStack:
         el = time.perf_counter() - t0
         return (el, outs) if keep_outputs else el
 
-    def decode(self, trace: np.ndarray, keep_outputs: bool = False, steps: Optional[int] = None):
+    def decode(self, trace: np.ndarray, keep_outputs: bool = False, steps: Optional[int] = None, first_step: int = 0):
         """Batch-1 decode over a routing trace [steps, L, k]: each layer's ids are forced from the
         trace (gates are the renormalised softmax of the router logits at those ids); per layer
         route -> ids back to the host -> cache lookup + fill -> permute/GEMV/combine.
+
+        `first_step` numbers the trace's first row (it selects the activations), so a trace can be
+        replayed in pieces, e.g. around a resize.
 
         Returns wall seconds (and outputs [(step, layer, y)] when keep_outputs)."""
         import torch
@@ -224,7 +234,8 @@ class OffloadStack:
         with torch.cuda.stream(self.compute):
             for s in range(steps):
                 for l in range(L):
-                    x = self.x_dec[l][s % nb:s % nb + 1]
+                    xb = (first_step + s) % nb
+                    x = self.x_dec[l][xb:xb + 1]
                     idx, w, perm = self._layer(l, x, forced[s, l:l + 1])
                     host_idx.copy_(idx, non_blocking=True)
                     done.record(self.compute)
@@ -234,7 +245,7 @@ class OffloadStack:
                     y = self._experts(l, x, w, perm)
                     self.cache.mark_read(l, self.compute)
                     if keep_outputs:
-                        outs.append((s, l, y.clone()))
+                        outs.append((first_step + s, l, y.clone()))
         self.compute.synchronize()
         el = time.perf_counter() - t0
         return (el, outs) if keep_outputs else el
@@ -323,6 +334,29 @@ def run_trace(wl, layers: int, capacity_fracs=(0.40, 0.58), steps: int = 2048, p
             log(f"capacity {fr:.0%} ({C} slots): " + ", ".join(f"{k}={v:.4g}" for k, v in r.items()
                                                               if isinstance(v, float)))
             out["runs"].append(r)
+        if len(caps) >= 2:
+            # elastic capacity: start at the larger cache, shrink to the smaller one half way
+            hi, lo = max(caps), min(caps)
+            stack.new_cache(hi)
+            stack.prefill()
+            half = steps // 2
+            t1 = stack.decode(trace[:half])
+            n_log = len(stack.cache.copy_log())
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            stack.resize(lo)
+            torch.cuda.synchronize()
+            t_resize = time.perf_counter() - t0
+            moves = int((stack.cache.copy_log()[n_log:, 2] <= -2).sum())
+            st0 = stack.cache.stats()
+            t2 = stack.decode(trace[half:], first_step=half)
+            st = stack.cache.stats()
+            out["elastic"] = {"from_slots": hi, "to_slots": lo, "at_step": half, "resize_ms": t_resize * 1e3,
+                              "moved_slots": moves, "decode_tokens_per_s_before": half / t1,
+                              "decode_tokens_per_s_after": (steps - half) / t2,
+                              "decode_miss_rate_after": (st["dec_miss"] - st0["dec_miss"]) /
+                                                        max(1, st["dec_acc"] - st0["dec_acc"])}
+            log("elastic: " + ", ".join(f"{k}={v:.4g}" for k, v in out["elastic"].items()))
     finally:
         stack.close()
         torch.cuda.empty_cache()

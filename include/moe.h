@@ -199,6 +199,17 @@ MOE_API moe_status moe_cache_prefetch_layer(moe_cache* c, int layer, moe_stream 
 /* Record on `compute` the point after which layer `layer`'s pinned slots are no longer read
  * (call after enqueueing the layer's kernels); unpins them. */
 MOE_API moe_status moe_cache_mark_read(moe_cache* c, int layer, moe_stream compute);
+/* Elastic capacity (FreeToken linux guide, mechanism table: the cache is resized at scheduler
+ * safe points; FreeToken RTX 5090 page, reconfiguration).  Allowed only at a safe point: every
+ * layer marked read and no fill pending (else MOE_ESTATE).  Growing adds free slots C..n-1 (the
+ * slot pool given at creation must hold n slots).  Shrinking keeps the n most recently used
+ * entries: LRU entries are evicted, oldest first; each kept entry in a slot >= n is copied
+ * device-to-device to the lowest free slot below n (kept entries taken in ascending old-slot
+ * order) on `copy`, after the last recorded read of its new slot; then the slot table is
+ * updated and `compute` waits.  A slot removed by a shrink and added back later is refilled only
+ * after every read recorded before the shrink.  Moves appear in moe_cache_copy_log with the
+ * third field = -2 - source slot.  Outputs never depend on the capacity. */
+MOE_API moe_status moe_cache_resize(moe_cache* c, int n_slots, moe_stream copy, moe_stream compute);
 /* out[0..5] = decode accesses, decode hits, decode misses, prefill accesses, prefill misses,
  * bytes copied host -> device. */
 MOE_API moe_status moe_cache_stats(const moe_cache* c, int64_t out[6]);

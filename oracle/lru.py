@@ -73,6 +73,35 @@ class LRUSim:
             self.stats["pre_miss"] += len(ids) - nh
         return [self.od[(layer, e)] for e in ids], flags, evicted
 
+    def resize(self, capacity: int):
+        """Change the capacity between requests (a safe point).
+
+        Growing adds free slots C..C'-1.  Shrinking keeps the C' most recently used entries
+        (the LRU ones are evicted, oldest first); each kept entry whose slot is >= C' moves to
+        the lowest free slot below C', taking the kept entries in ascending old-slot order.
+        Returns the moves as [(old_slot, new_slot, key)] in that order.
+        """
+        if capacity < 1:
+            raise CapacityError("capacity must be >= 1")
+        moves = []
+        if capacity < self.C:
+            while len(self.od) > capacity:
+                self.od.popitem(last=False)
+            used = set(self.od.values())
+            free = sorted(s for s in range(capacity) if s not in used)
+            for key, slot in sorted(self.od.items(), key=lambda kv: kv[1]):
+                if slot >= capacity:
+                    new = free.pop(0)
+                    self.od[key] = new  # assignment keeps the key's LRU position
+                    moves.append((slot, new, key))
+            used = set(self.od.values())
+            self.free = [s for s in range(capacity) if s not in used]
+        else:
+            self.free = list(self.free) + list(range(self.C, capacity))
+        heapq.heapify(self.free)
+        self.C = capacity
+        return moves
+
     def resident(self):
         return dict(self.od)
 
@@ -119,6 +148,24 @@ class BruteLRU:
         flags = [1 if was[e] else 0 for e in ids]
         self.log.extend(flags)
         return [self.slot[(layer, e)] for e in ids], flags
+
+    def resize(self, capacity: int):
+        """Same reading as LRUSim.resize, by linear scans."""
+        moves = []
+        if capacity < self.C:
+            while len(self.stamp) > capacity:
+                victim = min(self.stamp, key=lambda kk: self.stamp[kk])
+                del self.stamp[victim]
+                del self.slot[victim]
+            for key in sorted(self.slot, key=lambda kk: self.slot[kk]):
+                old = self.slot[key]
+                if old >= capacity:
+                    used = set(self.slot.values())
+                    new = min(s for s in range(capacity) if s not in used)
+                    self.slot[key] = new
+                    moves.append((old, new, key))
+        self.C = capacity
+        return moves
 
 
 def stack_distance_hits(requests, capacity: int):

@@ -127,3 +127,47 @@ def test_failed_copy_leaves_the_entry_non_resident(moe):
     assert nm == 1  # expert 1 misses again; it can take the freed slot
     c.policy_fill()
     assert c.slot_of(0, 1) >= 0
+
+
+def test_resize_matches_simulator(moe):
+    """Shrinks and grows at safe points: the C++ cache's hits, slots and moves equal the simulator's."""
+    L, E, k = 4, 16, 3
+    tr = synth.routing_trace(21, 60, L, E, k)
+    caps = {10: 20, 20: 9, 30: 14, 40: 6, 50: 25}
+    c = moe.SlotCache(L, E, 16)
+    sim = LRUSim(16)
+    for t in range(60):
+        if t in caps:
+            n0 = len(c.copy_log())
+            c.policy_resize(caps[t])
+            moves = sim.resize(caps[t])
+            log = c.copy_log()[n0:]
+            assert [(int(a), int(b), int(m)) for a, b, m in log] == \
+                [(new, key[0] * E + key[1], -2 - old) for old, new, key in moves]
+        for l in range(L):
+            slots, nm = c.lookup(l, tr[t, l])
+            ss, fl, _ = sim.request(l, tr[t, l])
+            assert list(slots) == ss and nm == len(fl) - sum(fl)
+            c.policy_fill()
+            c.policy_mark_read(l)
+    assert np.array_equal(c.trace(), np.array(sim.log, dtype=np.uint8))
+    for l in range(L):
+        for e in range(E):
+            assert c.slot_of(l, e) == sim.od.get((l, e), -1)
+
+
+def test_resize_only_at_a_safe_point(moe):
+    c = moe.SlotCache(2, 8, 6)
+    c.lookup(0, [1, 2])
+    with pytest.raises(moe.MoeError) as ei:
+        c.policy_resize(4)  # misses not filled yet
+    assert ei.value.status == -7
+    c.policy_fill()
+    with pytest.raises(moe.MoeError) as ei:
+        c.policy_resize(4)  # layer 0 not marked read
+    assert ei.value.status == -7
+    c.policy_mark_read(0)
+    c.policy_resize(4)
+    assert c.slot_of(0, 1) >= 0 and c.slot_of(0, 2) >= 0
+    with pytest.raises(moe.MoeError):
+        c.policy_resize(0)

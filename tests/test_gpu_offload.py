@@ -126,3 +126,48 @@ def test_outputs_do_not_depend_on_capacity(runs):
             assert (s0, l0) == (s1, l1) and np.array_equal(y0, y1)
         for (i0, y0), (i1, y1) in zip(ref["pre"], r["pre"]):
             assert np.array_equal(i0, i1) and np.array_equal(y0, y1)
+
+
+def test_resize_mid_trace():
+    """Shrink then grow between decode steps: outputs bitwise equal to a fixed-capacity run, and
+    hits, slots and moves equal to the simulator's."""
+    need_gpu()
+    from expert_offload_cache_amd.offload import OffloadStack
+
+    wl, trace = _wl(), _trace()
+    stack = OffloadStack(wl, L, 32, seed=0, n_images=IMAGES, prefill_tokens=T_PRE)
+    try:
+        stack.new_cache(20)
+        stack.prefill()
+        outs = []
+        plan = [(0, 9, None), (9, 17, 12), (17, STEPS, 28)]
+        for a, b, cap in plan:
+            if cap is not None:
+                stack.resize(cap)
+            _, o = stack.decode(trace[a:b], keep_outputs=True, first_step=a)
+            outs += [(s, l, y_to_f64(y)) for s, l, y in o]
+        sim = LRUSim(20)
+        flags, copies = [], []
+        for l in range(L):
+            slots, fl, _ = sim.request(l, list(range(E)), phase="prefill")
+            flags += fl
+            copies += [(sl, l * E + e, None) for e, sl, h in zip(range(E), slots, fl) if not h]
+        for a, b, cap in plan:
+            if cap is not None:
+                copies += [(new, key[0] * E + key[1], -2 - old) for old, new, key in sim.resize(cap)]
+            for s in range(a, b):
+                for l in range(L):
+                    ids = np.unique(trace[s, l]).tolist()
+                    slots, fl, _ = sim.request(l, ids)
+                    flags += fl
+                    copies += [(sl, l * E + e, None) for e, sl, h in zip(ids, slots, fl) if not h]
+        assert np.array_equal(stack.cache.trace(), np.array(flags, dtype=np.uint8))
+        log = stack.cache.copy_log()
+        got = [(int(a), int(b), int(m) if m <= -2 else None) for a, b, m in log]
+        assert got == copies
+    finally:
+        stack.close()
+    ref = _run(32)[1]
+    for (s0, l0, y0), (s1, l1, y1) in zip(ref["dec"], outs):
+        assert (s0, l0) == (s1, l1) and np.array_equal(y0, y1)
+    ref["stack"].close()

@@ -84,3 +84,48 @@ def test_capacity_error_and_stats():
     sim.request(0, [0, 1], phase="prefill")
     sim.request(0, [1, 2])
     assert sim.stats == dict(dec_acc=2, dec_hit=1, dec_miss=1, pre_acc=2, pre_miss=2)
+
+
+def test_resize_simulator_equals_brute_force():
+    """Resizes between requests: same hits, slots and moves as the linear-scan reading."""
+    rng = np.random.default_rng(11)
+    for trial in range(200):
+        L, E = 3, 6
+        C = int(rng.integers(3, 12))
+        a, b = LRUSim(C), BruteLRU(C)
+        for step in range(40):
+            if rng.random() < 0.15:
+                C2 = int(rng.integers(3, 14))
+                assert a.resize(C2) == b.resize(C2)
+            layer = int(rng.integers(0, L))
+            ids = rng.choice(E, size=int(rng.integers(1, 3)), replace=False)
+            sa, fa, _ = a.request(layer, ids)
+            sb, fb = b.request(layer, ids)
+            assert (sa, fa) == (sb, fb)
+
+
+def test_resize_keeps_the_most_recent_keys():
+    """Closed form: a shrink keeps, among the residents just before it, the C' with the latest use
+    in the access history (a grow keeps them all); every slot is then below C' and used once."""
+    rng = np.random.default_rng(12)
+    for trial in range(100):
+        C = int(rng.integers(4, 12))
+        sim = LRUSim(C)
+        last_use = {}
+        t = 0
+        for step in range(50):
+            if rng.random() < 0.2:
+                C = int(rng.integers(2, 14))
+                before = set(sim.od)
+                sim.resize(C)
+                expect = set(sorted(before, key=lambda key: -last_use[key])[:C])
+                assert set(sim.od) == expect
+                slots = list(sim.od.values())
+                assert len(set(slots)) == len(slots) and all(0 <= s < C for s in slots)
+            layer = int(rng.integers(0, 3))
+            ids = sorted(set(int(e) for e in rng.choice(6, size=min(C, int(rng.integers(1, 3))), replace=False)))
+            _, flags, _ = sim.request(layer, ids)
+            # use order inside a request: hits ascending, then misses ascending
+            for e in [e for e, f in zip(ids, flags) if f] + [e for e, f in zip(ids, flags) if not f]:
+                last_use[(layer, e)] = t
+                t += 1
