@@ -258,9 +258,11 @@ def bench_int4(moe, stream, replicas=4):
 
 
 def miss_rates_policy(layers, steps, fracs=(0.40, 0.58), prefill=True):
-    """Miss rates of the full-depth trace from the library's cache in policy-only mode (no weights)."""
+    """Miss rates of the full-depth trace from the library's cache in policy-only mode (no weights),
+    beside the two static placements at the same capacities."""
     import synth
     import expert_offload_cache_amd as moe
+    from expert_offload_cache_amd import placement
 
     wl = synth.WORKLOADS["dsv4_offload_int4"]
     trace = synth.routing_trace(0, steps, layers, wl.E, wl.k)
@@ -279,7 +281,10 @@ def miss_rates_policy(layers, steps, fracs=(0.40, 0.58), prefill=True):
                 c.policy_fill()
                 c.policy_mark_read(l)
         st = c.stats()
-        out[f"{fr:.2f}"] = st["dec_miss"] / st["dec_acc"]
+        C = int(round(fr * layers * wl.E))
+        out[f"{fr:.2f}"] = {"lru": st["dec_miss"] / st["dec_acc"],
+                            "static_partition": placement.miss_rate(trace, layers, wl.E, C, "partition"),
+                            "static_top_frequency": placement.miss_rate(trace, layers, wl.E, C, "top_frequency")}
         c.close()
     return out
 

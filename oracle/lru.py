@@ -197,3 +197,47 @@ def stack_distance_hits(requests, capacity: int):
             last[(layer, e)] = len(history)
             history.append((layer, e))
     return flags
+
+
+# ----------------------------------------------------------------------------------------------
+# Static placements (FreeToken linux guide, performance/compat: global LRU against a static expert
+# placement; Codex page, results).  A static placement fixes the resident keys before the trace and
+# never changes them: every access to another key is a miss.  Two readings:
+#   * "partition"      routing-unaware: the C slots are split evenly over the layers (the first
+#                      C mod L layers get one more) and layer l holds its lowest-numbered experts;
+#   * "top_frequency"  the C keys accessed most often in the trace (ties: lower layer, then lower
+#                      expert) -- the best any static placement can do on that trace.
+# ----------------------------------------------------------------------------------------------
+def static_resident(trace, L: int, E: int, C: int, placement: str):
+    """Set of resident (layer, expert) keys of a static placement over trace [steps, L, k]."""
+    C = max(0, min(C, L * E))
+    if placement == "partition":
+        keys = set()
+        for layer in range(L):
+            share = C // L + (1 if layer < C % L else 0)
+            for e in range(min(share, E)):
+                keys.add((layer, e))
+        return keys
+    if placement == "top_frequency":
+        count = {}
+        steps = len(trace)
+        for t in range(steps):
+            for layer in range(L):
+                for e in set(int(v) for v in trace[t][layer]):
+                    count[(layer, e)] = count.get((layer, e), 0) + 1
+        order = sorted(count, key=lambda key: (-count[key], key[0], key[1]))
+        return set(order[:C])
+    raise ValueError(placement)
+
+
+def static_miss_rate(trace, L: int, E: int, C: int, placement: str) -> float:
+    """Decode misses / decode accesses of a static placement (one access per distinct id per
+    (step, layer), as for the LRU)."""
+    res = static_resident(trace, L, E, C, placement)
+    acc = miss = 0
+    for t in range(len(trace)):
+        for layer in range(L):
+            for e in set(int(v) for v in trace[t][layer]):
+                acc += 1
+                miss += (layer, e) not in res
+    return miss / acc if acc else 0.0
