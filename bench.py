@@ -340,8 +340,10 @@ def main():
             from expert_offload_cache_amd.offload import run_trace
 
             log(f"offload trace: {args.offload_layers} layers, {args.offload_steps} steps")
+            # 40 % and 58 % of the routed experts, plus 20 % where misses per layer make the
+            # hybrid (host + PCIe) miss handling pay
             off = run_trace(synth.WORKLOADS["dsv4_offload_int4"], args.offload_layers, steps=args.offload_steps,
-                            prefill_tokens=2048, log=log)
+                            prefill_tokens=2048, capacity_fracs=(0.20, 0.40, 0.58), log=log)
             off["miss_rate_24_layers_policy"] = miss_rates_policy(24, args.offload_steps)
             extra["offload_int4"] = off
         except Exception as err:

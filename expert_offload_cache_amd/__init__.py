@@ -146,6 +146,19 @@ def pack_expert(wdt: str, d: int, f: int, wg, wu, wd, sg=None, su=None, sd=None,
     return out
 
 
+def cpu_expert_ffn(slot_image, wdt: str, d: int, f: int, x_bf16: np.ndarray, y: Optional[np.ndarray] = None,
+                   threads: int = 0) -> np.ndarray:
+    """One expert on the host from its packed slot image (numpy uint8 array or a host address).
+    x_bf16: bf16 bits (uint16) [n, d].  -> y float32 [n, d]."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    n = x.shape[0]
+    if y is None:
+        y = np.empty((n, d), dtype=np.float32)
+    img = slot_image.ctypes.data if isinstance(slot_image, np.ndarray) else int(slot_image)
+    check(lib().moe_cpu_expert_ffn(img, WDT[wdt], d, f, x.ctypes.data, n, y.ctypes.data, threads))
+    return y
+
+
 # ---------------------------------------------------------------------------------------------
 # expert-slot cache
 # ---------------------------------------------------------------------------------------------
@@ -174,6 +187,16 @@ class SlotCache:
 
     def fill(self, copy_stream=None, compute_stream=None):
         check(lib().moe_cache_fill(self.h, _s(copy_stream), _s(compute_stream)))
+
+    def fill_split(self, later, copy_stream=None, compute_stream=None):
+        """fill(), with the copies of the experts in `later` deferred (compute does not wait)."""
+        ids = np.ascontiguousarray(np.asarray(later, dtype=np.int32))
+        check(lib().moe_cache_fill_split(self.h, ids.ctypes.data if len(ids) else None, len(ids),
+                                         _s(copy_stream), _s(compute_stream)))
+
+    def policy_fill_split(self, later):
+        ids = np.ascontiguousarray(np.asarray(later, dtype=np.int32))
+        check(lib().moe_cache_fill_split(self.h, ids.ctypes.data if len(ids) else None, len(ids), None, None))
 
     def prefetch_layer(self, layer: int, copy_stream=None, compute_stream=None):
         check(lib().moe_cache_prefetch_layer(self.h, layer, _s(copy_stream), _s(compute_stream)))

@@ -32,6 +32,8 @@ SIGNATURES = {
     "moe_cache_prefetch_layer": (_st, [_vp, _i32, _vp, _vp]),
     "moe_cache_mark_read": (_st, [_vp, _i32, _vp]),
     "moe_cache_resize": (_st, [_vp, _i32, _vp, _vp]),
+    "moe_cache_fill_split": (_st, [_vp, _vp, _i32, _vp, _vp]),
+    "moe_cpu_expert_ffn": (_st, [_vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32]),
     "moe_cache_stats": (_st, [_vp, _vp]),
     "moe_cache_trace": (_st, [_vp, _vp, _i64, _vp]),
     "moe_cache_copy_log": (_st, [_vp, _vp, _i64, _vp]),

@@ -62,6 +62,9 @@ struct moe_cache {
     int64_t shrink_seq = -1;  // reads up to this one may still touch slots removed by a shrink
     hipEvent_t read_ev[kReadRing] = {};
     hipEvent_t fill_ev = nullptr;
+    hipEvent_t bg_ev = nullptr;  // end of the copies compute has not waited for yet
+    bool bg_pending = false;
+    int last_layer = -1;  // layer of the last request
     int32_t* stage[kStage] = {};
     hipEvent_t stage_ev[kStage] = {};
     bool stage_used[kStage] = {};
@@ -97,6 +100,7 @@ static moe_status request(moe_cache* c, int layer, const int32_t* ids, int n, in
         MOE_CHECK(ids[order[i]] != ids[order[i - 1]], MOE_EINVAL, "cache: duplicate expert id %d", ids[order[i]]);
 
     const int32_t base = layer * c->E;
+    c->last_layer = layer;
     // plan: victims are the oldest residents outside the request's hits; refuse pinned ones
     int n_miss = 0;
     std::vector<char> is_hit(n, 0);
@@ -230,6 +234,8 @@ moe_status moe_cache_create(int L, int E, int n_slots, size_t slot_stride, void*
                 fail(e, "hipEventCreate");
         if (st == MOE_OK && (e = hipEventCreateWithFlags(&c->fill_ev, hipEventDisableTiming)) != hipSuccess)
             fail(e, "hipEventCreate");
+        if (st == MOE_OK && (e = hipEventCreateWithFlags(&c->bg_ev, hipEventDisableTiming)) != hipSuccess)
+            fail(e, "hipEventCreate");
         for (int i = 0; i < kStage && st == MOE_OK; ++i) {
             if ((e = hipHostMalloc((void**)&c->stage[i], (size_t)L * E * 4, hipHostMallocDefault)) != hipSuccess)
                 fail(e, "hipHostMalloc");
@@ -256,13 +262,13 @@ moe_status moe_cache_lookup(moe_cache* c, int layer, const int32_t* ids, int n, 
     return request(c, layer, ids, n, slots_out, n_miss_out, false);
 }
 
-moe_status moe_cache_fill(moe_cache* c, moe_stream copy, moe_stream compute) {
-    MOE_CHECK(c, MOE_EINVAL, "moe_cache_fill: NULL cache");
+}  // extern "C"
+
+// Enqueue the copies of `todo` on cs (each after the last read of its slot); failed copies leave
+// their entries non-resident.  Returns the first error.
+static moe_status copy_entries(moe_cache* c, const std::vector<PendingCopy>& todo, hipStream_t cs) {
     moe_status result = MOE_OK;
     int n_copied = 0;
-    std::vector<PendingCopy> todo;
-    todo.swap(c->pending);
-    hipStream_t cs = (hipStream_t)copy;
     for (const PendingCopy& p : todo) {
         c->copy_log.push_back(p.slot);
         c->copy_log.push_back(p.key);
@@ -291,8 +297,11 @@ moe_status moe_cache_fill(moe_cache* c, moe_stream copy, moe_stream compute) {
         ++n_copied;
     }
     c->stats[5] += (int64_t)n_copied * (int64_t)c->stride;
-    if (c->policy_only || !c->table_dirty) return result;
-    // upload the whole table from a staging buffer whose previous upload has finished
+    return result;
+}
+
+// Upload the whole host table on cs from a staging buffer whose previous upload has finished.
+static moe_status upload_table(moe_cache* c, hipStream_t cs) {
     int i = c->stage_next;
     c->stage_next = (i + 1) % kStage;
     if (c->stage_used[i]) MOE_HIP(hipEventSynchronize(c->stage_ev[i]));
@@ -301,9 +310,57 @@ moe_status moe_cache_fill(moe_cache* c, moe_stream copy, moe_stream compute) {
     MOE_HIP(hipEventRecord(c->stage_ev[i], cs));
     c->stage_used[i] = true;
     c->table_dirty = false;
-    MOE_HIP(hipEventRecord(c->fill_ev, cs));
-    MOE_HIP(hipStreamWaitEvent((hipStream_t)compute, c->fill_ev, 0));
+    return MOE_OK;
+}
+
+static moe_status fill_impl(moe_cache* c, hipStream_t cs, hipStream_t compute, const int32_t* later, int n_later) {
+    std::vector<PendingCopy> todo, bg;
+    for (const PendingCopy& p : c->pending) {
+        bool is_later = false;
+        for (int i = 0; i < n_later && !is_later; ++i) is_later = p.key % c->E == later[i] && p.key / c->E == c->last_layer;
+        (is_later ? bg : todo).push_back(p);
+    }
+    c->pending.clear();
+    moe_status result = copy_entries(c, todo, cs);
+    if (c->policy_only) {
+        moe_status r2 = copy_entries(c, bg, cs);
+        return result != MOE_OK ? result : r2;
+    }
+    // compute waits for this request's copies and for earlier copies it has not waited for
+    if (c->table_dirty || !todo.empty() || c->bg_pending) {
+        if (c->table_dirty) {
+            moe_status r = upload_table(c, cs);
+            if (r != MOE_OK) return r;
+        }
+        MOE_HIP(hipEventRecord(c->fill_ev, cs));
+        MOE_HIP(hipStreamWaitEvent(compute, c->fill_ev, 0));
+        c->bg_pending = false;
+    }
+    if (!bg.empty()) {
+        moe_status r2 = copy_entries(c, bg, cs);
+        if (result == MOE_OK) result = r2;
+        if (c->table_dirty) {
+            moe_status r = upload_table(c, cs);
+            if (r != MOE_OK) return r;
+        }
+        MOE_HIP(hipEventRecord(c->bg_ev, cs));
+        c->bg_pending = true;
+    }
     return result;
+}
+
+extern "C" {
+
+moe_status moe_cache_fill(moe_cache* c, moe_stream copy, moe_stream compute) {
+    MOE_CHECK(c, MOE_EINVAL, "moe_cache_fill: NULL cache");
+    return fill_impl(c, (hipStream_t)copy, (hipStream_t)compute, nullptr, 0);
+}
+
+moe_status moe_cache_fill_split(moe_cache* c, const int32_t* later, int n_later, moe_stream copy,
+                                moe_stream compute) {
+    MOE_CHECK(c, MOE_EINVAL, "moe_cache_fill_split: NULL cache");
+    MOE_CHECK(n_later >= 0 && (n_later == 0 || later), MOE_EINVAL, "moe_cache_fill_split: bad id list");
+    return fill_impl(c, (hipStream_t)copy, (hipStream_t)compute, later, n_later);
 }
 
 moe_status moe_cache_prefetch_layer(moe_cache* c, int layer, moe_stream copy, moe_stream compute) {
@@ -466,6 +523,10 @@ void moe_cache_destroy(moe_cache* c) {
         if (c->fill_ev) {
             (void)hipEventSynchronize(c->fill_ev);
             (void)hipEventDestroy(c->fill_ev);
+        }
+        if (c->bg_ev) {
+            (void)hipEventSynchronize(c->bg_ev);
+            (void)hipEventDestroy(c->bg_ev);
         }
         for (int i = 0; i < kReadRing; ++i)
             if (c->read_ev[i]) (void)hipEventDestroy(c->read_ev[i]);

@@ -71,6 +71,7 @@ __global__ __launch_bounds__(max_threads(MODE, W)) void ffn_gemv_kernel(FfnArgs 
         base = a.shared_w;
     } else {
         const int slot = __builtin_amdgcn_readfirstlane(a.slot_of_expert[e]);
+        if (slot == MOE_SLOT_ELSEWHERE) return;  // rows produced elsewhere: leave them
         if (slot < 0 || slot >= a.n_slots) {
             // absent or invalid slot: flag it and give the expert's rows zeros; nothing is read
             if (threadIdx.x == 0) *a.status = 1;

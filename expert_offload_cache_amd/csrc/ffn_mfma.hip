@@ -100,6 +100,7 @@ __global__ __launch_bounds__(512) void ffn_mfma_kernel(FfnArgs a) {
         base = a.shared_w;
     } else {
         const int slot = __builtin_amdgcn_readfirstlane(a.slot_of_expert[e]);
+        if (slot == MOE_SLOT_ELSEWHERE) return;  // rows produced elsewhere: leave them
         if (slot < 0 || slot >= a.n_slots) {
             if (tid == 0) *a.status = 1;
             // zeros for this tile's outputs; nothing is read from the pool

@@ -25,6 +25,20 @@ from ._lib import MOE_BF16, MOE_F32
 from .layer import _expert_arrays, _to_device
 
 
+def hybrid_split(n_miss: int, cpu_rate: float, pcie_rate: float) -> int:
+    """Misses of one layer to run on the host: the n that minimises max((n_miss - n) / pcie_rate,
+    n / cpu_rate), both rates in expert images per second (ties: fewer on the host).  The host
+    takes the highest-numbered misses; they are not inserted into the cache."""
+    if cpu_rate <= 0 or n_miss <= 0:
+        return 0
+    best, best_t = 0, n_miss / pcie_rate
+    for n in range(1, n_miss + 1):
+        t = max((n_miss - n) / pcie_rate, n / cpu_rate)
+        if t < best_t - 1e-15:
+            best, best_t = n, t
+    return best
+
+
 class OffloadStack:
     """L stacked MoE layers whose routed experts live in a pinned host pool behind an LRU slot cache.
 
@@ -70,6 +84,7 @@ class OffloadStack:
                 self.x_pre.append(_to_device(xp, wl.act, device))
         self._ws = {}
         self._bufs = {}
+        self.cpu_experts = 0
         for T in ({1, prefill_tokens} - {0}):
             self._workspace(T)
             self._buffers(T)
@@ -176,42 +191,53 @@ class OffloadStack:
         perm = permute(idx, self.E, out=b["perm"], stream=self.compute)
         return idx, w, perm
 
-    def _experts(self, l: int, x, w, perm):
-        """Grouped experts through layer l's slot-table row, then the combine (compute stream)."""
+    def _experts(self, l: int, x, w, perm, table=None, do_combine: bool = True):
+        """Grouped experts through layer l's slot-table row (or `table`), then the combine (compute
+        stream).  Without the combine it returns y_perm."""
         T, E = x.shape[0], self.E
         b = self._buffers(T)
         counts, offsets, p, inv = perm
-        table = self.slot_table[l * E:(l + 1) * E]
+        if table is None:
+            table = self.slot_table[l * E:(l + 1) * E]
         y_perm, _ = expert_ffn_grouped(x, p, offsets, counts, table, self.slot_pool, self.n_slots, self.stride,
                                        self.wl.wdt, self.f, self.k, shared_w=self.shared[l], y_perm=b["y_perm"],
                                        ws=self._workspace(T), stream=self.compute)
+        if not do_combine:
+            return y_perm
         return combine(y_perm, w, inv, self.k, self.shared[l] is not None, x.dtype, y=b["y"], stream=self.compute)
 
     # ------------------------------------------------------------------------------------------
     def prefill(self, keep_outputs: bool = False):
         """All L layers over the prefill batch; layer l+1's experts stream in on the copy stream
-        while layer l computes.  Returns wall seconds (and per-layer (ids, y) when keep_outputs)."""
+        while layer l computes (when the cache holds two layers, else layer by layer).
+        Returns wall seconds (and per-layer (ids, y) when keep_outputs)."""
         import torch
 
         outs = []
+        # double buffering needs room for two layers (the one read and the one copied in)
+        double = self.n_slots >= 2 * self.E
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        self.cache.prefetch_layer(0, self.copy, self.compute)
+        if double:
+            self.cache.prefetch_layer(0, self.copy, self.compute)
         with torch.cuda.stream(self.compute):
             for l in range(self.L):
+                if not double:
+                    self.cache.prefetch_layer(l, self.copy, self.compute)
                 x = self.x_pre[l]
                 idx, w, perm = self._layer(l, x)
                 y = self._experts(l, x, w, perm)
                 if keep_outputs:
                     outs.append((idx.clone(), y.clone()))
-                if l + 1 < self.L:
+                if double and l + 1 < self.L:
                     self.cache.prefetch_layer(l + 1, self.copy, self.compute)
                 self.cache.mark_read(l, self.compute)
         self.compute.synchronize()
         el = time.perf_counter() - t0
         return (el, outs) if keep_outputs else el
 
-    def decode(self, trace: np.ndarray, keep_outputs: bool = False, steps: Optional[int] = None, first_step: int = 0):
+    def decode(self, trace: np.ndarray, keep_outputs: bool = False, steps: Optional[int] = None, first_step: int = 0,
+               hybrid: Optional[tuple] = None):
         """Batch-1 decode over a routing trace [steps, L, k]: each layer's ids are forced from the
         trace (gates are the renormalised softmax of the router logits at those ids); per layer
         route -> ids back to the host -> cache lookup + fill -> permute/GEMV/combine.
@@ -219,11 +245,19 @@ class OffloadStack:
         `first_step` numbers the trace's first row (it selects the activations), so a trace can be
         replayed in pieces, e.g. around a resize.
 
+        `hybrid` = (cpu_rate, pcie_rate[, copy_too]) turns on hybrid miss handling: each layer's
+        misses are split by hybrid_split; the host runs its share (moe_cpu_expert_ffn on the pinned
+        images) while the rest is copied and run on the GPU, and the host's rows are copied into
+        y_perm before the combine.  With copy_too (default) the host's misses are also inserted
+        and copied after the others, off this layer's critical path (the cache then sees every
+        request in full); without it they stay out of the cache.  The number of host-run experts
+        is added to self.cpu_experts.
+
         Returns wall seconds (and outputs [(step, layer, y)] when keep_outputs)."""
         import torch
 
         steps = steps or trace.shape[0]
-        L = self.L
+        L, E, k = self.L, self.E, self.k
         forced = self._forced(trace[:steps])
         host_idx = self._host_idx
         done = torch.cuda.Event()
@@ -231,6 +265,15 @@ class OffloadStack:
         nb = self.x_dec[0].shape[0]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        if hybrid:
+            from . import cpu_expert_ffn
+
+            dev, d = self.device, self.d
+            host_x = torch.empty((1, d), dtype=torch.int16, pin_memory=True)
+            host_tab = torch.full((E,), -1, dtype=torch.int32, pin_memory=True)
+            dev_tab = torch.empty(E, dtype=torch.int32, device=dev)
+            host_y = torch.empty((k, d), dtype=torch.float32, pin_memory=True)
+            y_perm_buf = self._buffers(1)["y_perm"]
         with torch.cuda.stream(self.compute):
             for s in range(steps):
                 for l in range(L):
@@ -238,11 +281,45 @@ class OffloadStack:
                     x = self.x_dec[l][xb:xb + 1]
                     idx, w, perm = self._layer(l, x, forced[s, l:l + 1])
                     host_idx.copy_(idx, non_blocking=True)
+                    if hybrid:
+                        host_x.copy_(x.view(torch.int16), non_blocking=True)
                     done.record(self.compute)
                     done.synchronize()  # the ids cross to the host: the cache decides there
-                    self.cache.lookup(l, np.unique(host_idx.numpy()))
-                    self.cache.fill(self.copy, self.compute)
-                    y = self._experts(l, x, w, perm)
+                    ids = np.unique(host_idx.numpy())
+                    if not hybrid:
+                        self.cache.lookup(l, ids)
+                        self.cache.fill(self.copy, self.compute)
+                        y = self._experts(l, x, w, perm)
+                    else:
+                        copy_too = hybrid[2] if len(hybrid) > 2 else True
+                        miss = [int(e) for e in ids if self.cache.slot_of(l, int(e)) < 0]
+                        n_cpu = hybrid_split(len(miss), hybrid[0], hybrid[1])
+                        on_cpu = miss[len(miss) - n_cpu:] if n_cpu else []
+                        gpu_ids = [int(e) for e in ids if copy_too or int(e) not in on_cpu]
+                        slots, _ = self.cache.lookup(l, gpu_ids)
+                        if copy_too:
+                            self.cache.fill_split(on_cpu, self.copy, self.compute)
+                        else:
+                            self.cache.fill(self.copy, self.compute)
+                        tab = host_tab.numpy()
+                        for e, sl in zip(gpu_ids, slots):
+                            tab[e] = sl
+                        for e in on_cpu:
+                            tab[e] = -2  # rows produced on the host
+                        dev_tab.copy_(host_tab, non_blocking=True)
+                        self._experts(l, x, w, perm, table=dev_tab, do_combine=False)
+                        # the host's experts, while the copies and the GPU experts run
+                        rank = {int(e): j for j, e in enumerate(ids)}  # one token: row = rank of the id
+                        hy = host_y.numpy()
+                        for e in on_cpu:
+                            key = l * E + e
+                            cpu_expert_ffn(self.pinned[0] + key * self.stride, self.wl.wdt, self.d, self.f,
+                                           host_x.numpy().view(np.uint16), y=hy[rank[e]:rank[e] + 1])
+                            y_perm_buf[rank[e]:rank[e] + 1].copy_(host_y[rank[e]:rank[e] + 1], non_blocking=True)
+                        self.cpu_experts += len(on_cpu)
+                        # the combine reads the host rows: it runs once they are in place
+                        y = combine(y_perm_buf, w, perm[3], k, self.shared[l] is not None, x.dtype,
+                                    y=self._buffers(1)["y"], stream=self.compute)
                     self.cache.mark_read(l, self.compute)
                     if keep_outputs:
                         outs.append((first_step + s, l, y.clone()))
@@ -294,6 +371,19 @@ def pinned_h2d_GBps(nbytes: int = 1 << 29, reps: int = 4) -> float:
     return nbytes * reps / (time.perf_counter() - t0) / 1e9
 
 
+def host_expert_rate(stack, reps: int = 5) -> float:
+    """Expert images per second the host kernel runs for one token (threads: the whole pool)."""
+    from . import cpu_expert_ffn
+
+    x = np.zeros((1, stack.d), dtype=np.uint16)
+    x[0, ::7] = 0x3F80  # some ones
+    cpu_expert_ffn(stack.pinned[0], stack.wl.wdt, stack.d, stack.f, x)
+    t0 = time.perf_counter()
+    for i in range(reps):
+        cpu_expert_ffn(stack.pinned[0] + i * stack.stride, stack.wl.wdt, stack.d, stack.f, x)
+    return reps / (time.perf_counter() - t0)
+
+
 def run_trace(wl, layers: int, capacity_fracs=(0.40, 0.58), steps: int = 2048, prefill_tokens: int = 2048,
               seed: int = 0, n_images: Optional[int] = None, log=None, min_layers: Optional[int] = 12):
     """The offload workload: a prefill of `prefill_tokens`, then a `steps`-step batch-1 decode over a
@@ -312,9 +402,11 @@ def run_trace(wl, layers: int, capacity_fracs=(0.40, 0.58), steps: int = 2048, p
     requested, layers = layers, stack.L
     trace = synth.routing_trace(seed, steps, layers, wl.E, wl.k)
     caps = [int(round(fr * layers * wl.E)) for fr in capacity_fracs]
+    cpu = host_expert_rate(stack)
     out = {"layers": layers, "layers_requested": requested, "experts_per_layer": wl.E, "slot_bytes": stack.stride,
            "pool_GiB": stack.pool_bytes / 2**30, "steps": steps, "prefill_tokens": prefill_tokens,
-           "pcie_h2d_GBps": pcie, "runs": []}
+           "pcie_h2d_GBps": pcie, "host_expert_GBps": cpu * stack.stride / 1e9, "runs": []}
+    rates = (cpu, pcie * 1e9 / stack.stride)  # expert images per second: host, PCIe
     try:
         for fr, C in zip(capacity_fracs, caps):
             stack.new_cache(C)
@@ -331,12 +423,21 @@ def run_trace(wl, layers: int, capacity_fracs=(0.40, 0.58), steps: int = 2048, p
                  "decode_miss_rate": st["dec_miss"] / max(1, st["dec_acc"]),
                  "decode_h2d_GBps": dec_bytes / t_dec / 1e9,
                  "decode_h2d_MB_per_token": dec_bytes / steps / 1e6}
+            # the same trace with hybrid miss handling: the host runs part of each layer's misses
+            stack.new_cache(C)
+            stack.prefill()
+            stack.cpu_experts = 0
+            t_hyb = stack.decode(trace, hybrid=rates)
+            sth = stack.cache.stats()
+            r["hybrid_decode_tokens_per_s"] = steps / t_hyb
+            r["hybrid_gpu_miss_rate"] = sth["dec_miss"] / max(1, sth["dec_acc"] + stack.cpu_experts)
+            r["hybrid_host_experts_per_token"] = stack.cpu_experts / steps
             log(f"capacity {fr:.0%} ({C} slots): " + ", ".join(f"{k}={v:.4g}" for k, v in r.items()
                                                               if isinstance(v, float)))
             out["runs"].append(r)
         if len(caps) >= 2:
-            # elastic capacity: start at the larger cache, shrink to the smaller one half way
-            hi, lo = max(caps), min(caps)
+            # elastic capacity: start at the largest cache, shrink to the next one half way
+            hi, lo = sorted(caps)[-1], sorted(caps)[-2]
             stack.new_cache(hi)
             stack.prefill()
             half = steps // 2

@@ -133,14 +133,17 @@ MOE_API moe_status moe_permute(const int32_t* topk_idx, int T, int k, int E, int
  * Expert e's weights are read from the slot slot_of_expert[e] of slot_pool (FreeToken GGUF
  * page, offload backend: expert slots on the GPU), i.e. at slot_pool + slot * slot_stride.
  *   x [T,d] act; perm, offsets, counts from moe_permute; slot_of_expert [E] int32 (a device
- *   row of the slot table; a slot outside [0, n_slots) sets the workspace status word to 1
- *   and that expert's rows to 0 -- it never reads outside the pool).
+ *   row of the slot table; MOE_SLOT_ELSEWHERE (-2) means the expert's rows of y_perm are
+ *   produced elsewhere, e.g. on the host (hybrid miss handling), and are left untouched; any
+ *   other slot outside [0, n_slots) sets the workspace status word to 1 and that expert's rows
+ *   to 0 -- it never reads outside the pool).
  *   shared_w: an always-on shared expert packed like a slot (or NULL); it runs on all T tokens.
  *   y_perm [T*k (+T if shared_w), d] f32: row p = expert output of sorted pair p; rows T*k+t
  *   hold the shared expert's output for token t.
  *   ws: device workspace of at least moe_workspace_bytes(...) bytes, zero-filled before its
  *   first use.  Its first 4 bytes are a sticky int32 status word (0 = no error).
  * Intermediate h is rounded to bf16 when act is BF16 (binary32 when act is F32). */
+#define MOE_SLOT_ELSEWHERE (-2)
 MOE_API size_t moe_workspace_bytes(int T, int d, int f, int E, int k, int has_shared,
                                    moe_dtype act, moe_dtype w);
 MOE_API moe_status moe_expert_ffn_grouped(const void* x, moe_dtype act, int T, int d, int f, int E,
@@ -191,6 +194,13 @@ MOE_API moe_status moe_cache_lookup(moe_cache* c, int layer, const int32_t* ids,
  * the slot it overwrites), then the slot-table update; `compute` waits for them.  A failed copy
  * enqueue leaves the failed entries non-resident (-1) and returns MOE_EHIP. */
 MOE_API moe_status moe_cache_fill(moe_cache* c, moe_stream copy, moe_stream compute);
+/* moe_cache_fill for hybrid miss handling (FreeToken linux guide, mechanism table: a miss is
+ * streamed, run on the CPU, or both): the pending misses of the last request whose expert ids are
+ * in `later` are copied after the others, and `compute` waits only for the others (those experts
+ * run elsewhere for this request, e.g. moe_cpu_expert_ffn).  The next fill, prefetch or resize
+ * makes `compute` wait for the deferred copies before anything else reads the slots. */
+MOE_API moe_status moe_cache_fill_split(moe_cache* c, const int32_t* later, int n_later, moe_stream copy,
+                                        moe_stream compute);
 /* Prefill: request all E experts of `layer` (prefill statistics) and fill on `copy`; `compute`
  * waits for the copies (enqueue the current layer's kernels on `compute` first, then prefetch
  * the next layer, so that the copies overlap the current layer). */
@@ -228,6 +238,16 @@ MOE_API moe_status moe_cache_copy_log(const moe_cache* c, int64_t* out, int64_t 
 MOE_API moe_status moe_cache_inject_copy_failures(moe_cache* c, int n);
 /* Waits for outstanding copies, releases events; the caller's buffers are untouched. */
 MOE_API void moe_cache_destroy(moe_cache* c);
+
+/* Host execution of one routed expert, the CPU side of hybrid miss handling (FreeToken RTX 5090
+ * page, miss split: a miss runs on the GPU after a PCIe copy or on the CPU, split by the measured
+ * host and PCIe bandwidths).  slot_image: host, the expert's packed slot (moe_pack_expert layout,
+ * w = MOE_BF16 or MOE_INT4_G128); x: host bf16 [n, d] (1 <= n <= 256); y: host binary32 [n, d],
+ * written.  y = W_d (silu(W_g x) * (W_u x)) with binary32 sums and h rounded to bf16, as on the GPU
+ * path.  threads: host threads to use (0 = all of the library's pool; MOE_CPU_THREADS sets the
+ * pool size, default the hardware concurrency).  Synchronous; no HIP call. */
+MOE_API moe_status moe_cpu_expert_ffn(const void* slot_image, moe_dtype w, int d, int f, const void* x, int n,
+                                      float* y, int threads);
 
 /* Page-locked host memory for the expert pool (hipHostMalloc). */
 MOE_API moe_status moe_pinned_alloc(size_t bytes, void** out);

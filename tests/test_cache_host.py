@@ -171,3 +171,25 @@ def test_resize_only_at_a_safe_point(moe):
     assert c.slot_of(0, 1) >= 0 and c.slot_of(0, 2) >= 0
     with pytest.raises(moe.MoeError):
         c.policy_resize(0)
+
+
+def test_fill_split_defers_the_listed_copies(moe):
+    """The deferred experts are still requested (same hits and slots as the plain LRU); their
+    copies are enqueued after the others."""
+    L, E, k = 3, 16, 4
+    tr = synth.routing_trace(31, 30, L, E, k)
+    c = moe.SlotCache(L, E, 10)
+    sim = LRUSim(10)
+    for t in range(30):
+        for l in range(L):
+            slots, nm = c.lookup(l, tr[t, l])
+            ss, fl, _ = sim.request(l, tr[t, l])
+            assert list(slots) == ss
+            miss = [int(e) for e, h in zip(sorted(tr[t, l]), fl) if not h]
+            later = miss[len(miss) // 2:]
+            n0 = len(c.copy_log())
+            c.policy_fill_split(later)
+            keys = [int(kk) % E for kk in c.copy_log()[n0:, 1]]
+            assert keys == [e for e in miss if e not in later] + later
+            c.policy_mark_read(l)
+    assert np.array_equal(c.trace(), np.array(sim.log, dtype=np.uint8))

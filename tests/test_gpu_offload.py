@@ -171,3 +171,57 @@ def test_resize_mid_trace():
     for (s0, l0, y0), (s1, l1, y1) in zip(ref["dec"], outs):
         assert (s0, l0) == (s1, l1) and np.array_equal(y0, y1)
     ref["stack"].close()
+
+
+@pytest.mark.parametrize("copy_too", [True, False])
+def test_hybrid_miss_split(copy_too):
+    """Hybrid miss handling: the host runs its share of each layer's misses from the pinned images
+    while the rest is copied.  With copy_too the host's misses are still inserted (deferred copies)
+    and the cache sees every request in full; without it the cache sees only the GPU share (as the
+    simulator fed the same split).  Outputs match the oracle."""
+    need_gpu()
+    from expert_offload_cache_amd.offload import OffloadStack, hybrid_split
+
+    wl, trace = _wl(), _trace()
+    rates = (1.0, 1.0, copy_too)  # equal host and PCIe rates: the host takes half of each layer's misses
+    stack = OffloadStack(wl, L, 16, seed=0, n_images=IMAGES, prefill_tokens=T_PRE)
+    try:
+        stack.prefill()
+        _, dec = stack.decode(trace, keep_outputs=True, hybrid=rates)
+        outs = [(s, l, y_to_f64(y)) for s, l, y in dec]
+        sim = LRUSim(16)
+        flags = []
+        for l in range(L):
+            flags += sim.request(l, list(range(E)), phase="prefill")[1]
+        n_cpu_total = 0
+        for s in range(STEPS):
+            for l in range(L):
+                ids = np.unique(trace[s, l]).tolist()
+                miss = [e for e in ids if (l, e) not in sim.od]
+                n_cpu = hybrid_split(len(miss), rates[0], rates[1])
+                on_cpu = miss[len(miss) - n_cpu:] if n_cpu else []
+                n_cpu_total += len(on_cpu)
+                flags += sim.request(l, [e for e in ids if copy_too or e not in on_cpu])[1]
+        assert np.array_equal(stack.cache.trace(), np.array(flags, dtype=np.uint8))
+        assert stack.cpu_experts == n_cpu_total > 0
+    finally:
+        stack.close()
+    per_layer = {}
+    worst = 0.0
+    for s, l, y in outs:
+        if l not in per_layer:
+            per_layer[l] = _layer_weights(stack, wl, l)
+        li = synth.layer_inputs(wl, 8, 0, layer=l, batch=1, with_experts=False)
+        experts, shared = per_layer[l]
+        ref = moe_layer(li.x[s % 8:s % 8 + 1], li.w_router, li.bias, "bf16", K, E, experts, shared,
+                        forced_idx=trace[s, l:l + 1])
+        worst = max(worst, float(rel_err_per_token(y, ref["y"]).max()))
+    assert worst <= 2e-2
+
+
+def test_hybrid_split_rule():
+    from expert_offload_cache_amd.offload import hybrid_split
+
+    assert hybrid_split(0, 1.0, 1.0) == 0 and hybrid_split(1, 1.0, 1.0) == 0 and hybrid_split(2, 1.0, 1.0) == 1
+    assert hybrid_split(3, 1.0, 2.0) == 1 and hybrid_split(6, 1.0, 2.0) == 2 and hybrid_split(4, 0.0, 1.0) == 0
+    assert hybrid_split(5, 10.0, 1.0) == 5
