@@ -27,6 +27,9 @@ constexpr size_t kPlanBytes = 1 << 16;
 
 // decode path: grouped GEMV kernels (ffn_gemv.hip)
 moe_status ffn_gemv(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st);
+// decode path, bf16 x bf16 on the matrix cores (ffn_gemv_mfma.hip); MOE_EDTYPE (nothing launched)
+// for shapes it does not cover
+moe_status ffn_gemv_mfma(const FfnArgs& a, hipStream_t st);
 // prefill path: MFMA grouped GEMM (ffn_mfma.hip); returns MOE_EDTYPE when it does not apply
 moe_status ffn_mfma(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st);
 

@@ -1,4 +1,6 @@
-// Grouped SwiGLU experts for few tokens per expert (decode): streaming GEMV over expert slots.
+// Grouped SwiGLU experts for few tokens per expert (decode): streaming GEMV over expert slots on
+// the vector ALUs.  It serves int4 and binary32 weights, and bf16 shapes the matrix-core decode
+// kernel (ffn_gemv_mfma.hip) does not cover (more than 8 fragments a wave).
 //
 // Expert weights are reached through the slot table (FreeToken GGUF page, "MoE backends",
 // offload backend: GPU expert slots; FreeToken linux guide, memory tier table).  The expert
@@ -287,6 +289,8 @@ moe_status launch(const FfnArgs& a, hipStream_t st, const char* name) {
 moe_status ffn_gemv(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st) {
     moe_status r;
     if (w == MOE_BF16 && act == MOE_BF16) {
+        r = ffn_gemv_mfma(a, st);
+        if (r != MOE_EDTYPE) return r;
         r = launch<kGateUp, MOE_BF16, true>(a, st, "ffn_gemv_gateup_bf16");
         if (r == MOE_OK) r = launch<kDown, MOE_BF16, true>(a, st, "ffn_gemv_down_bf16");
     } else if (w == MOE_INT4_G128 && act == MOE_BF16) {

@@ -191,7 +191,7 @@ class OffloadStack:
         perm = permute(idx, self.E, out=b["perm"], stream=self.compute)
         return idx, w, perm
 
-    def _experts(self, l: int, x, w, perm, table=None, do_combine: bool = True):
+    def _experts(self, l: int, x, w, perm, table=None, do_combine: bool = True, with_shared: bool = True):
         """Grouped experts through layer l's slot-table row (or `table`), then the combine (compute
         stream).  Without the combine it returns y_perm."""
         T, E = x.shape[0], self.E
@@ -200,7 +200,8 @@ class OffloadStack:
         if table is None:
             table = self.slot_table[l * E:(l + 1) * E]
         y_perm, _ = expert_ffn_grouped(x, p, offsets, counts, table, self.slot_pool, self.n_slots, self.stride,
-                                       self.wl.wdt, self.f, self.k, shared_w=self.shared[l], y_perm=b["y_perm"],
+                                       self.wl.wdt, self.f, self.k,
+                                       shared_w=self.shared[l] if with_shared else None, y_perm=b["y_perm"],
                                        ws=self._workspace(T), stream=self.compute)
         if not do_combine:
             return y_perm
@@ -237,13 +238,16 @@ class OffloadStack:
         return (el, outs) if keep_outputs else el
 
     def decode(self, trace: np.ndarray, keep_outputs: bool = False, steps: Optional[int] = None, first_step: int = 0,
-               hybrid: Optional[tuple] = None):
+               hybrid: Optional[tuple] = None, split_launch: bool = False):
         """Batch-1 decode over a routing trace [steps, L, k]: each layer's ids are forced from the
         trace (gates are the renormalised softmax of the router logits at those ids); per layer
         route -> ids back to the host -> cache lookup + fill -> permute/GEMV/combine.
 
         `first_step` numbers the trace's first row (it selects the activations), so a trace can be
         replayed in pieces, e.g. around a resize.
+
+        `split_launch`: a layer with misses runs its hit experts before waiting for the copies (the
+        misses marked as produced elsewhere), then the missed experts after them, then the combine.
 
         `hybrid` = (cpu_rate, pcie_rate[, copy_too]) turns on hybrid miss handling: each layer's
         misses are split by hybrid_split; the host runs its share (moe_cpu_expert_ffn on the pinned
@@ -265,6 +269,9 @@ class OffloadStack:
         nb = self.x_dec[0].shape[0]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        if hybrid or split_launch:
+            tabs = [torch.full((E,), -1, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+            dtabs = [torch.empty(E, dtype=torch.int32, device=self.device) for _ in range(2)]
         if hybrid:
             from . import cpu_expert_ffn
 
@@ -286,7 +293,28 @@ class OffloadStack:
                     done.record(self.compute)
                     done.synchronize()  # the ids cross to the host: the cache decides there
                     ids = np.unique(host_idx.numpy())
-                    if not hybrid:
+                    if not hybrid and split_launch:
+                        missed = {int(e) for e in ids if self.cache.slot_of(l, int(e)) < 0}
+                        slots, _ = self.cache.lookup(l, ids)
+                        if not missed:
+                            self.cache.fill(self.copy, self.compute)
+                            y = self._experts(l, x, w, perm)
+                        else:
+                            a, b_ = tabs[0].numpy(), tabs[1].numpy()
+                            a[:], b_[:] = -1, -1
+                            for e, sl in zip(ids, slots):
+                                e = int(e)
+                                a[e], b_[e] = (-2, sl) if e in missed else (sl, -2)
+                            dtabs[0].copy_(tabs[0], non_blocking=True)
+                            dtabs[1].copy_(tabs[1], non_blocking=True)
+                            # the resident experts run while the misses are copied in
+                            self._experts(l, x, w, perm, table=dtabs[0], do_combine=False)
+                            self.cache.fill(self.copy, self.compute)
+                            y_perm = self._experts(l, x, w, perm, table=dtabs[1], do_combine=False,
+                                                   with_shared=False)
+                            y = combine(y_perm, w, perm[3], k, self.shared[l] is not None, x.dtype,
+                                        y=self._buffers(1)["y"], stream=self.compute)
+                    elif not hybrid:
                         self.cache.lookup(l, ids)
                         self.cache.fill(self.copy, self.compute)
                         y = self._experts(l, x, w, perm)
@@ -432,6 +460,10 @@ def run_trace(wl, layers: int, capacity_fracs=(0.40, 0.58), steps: int = 2048, p
             r["hybrid_decode_tokens_per_s"] = steps / t_hyb
             r["hybrid_gpu_miss_rate"] = sth["dec_miss"] / max(1, sth["dec_acc"] + stack.cpu_experts)
             r["hybrid_host_experts_per_token"] = stack.cpu_experts / steps
+            # the same trace with split launches: resident experts overlap the miss copies
+            stack.new_cache(C)
+            stack.prefill()
+            r["split_decode_tokens_per_s"] = steps / stack.decode(trace, split_launch=True)
             log(f"capacity {fr:.0%} ({C} slots): " + ", ".join(f"{k}={v:.4g}" for k, v in r.items()
                                                               if isinstance(v, float)))
             out["runs"].append(r)

@@ -36,6 +36,10 @@ SMALL = [
     ("bf16", "bf16", 256, 96, 16, 4, 9, False),
     ("bf16", "bf16", 512, 160, 12, 3, 130, True),
     ("bf16", "bf16", 128, 64, 4, 4, 1, True),
+    # decode path on the matrix cores: several 16-token groups per workgroup (shared expert: 3)
+    ("bf16", "bf16", 384, 64, 4, 2, 40, True),
+    # gate/up K = 4096 inputs: beyond the matrix-core decode shapes, the VALU kernel runs
+    ("bf16", "bf16", 4096, 64, 4, 2, 3, False),
     ("bf16", "int4", 256, 128, 8, 2, 5, True),
     ("bf16", "int4", 512, 256, 16, 4, 67, False),
     # many tokens per expert: the MFMA grouped GEMM (several 128-token tiles, ragged tails)

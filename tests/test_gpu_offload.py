@@ -128,6 +128,26 @@ def test_outputs_do_not_depend_on_capacity(runs):
             assert np.array_equal(i0, i1) and np.array_equal(y0, y1)
 
 
+def test_split_launch_matches_plain_decode(runs):
+    """Split launches (resident experts before the copies' wait, missed ones after) change when the
+    experts run, not what they compute: outputs and the cache's decisions are bitwise those of the
+    plain decode at the same capacity."""
+    from expert_offload_cache_amd.offload import OffloadStack
+
+    _, ref = runs[16]
+    stack = OffloadStack(_wl(), L, 16, seed=0, n_images=IMAGES, prefill_tokens=T_PRE)
+    try:
+        stack.prefill()
+        _, dec = stack.decode(_trace(), keep_outputs=True, split_launch=True)
+        assert np.array_equal(stack.cache.trace(), ref["trace"])
+        st = stack.cache.stats()
+        assert st["dec_miss"] == ref["stats"]["dec_miss"] > 0
+    finally:
+        stack.close()
+    for (s0, l0, y0), (s1, l1, y1) in zip(ref["dec"], dec):
+        assert (s0, l0) == (s1, l1) and np.array_equal(y0, y_to_f64(y1))
+
+
 def test_resize_mid_trace():
     """Shrink then grow between decode steps: outputs bitwise equal to a fixed-capacity run, and
     hits, slots and moves equal to the simulator's."""
