@@ -181,24 +181,20 @@ def bench_decode(args, moe, stream):
     return wl, li, res
 
 
-def bench_prefill(moe, stream):
+def prefill_figures(moe, wl, layer, Ts, stream, w_bytes=2.0):
+    """Prefill tokens/s, FFN TFLOP/s and the fraction of the attainable roof for each T, then the
+    dense contraction alone (every token routed to the same k experts)."""
     import torch
-    import synth
-    from expert_offload_cache_amd.layer import DeviceLayer
 
-    wl = synth.WORKLOADS["dsv4_prefill_bf16"]
-    log(f"generating {wl.name} weights")
-    li = synth.layer_inputs(wl, 1, seed=0)
-    layer = DeviceLayer.from_inputs(li)
     out = {}
-    for T in wl.T_list:
+    for T in Ts:
         steps = 10
         el, kern, counts = time_layer(moe, wl, [layer], T, steps, 2, stream)
         c = counts[0]
         rows = T * wl.k + T
         U = int((c > 0).sum()) + 1
         fl_gu, fl_dn = 2.0 * rows * 2 * wl.f * wl.d, 2.0 * rows * wl.d * wl.f
-        b = algorithmic_bytes(c, T, wl.d, wl.f, wl.k, wl.E, shared=True)
+        b = algorithmic_bytes(c, T, wl.d, wl.f, wl.k, wl.E, w_bytes=w_bytes, shared=True)
         gu, dn = kern.get(kname(kern, "gateup")), kern.get(kname(kern, "down"))
         ffn_us = gu + dn
         roof_us = max((b["gateup"] + b["down"]) / HBM_PEAK_GBS / 1e3, (fl_gu + fl_dn) / MFMA_BF16_PEAK_TFS / 1e6)
@@ -208,13 +204,12 @@ def bench_prefill(moe, stream):
             "gateup_us": gu, "down_us": dn, "gateup_TFLOPs": fl_gu / gu / 1e6, "down_TFLOPs": fl_dn / dn / 1e6,
             "ffn_TFLOPs": (fl_gu + fl_dn) / ffn_us / 1e6,
             "ffn_mfma_frac": (fl_gu + fl_dn) / ffn_us / 1e6 / MFMA_BF16_PEAK_TFS,
-            "ffn_weights_GBps": U * 3 * wl.d * wl.f * 2 / ffn_us / 1e3,
+            "ffn_weights_GBps": U * 3 * wl.d * wl.f * w_bytes / ffn_us / 1e3,
             "ffn_frac_of_attainable_roof": roof_us / ffn_us,
             "kernels_us": kern,
         }
-        log(f"prefill T={T}: {out[str(T)]['tokens_per_s']:.0f} tok/s, FFN {out[str(T)]['ffn_TFLOPs']:.0f} TF/s")
-    # the dense contraction alone: every token routed to the same k experts (n_e = T for k experts)
-    T = wl.T_list[-1]
+        log(f"{wl.name} prefill T={T}: {out[str(T)]['tokens_per_s']:.0f} tok/s, FFN {out[str(T)]['ffn_TFLOPs']:.0f} TF/s")
+    T = Ts[-1]
     forced = torch.from_numpy(np.tile(np.arange(wl.k, dtype=np.int32), (T, 1))).to("cuda")
     el, kern, _ = time_layer(moe, wl, [layer], T, 10, 2, stream, forced=forced)
     rows = T * wl.k + T
@@ -225,6 +220,19 @@ def bench_prefill(moe, stream):
         "gateup_TFLOPs": fl_gu / gu / 1e6, "down_TFLOPs": fl_dn / dn / 1e6,
         "gateup_mfma_frac": fl_gu / gu / 1e6 / MFMA_BF16_PEAK_TFS, "down_mfma_frac": fl_dn / dn / 1e6 / MFMA_BF16_PEAK_TFS,
     }
+    return out
+
+
+def bench_prefill(moe, stream):
+    import torch
+    import synth
+    from expert_offload_cache_amd.layer import DeviceLayer
+
+    wl = synth.WORKLOADS["dsv4_prefill_bf16"]
+    log(f"generating {wl.name} weights")
+    li = synth.layer_inputs(wl, 1, seed=0)
+    layer = DeviceLayer.from_inputs(li)
+    out = prefill_figures(moe, wl, layer, wl.T_list, stream)
     del layer
     torch.cuda.empty_cache()
     return out
@@ -252,6 +260,8 @@ def bench_int4(moe, stream, replicas=4):
                        "gateup_us": gu, "down_us": dn, "gateup_GBps": gu_b / gu / 1e3,
                        "ffn_GBps": (gu_b + dn_b) / (gu + dn) / 1e3, "kernels_us": kern}
         log(f"int4 decode T={T}: {out[str(T)]['tokens_per_s']:.0f} tok/s, FFN {out[str(T)]['ffn_GBps']:.0f} GB/s")
+    # the same int4 layer at prefill sizes: the int4 MFMA grouped GEMM (weights dequantised in registers)
+    out["prefill"] = prefill_figures(moe, wl, layers[0], (512, 2048, 8192), stream, w_bytes=wb)
     del layers
     torch.cuda.empty_cache()
     return out

@@ -8,10 +8,10 @@
 // B = 32 inputs x 16 tokens with the same input split; C (binary32) holds, in lane l, token
 // l%16 and weight rows 4(l/16)..+3.
 //
-// Tiling: a workgroup of 8 waves (4 along weight rows x 2 along tokens) computes 256 weight
-// rows x NT tokens of one expert (NT = 128 or 256); each wave owns 64 rows x NT/2 tokens.  In the
-// gate/up launch a wave's 64 rows are 32 gate rows and the same 32 up rows, so SwiGLU is
-// applied in registers before one bf16 store of h.  Inputs advance 32 at a time through a ring
+// Tiling (bf16 weights): a workgroup of 8 waves computes MT = 512 weight rows x NT = 128 tokens of
+// one expert; each wave owns 64 rows x 128 tokens.  In the gate/up launch a wave's 64 rows are 32
+// gate rows and the same 32 up rows, so SwiGLU is applied in registers before one bf16 store of h.
+// int4 weights use a 256-row variant that dequantises in registers (below).  Inputs advance 32 at a time through a ring
 // of LDS stages filled by direct-to-LDS loads (global_load_lds_dwordx4), several stages ahead of
 // the MFMAs and without passing through registers: weights are copied fragment for fragment (the
 // slot layout is the LDS layout), and token rows are gathered through the permutation straight
@@ -206,6 +206,209 @@ __global__ __launch_bounds__(512) void ffn_mfma_kernel(FfnArgs a) {
     }
 }
 
+// int4 weights.  A fragment of the slot layout holds 16 rows x 128 inputs (1 KB); lane l's word s
+// carries inputs 32 s + 8(l/16) + 0..7 of row l%16, i.e. the A operand of the MFMA's s-th 32-input
+// step, 4 bits an input.  Each wave loads its own fragments straight into registers (non-temporal,
+// one 128-input group ahead) and dequantises one word per step into bf16(q s) -- the weight of the
+// int4 format, rounded once to bf16 -- with the row's group scale; the token rows go through the
+// same direct-to-LDS ring as in the bf16 kernel, 32 inputs a stage.
+template <int MT, int NT, int WM, int R>
+struct Tile4 {
+    static constexpr int kWN = 8 / WM;
+    static constexpr int kRA = MT / 16 / WM;   // row blocks per wave
+    static constexpr int kRB = NT / 16 / kWN;  // token blocks per wave
+    static constexpr int kLB = NT / 128;       // token fragments each wave loads per stage
+    static constexpr int kStage = NT * kKT * 2;
+    static constexpr int kLds = R * kStage;
+    static constexpr int kLoads = kLB;
+    static_assert(kRA % 2 == 0 && kRA * WM * 16 == MT && kRB * kWN * 16 == NT && R >= 3, "tile shape");
+};
+
+// word w of an int4 fragment (input pairs at bits 4p and 16+4p, nibble u -> q = u - 8) times the
+// scale s -> the 8 bf16 A-operand values (round to nearest even; q s itself is exact in binary32)
+__device__ __forceinline__ u32x4_t dequant_word(uint32_t w, float s) {
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    typedef float f32x2v __attribute__((ext_vector_type(2)));
+    const float m8 = -8.f * s;
+    uint32_t r[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float lo = __builtin_fmaf((float)((w >> (4 * p)) & 15u), s, m8);
+        const float hi = __builtin_fmaf((float)((w >> (16 + 4 * p)) & 15u), s, m8);
+        r[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){lo, hi}, bf16x2v));
+    }
+    return u32x4_t{r[0], r[1], r[2], r[3]};
+}
+
+template <int MODE, int MT, int NT, int WM, int R>
+__global__ __launch_bounds__(512) void ffn_mfma_int4_kernel(FfnArgs a) {
+    using TL = Tile4<MT, NT, WM, R>;
+    constexpr int RA = TL::kRA, RB = TL::kRB, LB = TL::kLB;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv % WM, wn = wv / WM;
+    const int K = (MODE == kGateUp) ? a.d : a.f;
+    const int nks = K / kKT;   // 32-input stages
+    const int ng = K / 128;    // int4 groups (fragments per row block)
+
+    int e, chunk;
+    if (!find_work(a.counts, a.E, a.T, NT, a.shared_w != nullptr, blockIdx.y, e, chunk)) return;
+    const bool shared = e == -1;
+    const int n_all = __builtin_amdgcn_readfirstlane(shared ? a.T : a.counts[e]);
+    const int t0 = chunk * NT;
+    const int nt = __builtin_amdgcn_readfirstlane(min(NT, n_all - t0));
+    const int p0 = __builtin_amdgcn_readfirstlane(shared ? a.T * a.k : a.offsets[e]);
+    const uint8_t* base;
+    if (shared) {
+        base = a.shared_w;
+    } else {
+        const int slot = __builtin_amdgcn_readfirstlane(a.slot_of_expert[e]);
+        if (slot == MOE_SLOT_ELSEWHERE) return;  // rows produced elsewhere: leave them
+        if (slot < 0 || slot >= a.n_slots) {
+            if (tid == 0) *a.status = 1;
+            const int rows0 = (MODE == kGateUp) ? blockIdx.x * (MT / 2) : blockIdx.x * MT;
+            const int nr = (MODE == kGateUp) ? MT / 2 : MT;
+            for (int i = tid; i < nt * nr; i += blockDim.x) {
+                const size_t row = (size_t)(p0 + t0 + i / nr);
+                const int col = rows0 + i % nr;
+                if (MODE == kGateUp) ((uint16_t*)a.h)[row * a.f + col] = 0;
+                else a.y_perm[row * a.d + col] = 0.f;
+            }
+            return;
+        }
+        base = a.pool + (size_t)slot * a.stride;
+    }
+
+    // this wave's row blocks (gate/up: pairs g, u of the same 16 outputs) and their scales
+    const uint8_t* a_blk[RA];
+#pragma unroll
+    for (int u = 0; u < RA; ++u) {
+        const int j = wm * RA + u;
+        if constexpr (MODE == kGateUp)
+            a_blk[u] = base + gu_block_offset(blockIdx.x * (MT / 32) + (j >> 1), j & 1, a.d, MOE_INT4_G128);
+        else
+            a_blk[u] = base + down_block_offset(blockIdx.x * (MT / 16) + j, a.d, a.f, MOE_INT4_G128);
+    }
+    const int r16 = lane & 15;
+    u32x4_t aw[RA], an[RA];  // raw fragments of the current and the next group
+    uint32_t sc[RA], sn[RA];  // their bf16 scales, converted where used (not across the loop edge)
+    auto load_group = [&](int g, u32x4_t (&w)[RA], uint32_t (&scl)[RA]) __attribute__((always_inline)) {
+        g = min(g, ng - 1);  // past the end: reload the last group (never used)
+#pragma unroll
+        for (int u = 0; u < RA; ++u) {
+            w[u] = __builtin_nontemporal_load((const u32x4_t*)(a_blk[u] + (size_t)g * 1024 + lane * 16));
+            scl[u] = *(const uint16_t*)(a_blk[u] + (size_t)ng * 1024 + ((size_t)r16 * ng + g) * 2);
+        }
+    };
+
+    // B fragment lane l: token 16 tb + l%16, inputs 8(l/16)..+7 of the stage.  Tokens past the
+    // tile's end read the tile's first row: MFMA columns are independent and are never stored.
+    const uint8_t* b_src[LB];
+    {
+        const uint8_t* b_base = (MODE == kGateUp) ? (const uint8_t*)a.x : (const uint8_t*)a.h;
+#pragma unroll
+        for (int u = 0; u < LB; ++u) {
+            int tok = (LB * wv + u) * 16 + (lane & 15);
+            tok = tok < nt ? tok : 0;
+            int src;
+            if (MODE == kGateUp) src = shared ? (t0 + tok) : (a.perm[p0 + t0 + tok] / a.k);
+            else src = p0 + t0 + tok;
+            b_src[u] = b_base + (size_t)src * K * 2 + (lane >> 4) * 16;
+        }
+    }
+    auto issue = [&](int ks) __attribute__((always_inline)) {
+        ks = min(ks, nks - 1);  // past the end: reload the last stage into a buffer nobody reads
+        uint8_t* buf = smem + (ks % R) * TL::kStage;
+#pragma unroll
+        for (int u = 0; u < LB; ++u) load_to_lds(b_src[u] + (size_t)ks * (kKT * 2), buf + (LB * wv + u) * 1024);
+    };
+
+    f32x4_t acc[RA][RB];
+#pragma unroll
+    for (int i = 0; i < RA; ++i)
+#pragma unroll
+        for (int j = 0; j < RB; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    // The next group's fragments and scales (2 RA loads) are issued in step 0 of a group, after that
+    // step's ring load; the barrier of step s counts them among the loads younger than stage ks
+    // while they are (steps 1 .. R-1 of the group), so the ring keeps its R-1 stages of lead.
+    // Two register sets take turns (group g in set g % 2), so a fragment is used in the registers
+    // its load wrote and no copy makes the compiler wait for loads in flight.
+    static_assert(R <= 4, "one group start at most among the R-1 younger ring loads");
+    auto run_group = [&](int g, const u32x4_t (&cw)[RA], const uint32_t (&cs)[RA], u32x4_t (&nw)[RA],
+                         uint32_t (&ns)[RA]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int ks = 4 * g + s;
+            if (s == 0) stage_barrier<(R - 2) * TL::kLoads>();
+            else if (s <= R - 1) stage_barrier<(R - 2) * TL::kLoads + 2 * RA>();
+            else stage_barrier<(R - 2) * TL::kLoads>();
+            issue(ks + R - 1);
+            if (s == 0) load_group(g + 1, nw, ns);
+            const uint8_t* sb = smem + (ks % R) * TL::kStage;
+            u32x4_t av[RA], bv[RB];
+#pragma unroll
+            for (int i = 0; i < RA; ++i) av[i] = dequant_word(cw[i][s], bf16_to_f32((uint16_t)cs[i]));
+#pragma unroll
+            for (int j = 0; j < RB; ++j) bv[j] = *(const u32x4_t*)(sb + (wn * RB + j) * 1024 + lane * 16);
+#pragma unroll
+            for (int j = 0; j < RB; ++j)
+#pragma unroll
+                for (int i = 0; i < RA; ++i) acc[i][j] = mfma(av[i], bv[j], acc[i][j]);
+        }
+    };
+    load_group(0, aw, sc);
+#pragma unroll
+    for (int s = 0; s < R - 1; ++s) issue(s);
+    for (int g = 0; g < ng; g += 2) {
+        run_group(g, aw, sc, an, sn);
+        if (g + 1 < ng) run_group(g + 1, an, sn, aw, sc);
+    }
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));  // drain the tail reloads (vmcnt(0))
+
+    // ---- epilogue (as in the bf16 kernel) ---------------------------------------------------------
+    const int quad = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+        const int tok = (wn * RB + j) * 16 + (lane & 15);
+        if (tok >= nt) continue;
+        const size_t row = (size_t)(p0 + t0 + tok);
+        if constexpr (MODE == kGateUp) {
+#pragma unroll
+            for (int i2 = 0; i2 < RA / 2; ++i2) {
+                const f32x4_t g = acc[2 * i2][j], u = acc[2 * i2 + 1][j];
+                const int col = (blockIdx.x * (MT / 32) + (wm * RA) / 2 + i2) * 16 + quad * 4;
+                uint2 o;
+                o.x = (uint32_t)f32_to_bf16(silu_mul(g[0], u[0])) | ((uint32_t)f32_to_bf16(silu_mul(g[1], u[1])) << 16);
+                o.y = (uint32_t)f32_to_bf16(silu_mul(g[2], u[2])) | ((uint32_t)f32_to_bf16(silu_mul(g[3], u[3])) << 16);
+                *(uint2*)((uint16_t*)a.h + row * a.f + col) = o;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < RA; ++i) {
+                const int col = (blockIdx.x * (MT / 16) + wm * RA + i) * 16 + quad * 4;
+                *(float4*)(a.y_perm + row * a.d + col) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+            }
+        }
+    }
+}
+
+template <int MODE, int MT, int NT, int WM, int R>
+moe_status launch_int4(const FfnArgs& a, hipStream_t st, const char* name) {
+    using TL = Tile4<MT, NT, WM, R>;
+    const int M = (MODE == kGateUp) ? 2 * a.f : a.d;
+    const int64_t tk = (int64_t)a.T * a.k;
+    const int64_t items = (tk + NT - 1) / NT + std::min<int64_t>(a.E, tk) + (a.shared_w ? (a.T + NT - 1) / NT : 0);
+    if (items > 65535) return set_error(MOE_ESHAPE, "%s: %lld token tiles exceed one launch", name, (long long)items);
+    auto kern = ffn_mfma_int4_kernel<MODE, MT, NT, WM, R>;
+    MOE_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, TL::kLds));
+    dim3 grid((unsigned)(M / MT), (unsigned)items);
+    ProfScope p(name, st);
+    kern<<<grid, 512, TL::kLds, st>>>(a);
+    return check_launch(name);
+}
+
 template <int MODE, int MT, int NT, int WM, int R>
 moe_status launch(const FfnArgs& a, hipStream_t st, const char* name) {
     using TL = Tile<MT, NT, WM, R>;
@@ -235,11 +438,28 @@ moe_status launch(const FfnArgs& a, hipStream_t st, const char* name) {
 #ifndef MOE_MFMA_R
 #define MOE_MFMA_R 3
 #endif
+#ifndef MOE_MFMA4_MT
+#define MOE_MFMA4_MT 256
+#endif
+#ifndef MOE_MFMA4_R
+#define MOE_MFMA4_R 4
+#endif
 
-// Many tokens per expert and bf16: the MFMA path.  Other cases report MOE_EDTYPE ("not mine").
+// Many tokens per expert, bf16 activations, bf16 or int4 weights: the MFMA path.  Other cases
+// report MOE_EDTYPE ("not mine").
 moe_status ffn_mfma(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st) {
     constexpr int MT = MOE_MFMA_MT, NT = MOE_MFMA_NT, WM = MOE_MFMA_WM, R = MOE_MFMA_R;
-    if (act != MOE_BF16 || w != MOE_BF16 || a.T <= 64) return MOE_EDTYPE;
+    if (act != MOE_BF16 || a.T <= 64) return MOE_EDTYPE;
+    if (w == MOE_INT4_G128) {
+        // 256 weight rows a workgroup: 2 row blocks x 8 token blocks a wave keep the accumulators,
+        // the raw fragments of two groups and the dequantised operands within 256 registers
+        constexpr int MT4 = MOE_MFMA4_MT, R4 = MOE_MFMA4_R;
+        if ((2 * a.f) % MT4 || a.d % MT4) return MOE_EDTYPE;
+        moe_status r = launch_int4<kGateUp, MT4, NT, WM, R4>(a, st, "ffn_mfma_gateup_int4");
+        if (r != MOE_OK) return r;
+        return launch_int4<kDown, MT4, NT, WM, R4>(a, st, "ffn_mfma_down_int4");
+    }
+    if (w != MOE_BF16) return MOE_EDTYPE;
     if ((2 * a.f) % MT || a.d % MT) return MOE_EDTYPE;
     moe_status r = launch<kGateUp, MT, NT, WM, R>(a, st, "ffn_mfma_gateup_bf16");
     if (r != MOE_OK) return r;

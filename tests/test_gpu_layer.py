@@ -42,6 +42,9 @@ SMALL = [
     ("bf16", "bf16", 4096, 64, 4, 2, 3, False),
     ("bf16", "int4", 256, 128, 8, 2, 5, True),
     ("bf16", "int4", 512, 256, 16, 4, 67, False),
+    # int4 with many tokens per expert: the int4 MFMA grouped GEMM (down: an odd number of groups)
+    ("bf16", "int4", 512, 256, 6, 2, 300, True),
+    ("bf16", "int4", 1024, 384, 16, 4, 257, False),
     # many tokens per expert: the MFMA grouped GEMM (several 128-token tiles, ragged tails)
     ("bf16", "bf16", 256, 128, 6, 2, 300, True),
     ("bf16", "bf16", 512, 384, 16, 4, 257, False),
@@ -164,6 +167,30 @@ def test_dsv4_int4_decode_layer(dsv4_int4_layer, T):
     err = rel_err_per_token(y_to_f64(out["y"]), ref["y"])
     print(f"max per-token rel err {err.max():.3g}")
     assert err.max() <= 2e-2
+
+
+@pytest.mark.parametrize("T", [512, 2048])
+def test_dsv4_int4_prefill_layer_sampled(dsv4_int4_layer, T):
+    """Full-size int4 prefill (the int4 MFMA GEMM): routing integers bit-exact, outputs on sampled
+    tokens against the oracle's exactly dequantised weights."""
+    wl, li8, layer = dsv4_int4_layer
+    print(f"dsv4 prefill int4 T={T}", flush=True)
+    li = synth.layer_inputs(wl, T, seed=0, with_experts=False)
+    out = _run(layer, li)
+    from oracle.permute import permute as o_permute
+    from oracle.router import route as o_route
+
+    _, idx, _ = o_route(li.x, li8.w_router, li8.bias, "bf16", wl.k)
+    assert np.array_equal(out["topk_idx"].cpu().numpy(), idx)
+    c, o, p, ip = o_permute(idx, wl.E)
+    for key, v in (("counts", c), ("offsets", o), ("perm", p), ("inv_perm", ip)):
+        assert np.array_equal(out[key].cpu().numpy(), v), key
+    toks = sorted({0, T // 3, T - 1, *np.random.default_rng(T).choice(T, 3, replace=False).tolist()})
+    ref = moe_layer_tokens(toks, li.x, li8.w_router, li8.bias, "bf16", wl.k, wl.E, li8.experts, li8.shared)
+    err = rel_err_per_token(y_to_f64(out["y"])[toks], ref["y"])
+    print(f"max n_e {int(c.max())} sampled max rel err {err.max():.3g}")
+    assert err.max() <= 2e-2
+    assert int(out["ws"][:4].view(dtype=__import__("torch").int32).item()) == 0
 
 
 def test_tiny_fp32_layer():
