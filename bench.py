@@ -267,7 +267,27 @@ def bench_int4(moe, stream, replicas=4):
     return out
 
 
-def miss_rates_policy(layers, steps, fracs=(0.40, 0.58), prefill=True):
+def hbm_copy_GBps(nbytes=2 << 30, reps=10):
+    """Achievable HBM ceiling: a device-to-device copy (the runtime's copy kernel) of `nbytes`,
+    read + write bytes per second, timed with HIP events."""
+    import torch
+
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    t1.record()
+    t1.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def miss_rates_policy(layers, steps, fracs=(0.40, 0.58), prefill=True, seed=0):
     """Miss rates of the full-depth trace from the library's cache in policy-only mode (no weights),
     beside the two static placements at the same capacities."""
     import synth
@@ -275,7 +295,7 @@ def miss_rates_policy(layers, steps, fracs=(0.40, 0.58), prefill=True):
     from expert_offload_cache_amd import placement
 
     wl = synth.WORKLOADS["dsv4_offload_int4"]
-    trace = synth.routing_trace(0, steps, layers, wl.E, wl.k)
+    trace = synth.routing_trace(seed, steps, layers, wl.E, wl.k)
     out = {}
     for fr in fracs:
         c = moe.SlotCache(layers, wl.E, int(round(fr * layers * wl.E)))
@@ -336,7 +356,7 @@ def main():
         }
     torch.cuda.empty_cache()
 
-    extra = {}
+    extra = {"hbm_copy_GBps": hbm_copy_GBps()}
     for name, enabled, fn in (("prefill_bf16", not args.no_prefill, lambda: bench_prefill(moe, stream)),
                               ("decode_int4", not args.no_int4, lambda: bench_int4(moe, stream))):
         if enabled:
@@ -355,6 +375,9 @@ def main():
             off = run_trace(synth.WORKLOADS["dsv4_offload_int4"], args.offload_layers, steps=args.offload_steps,
                             prefill_tokens=2048, capacity_fracs=(0.20, 0.40, 0.58), log=log)
             off["miss_rate_24_layers_policy"] = miss_rates_policy(24, args.offload_steps)
+            # the same at trace seeds 1 and 2 (the spread of the seed-0 figure)
+            off["miss_rate_24_layers_policy_seeds_1_2"] = [miss_rates_policy(24, args.offload_steps, seed=sd)
+                                                           for sd in (1, 2)]
             extra["offload_int4"] = off
         except Exception as err:
             extra["offload_int4"] = {"error": f"{type(err).__name__}: {err}"}

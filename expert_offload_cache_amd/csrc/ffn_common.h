@@ -115,7 +115,48 @@ __device__ __forceinline__ void gemv_group(const uint4 (&wreg)[FPW][NM][Frag<W>:
     for (int c = 0; c < FPW; ++c) {
         if (c < nmine) {
             const int fr = f0 + c;
-            if constexpr (W == MOE_INT4_G128) {
+            if constexpr (W == MOE_INT4_G128 && NTG <= 4) {
+                // few tokens: widen one word (32 inputs) at a time, so only 4 bf16 pairs per
+                // matrix are live (fewer registers, more resident waves); the sums run in the
+                // same order as in the general branch below
+                float xs[NTG], p[NTG][NM];
+#pragma unroll
+                for (int i = 0; i < NTG; ++i) {
+                    xs[i] = 0.f;
+#pragma unroll
+                    for (int m = 0; m < NM; ++m) p[i][m] = 0.f;
+                }
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    uint32_t wb[NM][4];
+#pragma unroll
+                    for (int m = 0; m < NM; ++m) {
+                        const uint4 wv = wreg[c][m][0];
+                        const uint32_t w = s == 0 ? wv.x : s == 1 ? wv.y : s == 2 ? wv.z : wv.w;
+                        int4_word_to_bf16(w, &wb[m][0]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < NTG; ++i) {
+                        if (i < nt) {
+                            const uint16_t* xr = (const uint16_t*)(s_x + (size_t)i * row_bytes) + fr * 128 + 8 * q;
+                            const uint4 xv = *(const uint4*)(xr + 32 * s);
+                            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                            for (int pp = 0; pp < 4; ++pp) {
+                                xs[i] = dot2(kOnes, xw[pp], xs[i]);
+#pragma unroll
+                                for (int m = 0; m < NM; ++m) p[i][m] = dot2(wb[m][pp], xw[pp], p[i][m]);
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < NTG; ++i)
+                    if (i < nt)
+#pragma unroll
+                        for (int m = 0; m < NM; ++m)
+                            acc[i][m] = __builtin_fmaf(sc[c][m], __builtin_fmaf(-136.0f, xs[i], p[i][m]), acc[i][m]);
+            } else if constexpr (W == MOE_INT4_G128) {
                 uint32_t wb[NM][16];
 #pragma unroll
                 for (int m = 0; m < NM; ++m) {

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(max_threads(MODE, W)) void ffn_gemv_kernel(FfnArgs 
     // 16-byte vectors of the group's rows into registers, before any weight load.
     const uint8_t* in_base = (MODE == kGateUp) ? (const uint8_t*)a.x : (const uint8_t*)a.h;
     const size_t row_bytes = (size_t)K * ESZ;
-    constexpr int XV = 4;
+    constexpr int XV = (NTG <= 2) ? 2 : 4;  // vectors a thread loads ahead; the copy loop below takes any rest
     const int vpr = (int)(row_bytes / 16);
     const int total = nt * vpr;
     int my_row = 0;
