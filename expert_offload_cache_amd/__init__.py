@@ -159,6 +159,23 @@ def cpu_expert_ffn(slot_image, wdt: str, d: int, f: int, x_bf16: np.ndarray, y: 
     return y
 
 
+# moe_decode_layer (include/moe.h): six pointers, then layer and a reserved int32
+DECODE_LAYER = np.dtype([("x", "<u8"), ("w_router", "<u8"), ("bias", "<u8"), ("forced", "<u8"),
+                         ("shared_w", "<u8"), ("y", "<u8"), ("layer", "<i4"), ("reserved", "<i4")])
+
+
+def decode_step(cache, layers: np.ndarray, T: int, d: int, f: int, E: int, k: int, act: int, wdt: str, slot_pool,
+                n_slots: int, slot_stride: int, slot_table, route_bufs, perm_bufs, y_perm, ws, host_idx, compute,
+                copy):
+    """One decode step of every layer in `layers` (a DECODE_LAYER array) through moe_decode_step."""
+    idx, w, logits = route_bufs
+    c, o, p, ip = perm_bufs
+    check(lib().moe_decode_step(cache.h, len(layers), layers.ctypes.data, T, d, f, E, k, act, WDT[wdt],
+                                _p(slot_pool), n_slots, slot_stride, _p(slot_table), _p(idx), _p(w), _p(logits),
+                                _p(c), _p(o), _p(p), _p(ip), _p(y_perm), _p(ws), ws.numel(), host_idx.data_ptr(),
+                                _s(compute), _s(copy)))
+
+
 # ---------------------------------------------------------------------------------------------
 # expert-slot cache
 # ---------------------------------------------------------------------------------------------

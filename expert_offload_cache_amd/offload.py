@@ -238,13 +238,16 @@ class OffloadStack:
         return (el, outs) if keep_outputs else el
 
     def decode(self, trace: np.ndarray, keep_outputs: bool = False, steps: Optional[int] = None, first_step: int = 0,
-               hybrid: Optional[tuple] = None, split_launch: bool = False):
+               hybrid: Optional[tuple] = None, split_launch: bool = False, native: bool = True):
         """Batch-1 decode over a routing trace [steps, L, k]: each layer's ids are forced from the
         trace (gates are the renormalised softmax of the router logits at those ids); per layer
         route -> ids back to the host -> cache lookup + fill -> permute/GEMV/combine.
 
         `first_step` numbers the trace's first row (it selects the activations), so a trace can be
         replayed in pieces, e.g. around a resize.
+
+        `native` (the plain mode): each step is one moe_decode_step call, which makes the same
+        library calls per layer without the Python marshalling between them.
 
         `split_launch`: a layer with misses runs its hit experts before waiting for the copies (the
         misses marked as produced elsewhere), then the missed experts after them, then the combine.
@@ -267,6 +270,8 @@ class OffloadStack:
         done = torch.cuda.Event()
         outs = []
         nb = self.x_dec[0].shape[0]
+        if native and not hybrid and not split_launch:
+            return self._decode_native(forced, steps, first_step, keep_outputs)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         if hybrid or split_launch:
@@ -351,6 +356,42 @@ class OffloadStack:
                     self.cache.mark_read(l, self.compute)
                     if keep_outputs:
                         outs.append((first_step + s, l, y.clone()))
+        self.compute.synchronize()
+        el = time.perf_counter() - t0
+        return (el, outs) if keep_outputs else el
+
+    def _decode_native(self, forced, steps: int, first_step: int, keep_outputs: bool):
+        """decode() in the plain mode, one moe_decode_step call per step."""
+        import torch
+        from . import DECODE_LAYER, decode_step
+
+        L, E, k, d = self.L, self.E, self.k, self.d
+        nb = self.x_dec[0].shape[0]
+        esz = 2 if self.wl.act == "bf16" else 4
+        b = self._buffers(1)
+        ws = self._workspace(1)
+        ys = ([torch.empty_like(b["y"]) for _ in range(L)] if keep_outputs else [b["y"]] * L)
+        # every step's layer descriptors, built before the timed loop
+        xb = (first_step + np.arange(steps)) % nb
+        arr = np.zeros((steps, L), dtype=DECODE_LAYER)
+        x0 = np.array([self.x_dec[l].data_ptr() for l in range(L)], dtype=np.uint64)
+        arr["x"] = x0[None, :] + (xb[:, None] * d * esz).astype(np.uint64)
+        arr["w_router"] = np.array([w.data_ptr() for w in self.w_router], dtype=np.uint64)[None, :]
+        arr["bias"] = np.array([0 if bb is None else bb.data_ptr() for bb in self.bias], dtype=np.uint64)[None, :]
+        arr["shared_w"] = np.array([0 if sw is None else sw.data_ptr() for sw in self.shared], dtype=np.uint64)[None, :]
+        arr["forced"] = forced.data_ptr() + (np.arange(steps * L, dtype=np.uint64) * (k * 4)).reshape(steps, L)
+        arr["y"] = np.array([y.data_ptr() for y in ys], dtype=np.uint64)[None, :]
+        arr["layer"] = np.arange(L, dtype=np.int32)[None, :]
+        outs = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(self.compute):
+            for s in range(steps):
+                decode_step(self.cache, arr[s], 1, d, self.f, E, k, self.act_code, self.wl.wdt, self.slot_pool,
+                            self.n_slots, self.stride, self.slot_table, b["route"], b["perm"], b["y_perm"], ws,
+                            self._host_idx, self.compute, self.copy)
+                if keep_outputs:
+                    outs += [(first_step + s, l, ys[l].clone()) for l in range(L)]
         self.compute.synchronize()
         el = time.perf_counter() - t0
         return (el, outs) if keep_outputs else el
@@ -451,6 +492,10 @@ def run_trace(wl, layers: int, capacity_fracs=(0.40, 0.58), steps: int = 2048, p
                  "decode_miss_rate": st["dec_miss"] / max(1, st["dec_acc"]),
                  "decode_h2d_GBps": dec_bytes / t_dec / 1e9,
                  "decode_h2d_MB_per_token": dec_bytes / steps / 1e6}
+            # the same trace through the per-layer Python loop (the loop hybrid and split use)
+            stack.new_cache(C)
+            stack.prefill()
+            r["python_loop_decode_tokens_per_s"] = steps / stack.decode(trace, native=False)
             # the same trace with hybrid miss handling: the host runs part of each layer's misses
             stack.new_cache(C)
             stack.prefill()

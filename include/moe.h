@@ -239,6 +239,33 @@ MOE_API moe_status moe_cache_inject_copy_failures(moe_cache* c, int n);
 /* Waits for outstanding copies, releases events; the caller's buffers are untouched. */
 MOE_API void moe_cache_destroy(moe_cache* c);
 
+/* ------------------------------------------------------------------------------------------
+ * moe_decode_step -- one decode step of an offloaded stack, every layer in one call (FreeToken
+ * linux guide, "MoE memory handling"; FreeToken GGUF page, offload backend).  For each layer,
+ * in order, on `compute`: moe_route (forced_idx may be NULL) and moe_permute into the given
+ * buffers; topk_idx copied to host_idx (pinned, T*k int32) and `compute` synchronised; the
+ * distinct ids, ascending, to moe_cache_lookup(layer); moe_cache_fill(copy, compute);
+ * moe_expert_ffn_grouped through slot_table row `layer` (the cache's slot table, device [L*E]);
+ * moe_combine into y (act dtype); moe_cache_mark_read(layer).  Outputs, cache decisions and
+ * statistics are those of the same calls made one by one.  Buffers as in those calls; y_perm
+ * [T*k (+T), d] f32; ws: moe_workspace_bytes(T, ...) bytes.  Returns the first error. */
+typedef struct {
+    const void* x;             /* [T, d] act: this layer's input (device) */
+    const void* w_router;      /* [E, d] act */
+    const float* bias;         /* [E] or NULL */
+    const int32_t* forced_idx; /* [T, k] or NULL */
+    const void* shared_w;      /* shared expert slot image or NULL */
+    void* y;                   /* [T, d] act: output (device) */
+    int32_t layer;             /* cache layer index */
+    int32_t reserved;          /* 0 */
+} moe_decode_layer;
+MOE_API moe_status moe_decode_step(moe_cache* cache, int n_layers, const moe_decode_layer* layers, int T, int d,
+                                   int f, int E, int k, moe_dtype act, moe_dtype w, const void* slot_pool,
+                                   int n_slots, size_t slot_stride, const int32_t* slot_table, int32_t* topk_idx,
+                                   float* topk_w, float* logits, int32_t* counts, int32_t* offsets, int32_t* perm,
+                                   int32_t* inv_perm, float* y_perm, void* ws, size_t ws_bytes, int32_t* host_idx,
+                                   moe_stream compute, moe_stream copy);
+
 /* Host execution of one routed expert, the CPU side of hybrid miss handling (FreeToken RTX 5090
  * page, miss split: a miss runs on the GPU after a PCIe copy or on the CPU, split by the measured
  * host and PCIe bandwidths).  slot_image: host, the expert's packed slot (moe_pack_expert layout,

@@ -128,6 +128,27 @@ def test_outputs_do_not_depend_on_capacity(runs):
             assert np.array_equal(i0, i1) and np.array_equal(y0, y1)
 
 
+def test_native_decode_step_matches_the_call_by_call_loop(runs):
+    """moe_decode_step (one call per step) makes the same calls as the Python loop over layers:
+    outputs, the cache's hit/miss sequence, copy plan and statistics are bitwise the same."""
+    from expert_offload_cache_amd.offload import OffloadStack
+
+    _, ref = runs[16]  # the fixture's decode runs through moe_decode_step
+    stack = OffloadStack(_wl(), L, 16, seed=0, n_images=IMAGES, prefill_tokens=T_PRE)
+    try:
+        stack.prefill()
+        _, dec = stack.decode(_trace(), keep_outputs=True, native=False)
+        assert np.array_equal(stack.cache.trace(), ref["trace"])
+        assert stack.cache.stats() == ref["stats"]
+        log = stack.cache.copy_log()
+        assert np.array_equal(log, ref["stack"].cache.copy_log())
+    finally:
+        stack.close()
+    assert len(dec) == len(ref["dec"]) == STEPS * L
+    for (s0, l0, y0), (s1, l1, y1) in zip(ref["dec"], dec):
+        assert (s0, l0) == (s1, l1) and np.array_equal(y0, y_to_f64(y1))
+
+
 def test_split_launch_matches_plain_decode(runs):
     """Split launches (resident experts before the copies' wait, missed ones after) change when the
     experts run, not what they compute: outputs and the cache's decisions are bitwise those of the
