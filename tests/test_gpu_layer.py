@@ -246,3 +246,54 @@ def test_dsv4_prefill_layer_sampled(dsv4_bf16_layer, T):
     err = rel_err_per_token(y, ref["y"])
     print(f"max n_e {int(c.max())} sampled max rel err {err.max():.3g}")
     assert err.max() <= 2e-2
+
+
+EDGE = [
+    # (name, act, wdt, d, f, E, k, T, shared, forced expert or None)
+    ("one expert, decode", "bf16", "bf16", 256, 128, 1, 1, 5, False, None),
+    ("one expert, prefill", "bf16", "bf16", 512, 256, 1, 1, 300, True, None),
+    ("all tokens on expert 2, bf16 prefill", "bf16", "bf16", 512, 256, 8, 1, 700, False, 2),
+    ("all tokens on expert 5, int4 prefill", "bf16", "int4", 512, 256, 8, 1, 700, True, 5),
+    ("k = E, decode (every expert holds every token)", "bf16", "bf16", 256, 96, 8, 8, 20, True, None),
+    ("1024 experts, most empty", "bf16", "bf16", 256, 64, 1024, 8, 16, False, None),
+    ("int4, k = E", "bf16", "int4", 256, 128, 4, 4, 33, False, None),
+]
+
+
+@pytest.mark.parametrize("name,act,wdt,d,f,E,k,T,shared,forced", EDGE, ids=[c[0] for c in EDGE])
+def test_degenerate_layers(name, act, wdt, d, f, E, k, T, shared, forced):
+    """Degenerate routings against the oracle: a single expert, every token on one expert (one
+    expert's chunks fill the launch, the others are empty), k = E, and a thousand mostly empty
+    experts."""
+    need_gpu()
+    from expert_offload_cache_amd.layer import DeviceLayer
+
+    print(f"edge layer: {name}", flush=True)
+    wl = small_workload(act, wdt, d, f, E, k, shared=shared, bias=1.1)
+    li = synth.layer_inputs(wl, T, seed=9)
+    layer = DeviceLayer.from_inputs(li)
+    fidx = None if forced is None else np.full((T, k), forced, dtype=np.int32)
+    out = _run(layer, li, forced=fidx)
+    ref = moe_layer(li.x, li.w_router, li.bias, act, k, E, li.experts, li.shared, forced_idx=fidx)
+    _check_ints(out, ref)
+    err = rel_err_per_token(y_to_f64(out["y"]), ref["y"])
+    print(f"max per-token rel err {err.max():.3g}")
+    assert err.max() <= tol_for(wl)
+    assert int(out["ws"][:4].view(dtype=__import__("torch").int32).item()) == 0
+
+
+def test_empty_batch_is_a_no_op():
+    """T = 0: every hot-path call returns OK; the permutation of an empty batch has zero counts and
+    offsets and writes nothing else."""
+    need_gpu()
+    import torch
+    from expert_offload_cache_amd._lib import lib, MOE_BF16
+
+    E, k, d = 8, 2, 256
+    counts = torch.full((E,), 7, dtype=torch.int32, device="cuda")
+    offsets = torch.full((E + 1,), 7, dtype=torch.int32, device="cuda")
+    assert lib().moe_route(None, MOE_BF16, 0, d, None, None, E, k, None, None, None, None, None) == 0
+    assert lib().moe_permute(None, 0, k, E, counts.data_ptr(), offsets.data_ptr(), None, None, None, 0, None) == 0
+    torch.cuda.synchronize()
+    assert counts.cpu().tolist() == [0] * E and offsets.cpu().tolist() == [0] * (E + 1)
+    assert lib().moe_combine(None, None, None, 0, k, d, 0, None, MOE_BF16, None) == 0
