@@ -11,14 +11,17 @@
 // Tiling (bf16 weights): a workgroup of 8 waves computes MT = 512 weight rows x NT = 128 tokens of
 // one expert; each wave owns 64 rows x 128 tokens.  In the gate/up launch a wave's 64 rows are 32
 // gate rows and the same 32 up rows, so SwiGLU is applied in registers before one bf16 store of h.
-// int4 weights use a 256-row variant that dequantises in registers (below).  Inputs advance 32 at a time through a ring
-// of LDS stages filled by direct-to-LDS loads (global_load_lds_dwordx4), several stages ahead of
-// the MFMAs and without passing through registers: weights are copied fragment for fragment (the
-// slot layout is the LDS layout), and token rows are gathered through the permutation straight
-// into B fragments, so every LDS read of the MFMA loop is a conflict-free 16-byte lane read.
-// Workgroup (m, n) follows (m, n-1) sixteen blocks later in dispatch order, i.e. on the same
-// XCD (blocks go round-robin over 8), so an expert's weight tile is reused from that XCD's L2
-// across its token tiles.
+// Inputs advance 32 at a time.  Each wave loads its own weight fragments (4 x 1 KB a stage, one
+// 16-byte load per lane each, already in A-operand order) straight into registers, R-1 stages
+// ahead; the token rows are gathered through the permutation straight into B fragments in a ring
+// of R LDS stages filled by direct-to-LDS loads (global_load_lds_dwordx4), shared by the 8 waves.
+// So the LDS carries only the token fragments (written once, read by every wave as conflict-free
+// 16-byte lane reads) -- measured against staging the weights in LDS too, this lifts the dense
+// contraction from 0.43 to 0.46 of the MFMA peak and moves the same bits.
+// int4 weights use a 256-row variant that dequantises in registers (below).
+// Workgroup (m, n) follows (m, n-1) M/MT blocks later in dispatch order; blocks go round-robin
+// over the 8 XCDs, so where M/MT is a multiple of 8 (the large shapes) an expert's weight tile
+// stays on one XCD and is reused from its L2 across the token tiles.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -36,23 +39,6 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
 constexpr int kKT = 32;  // inputs per stage (one fragment)
-
-// MT weight rows x NT tokens per workgroup; 8 waves as WM (rows) x 8/WM (tokens); R stages of the
-// ring in LDS.  Each stage holds the MT/16 row blocks' fragments, then the NT/16 token fragments.
-template <int MT, int NT, int WM, int R>
-struct Tile {
-    static constexpr int kWN = 8 / WM;
-    static constexpr int kRA = MT / 16 / WM;             // row blocks per wave
-    static constexpr int kRB = NT / 16 / kWN;            // token blocks per wave
-    static constexpr int kLA = MT / 128;                 // row-block fragments each wave loads per stage
-    static constexpr int kLB = NT / 128;                 // token fragments each wave loads per stage
-    static constexpr int kAStage = MT * kKT * 2;
-    static constexpr int kStage = kAStage + NT * kKT * 2;
-    static constexpr int kRing = R;
-    static constexpr int kLds = R * kStage;
-    static constexpr int kLoads = kLA + kLB;             // direct-to-LDS loads per wave per stage
-    static_assert(kRA % 2 == 0 && kRA * WM * 16 == MT && kRB * kWN * 16 == NT && R >= 3, "tile shape");
-};
 
 __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
@@ -75,135 +61,6 @@ __device__ __forceinline__ void stage_barrier() {
 __device__ __forceinline__ void load_to_lds(const uint8_t* src, uint8_t* lds_wave_base) {
     // 16 bytes per lane; lane i's bytes land at lds_wave_base + 16 i whatever its source address
     __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)lds_wave_base, 16, 0, 0);
-}
-
-template <int MODE, int MT, int NT, int WM, int R>
-__global__ __launch_bounds__(512) void ffn_mfma_kernel(FfnArgs a) {
-    using TL = Tile<MT, NT, WM, R>;
-    constexpr int RA = TL::kRA, RB = TL::kRB, LA = TL::kLA, LB = TL::kLB;
-    extern __shared__ __align__(16) uint8_t smem[];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wv % WM, wn = wv / WM;  // wave position along rows, along tokens
-    const int K = (MODE == kGateUp) ? a.d : a.f;
-    const int nks = K / kKT;  // stages
-
-    int e, chunk;
-    if (!find_work(a.counts, a.E, a.T, NT, a.shared_w != nullptr, blockIdx.y, e, chunk)) return;
-    const bool shared = e == -1;
-    const int n_all = __builtin_amdgcn_readfirstlane(shared ? a.T : a.counts[e]);
-    const int t0 = chunk * NT;
-    const int nt = __builtin_amdgcn_readfirstlane(min(NT, n_all - t0));
-    const int p0 = __builtin_amdgcn_readfirstlane(shared ? a.T * a.k : a.offsets[e]);
-    const uint8_t* base;
-    if (shared) {
-        base = a.shared_w;
-    } else {
-        const int slot = __builtin_amdgcn_readfirstlane(a.slot_of_expert[e]);
-        if (slot == MOE_SLOT_ELSEWHERE) return;  // rows produced elsewhere: leave them
-        if (slot < 0 || slot >= a.n_slots) {
-            if (tid == 0) *a.status = 1;
-            // zeros for this tile's outputs; nothing is read from the pool
-            const int rows0 = (MODE == kGateUp) ? blockIdx.x * (MT / 2) : blockIdx.x * MT;
-            const int nr = (MODE == kGateUp) ? MT / 2 : MT;
-            for (int i = tid; i < nt * nr; i += blockDim.x) {
-                const size_t row = (size_t)(p0 + t0 + i / nr);
-                const int col = rows0 + i % nr;
-                if (MODE == kGateUp) ((uint16_t*)a.h)[row * a.f + col] = 0;
-                else a.y_perm[row * a.d + col] = 0.f;
-            }
-            return;
-        }
-        base = a.pool + (size_t)slot * a.stride;
-    }
-
-    // Stage buffer layout (both operands in fragment order, 1 KB per fragment, lane l's 16 bytes
-    // at 16 l): A = the MT/16 row blocks (gate/up: g0,u0,g1,u1,...; down: d blocks), then B = the
-    // NT/16 token blocks.  Wave w fills row blocks LA*w .. +LA-1 and token blocks LB*w .. +LB-1.
-    const uint8_t* a_src[LA];
-#pragma unroll
-    for (int u = 0; u < LA; ++u) {
-        const int j = LA * wv + u;
-        if constexpr (MODE == kGateUp) a_src[u] = base + gu_block_offset(blockIdx.x * (MT / 32) + (j >> 1), j & 1, a.d, MOE_BF16);
-        else a_src[u] = base + down_block_offset(blockIdx.x * (MT / 16) + j, a.d, a.f, MOE_BF16);
-        a_src[u] += lane * 16;
-    }
-    // B fragment lane l: token 16 tb + l%16, inputs 8(l/16)..+7 of the stage.  Tokens past the
-    // tile's end read the tile's first row: MFMA columns are independent and are never stored.
-    const uint8_t* b_src[LB];
-    {
-        const uint8_t* b_base = (MODE == kGateUp) ? (const uint8_t*)a.x : (const uint8_t*)a.h;
-#pragma unroll
-        for (int u = 0; u < LB; ++u) {
-            int tok = (LB * wv + u) * 16 + (lane & 15);
-            tok = tok < nt ? tok : 0;
-            int src;
-            if (MODE == kGateUp) src = shared ? (t0 + tok) : (a.perm[p0 + t0 + tok] / a.k);
-            else src = p0 + t0 + tok;
-            b_src[u] = b_base + (size_t)src * K * 2 + (lane >> 4) * 16;
-        }
-    }
-    auto issue = [&](int ks) __attribute__((always_inline)) {
-        ks = min(ks, nks - 1);  // past the end: reload the last stage into a buffer nobody reads
-        uint8_t* buf = smem + (ks % R) * TL::kStage;
-#pragma unroll
-        for (int u = 0; u < LA; ++u) load_to_lds(a_src[u] + (size_t)ks * 1024, buf + (LA * wv + u) * 1024);
-#pragma unroll
-        for (int u = 0; u < LB; ++u)
-            load_to_lds(b_src[u] + (size_t)ks * (kKT * 2), buf + TL::kAStage + (LB * wv + u) * 1024);
-    };
-
-    f32x4_t acc[RA][RB];  // [row block of the wave][token block of the wave]
-#pragma unroll
-    for (int i = 0; i < RA; ++i)
-#pragma unroll
-        for (int j = 0; j < RB; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-
-    // R-1 stages in flight ahead of the one being multiplied; past the last stage the loads
-    // repeat the last stage (branch-free, so every wait count stays exact)
-#pragma unroll
-    for (int s = 0; s < R - 1; ++s) issue(s);
-    for (int ks = 0; ks < nks; ++ks) {
-        stage_barrier<(R - 2) * TL::kLoads>();  // stage ks landed; buffer (ks-1)%R is free
-        issue(ks + R - 1);
-        const uint8_t* sa = smem + (ks % R) * TL::kStage;
-        u32x4_t av[RA], bv[RB];
-#pragma unroll
-        for (int i = 0; i < RA; ++i) av[i] = *(const u32x4_t*)(sa + (wm * RA + i) * 1024 + lane * 16);
-#pragma unroll
-        for (int j = 0; j < RB; ++j) bv[j] = *(const u32x4_t*)(sa + TL::kAStage + (wn * RB + j) * 1024 + lane * 16);
-#pragma unroll
-        for (int j = 0; j < RB; ++j)
-#pragma unroll
-            for (int i = 0; i < RA; ++i) acc[i][j] = mfma(av[i], bv[j], acc[i][j]);
-    }
-    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));  // drain the tail reloads (vmcnt(0))
-
-    // ---- epilogue --------------------------------------------------------------------------
-    const int quad = lane >> 4;  // C rows 4*quad .. +3 of each 16-row tile
-#pragma unroll
-    for (int j = 0; j < RB; ++j) {
-        const int tok = (wn * RB + j) * 16 + (lane & 15);
-        if (tok >= nt) continue;
-        const size_t row = (size_t)(p0 + t0 + tok);
-        if constexpr (MODE == kGateUp) {
-#pragma unroll
-            for (int i2 = 0; i2 < RA / 2; ++i2) {  // wave row blocks (g, u) pairs: (2 i2, 2 i2 + 1)
-                const f32x4_t g = acc[2 * i2][j], u = acc[2 * i2 + 1][j];
-                const int col = (blockIdx.x * (MT / 32) + (wm * RA) / 2 + i2) * 16 + quad * 4;
-                uint2 o;
-                o.x = (uint32_t)f32_to_bf16(silu_mul(g[0], u[0])) | ((uint32_t)f32_to_bf16(silu_mul(g[1], u[1])) << 16);
-                o.y = (uint32_t)f32_to_bf16(silu_mul(g[2], u[2])) | ((uint32_t)f32_to_bf16(silu_mul(g[3], u[3])) << 16);
-                *(uint2*)((uint16_t*)a.h + row * a.f + col) = o;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < RA; ++i) {
-                const int col = (blockIdx.x * (MT / 16) + wm * RA + i) * 16 + quad * 4;
-                *(float4*)(a.y_perm + row * a.d + col) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-            }
-        }
-    }
 }
 
 // int4 weights.  A fragment of the slot layout holds 16 rows x 128 inputs (1 KB); lane l's word s
@@ -394,14 +251,149 @@ __global__ __launch_bounds__(512) void ffn_mfma_int4_kernel(FfnArgs a) {
     }
 }
 
+// bf16 weights with the A operands in registers: each wave loads its own weight fragments
+// (RA row blocks x 1 KB a stage) straight into one of R register sets, the same R-1 stages ahead as
+// the token ring; only the token rows go through LDS, so the LDS carries B reads and DMA writes
+// only.
 template <int MODE, int MT, int NT, int WM, int R>
-moe_status launch_int4(const FfnArgs& a, hipStream_t st, const char* name) {
+__global__ __launch_bounds__(512) void ffn_mfma_areg_kernel(FfnArgs a) {
+    using TL = Tile4<MT, NT, WM, R>;
+    constexpr int RA = TL::kRA, RB = TL::kRB, LB = TL::kLB;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv % WM, wn = wv / WM;
+    const int K = (MODE == kGateUp) ? a.d : a.f;
+    const int nks = K / kKT;
+
+    int e, chunk;
+    if (!find_work(a.counts, a.E, a.T, NT, a.shared_w != nullptr, blockIdx.y, e, chunk)) return;
+    const bool shared = e == -1;
+    const int n_all = __builtin_amdgcn_readfirstlane(shared ? a.T : a.counts[e]);
+    const int t0 = chunk * NT;
+    const int nt = __builtin_amdgcn_readfirstlane(min(NT, n_all - t0));
+    const int p0 = __builtin_amdgcn_readfirstlane(shared ? a.T * a.k : a.offsets[e]);
+    const uint8_t* base;
+    if (shared) {
+        base = a.shared_w;
+    } else {
+        const int slot = __builtin_amdgcn_readfirstlane(a.slot_of_expert[e]);
+        if (slot == MOE_SLOT_ELSEWHERE) return;
+        if (slot < 0 || slot >= a.n_slots) {
+            if (tid == 0) *a.status = 1;
+            const int rows0 = (MODE == kGateUp) ? blockIdx.x * (MT / 2) : blockIdx.x * MT;
+            const int nr = (MODE == kGateUp) ? MT / 2 : MT;
+            for (int i = tid; i < nt * nr; i += blockDim.x) {
+                const size_t row = (size_t)(p0 + t0 + i / nr);
+                const int col = rows0 + i % nr;
+                if (MODE == kGateUp) ((uint16_t*)a.h)[row * a.f + col] = 0;
+                else a.y_perm[row * a.d + col] = 0.f;
+            }
+            return;
+        }
+        base = a.pool + (size_t)slot * a.stride;
+    }
+    const uint8_t* a_blk[RA];
+#pragma unroll
+    for (int u = 0; u < RA; ++u) {
+        const int j = wm * RA + u;
+        if constexpr (MODE == kGateUp)
+            a_blk[u] = base + gu_block_offset(blockIdx.x * (MT / 32) + (j >> 1), j & 1, a.d, MOE_BF16) + lane * 16;
+        else
+            a_blk[u] = base + down_block_offset(blockIdx.x * (MT / 16) + j, a.d, a.f, MOE_BF16) + lane * 16;
+    }
+    const uint8_t* b_src[LB];
+    {
+        const uint8_t* b_base = (MODE == kGateUp) ? (const uint8_t*)a.x : (const uint8_t*)a.h;
+#pragma unroll
+        for (int u = 0; u < LB; ++u) {
+            int tok = (LB * wv + u) * 16 + (lane & 15);
+            tok = tok < nt ? tok : 0;
+            int src;
+            if (MODE == kGateUp) src = shared ? (t0 + tok) : (a.perm[p0 + t0 + tok] / a.k);
+            else src = p0 + t0 + tok;
+            b_src[u] = b_base + (size_t)src * K * 2 + (lane >> 4) * 16;
+        }
+    }
+    u32x4_t areg[R][RA];
+    // stage ks: the token fragments to LDS buffer ks % R, then this wave's weight fragments to
+    // register set `set` (== ks % R); past the end both repeat the last stage (never used)
+    auto issue = [&](int ks, u32x4_t (&set)[RA]) __attribute__((always_inline)) {
+        ks = min(ks, nks - 1);
+        uint8_t* buf = smem + (ks % R) * TL::kStage;
+#pragma unroll
+        for (int u = 0; u < LB; ++u) load_to_lds(b_src[u] + (size_t)ks * (kKT * 2), buf + (LB * wv + u) * 1024);
+#pragma unroll
+        for (int u = 0; u < RA; ++u) set[u] = __builtin_nontemporal_load((const u32x4_t*)(a_blk[u] + (size_t)ks * 1024));
+    };
+
+    f32x4_t acc[RA][RB];
+#pragma unroll
+    for (int i = 0; i < RA; ++i)
+#pragma unroll
+        for (int j = 0; j < RB; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    auto step = [&](int ks, const u32x4_t (&cur)[RA], u32x4_t (&ahead)[RA]) __attribute__((always_inline)) {
+        // stage ks landed (its token rows for every wave, its weights for this wave); the younger
+        // loads are the R-2 later stages' LB + RA loads
+        stage_barrier<(R - 2) * (LB + RA)>();
+        issue(ks + R - 1, ahead);
+        const uint8_t* sb = smem + (ks % R) * TL::kStage;
+        u32x4_t bv[RB];
+#pragma unroll
+        for (int j = 0; j < RB; ++j) bv[j] = *(const u32x4_t*)(sb + (wn * RB + j) * 1024 + lane * 16);
+#pragma unroll
+        for (int j = 0; j < RB; ++j)
+#pragma unroll
+            for (int i = 0; i < RA; ++i) acc[i][j] = mfma(cur[i], bv[j], acc[i][j]);
+    };
+    static_assert(R == 3, "register sets rotate by three");
+    issue(0, areg[0]);
+    issue(1, areg[1]);
+    int ks = 0;
+    for (; ks + 3 <= nks; ks += 3) {
+        step(ks, areg[0], areg[2]);
+        step(ks + 1, areg[1], areg[0]);
+        step(ks + 2, areg[2], areg[1]);
+    }
+    if (ks < nks) step(ks, areg[0], areg[2]);
+    if (ks + 1 < nks) step(ks + 1, areg[1], areg[0]);
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
+
+    const int quad = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+        const int tok = (wn * RB + j) * 16 + (lane & 15);
+        if (tok >= nt) continue;
+        const size_t row = (size_t)(p0 + t0 + tok);
+        if constexpr (MODE == kGateUp) {
+#pragma unroll
+            for (int i2 = 0; i2 < RA / 2; ++i2) {
+                const f32x4_t g = acc[2 * i2][j], u = acc[2 * i2 + 1][j];
+                const int col = (blockIdx.x * (MT / 32) + (wm * RA) / 2 + i2) * 16 + quad * 4;
+                uint2 o;
+                o.x = (uint32_t)f32_to_bf16(silu_mul(g[0], u[0])) | ((uint32_t)f32_to_bf16(silu_mul(g[1], u[1])) << 16);
+                o.y = (uint32_t)f32_to_bf16(silu_mul(g[2], u[2])) | ((uint32_t)f32_to_bf16(silu_mul(g[3], u[3])) << 16);
+                *(uint2*)((uint16_t*)a.h + row * a.f + col) = o;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < RA; ++i) {
+                const int col = (blockIdx.x * (MT / 16) + wm * RA + i) * 16 + quad * 4;
+                *(float4*)(a.y_perm + row * a.d + col) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+            }
+        }
+    }
+}
+
+template <int MODE, int MT, int NT, int WM, int R>
+moe_status launch_areg(const FfnArgs& a, hipStream_t st, const char* name) {
     using TL = Tile4<MT, NT, WM, R>;
     const int M = (MODE == kGateUp) ? 2 * a.f : a.d;
     const int64_t tk = (int64_t)a.T * a.k;
     const int64_t items = (tk + NT - 1) / NT + std::min<int64_t>(a.E, tk) + (a.shared_w ? (a.T + NT - 1) / NT : 0);
     if (items > 65535) return set_error(MOE_ESHAPE, "%s: %lld token tiles exceed one launch", name, (long long)items);
-    auto kern = ffn_mfma_int4_kernel<MODE, MT, NT, WM, R>;
+    auto kern = ffn_mfma_areg_kernel<MODE, MT, NT, WM, R>;
     MOE_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, TL::kLds));
     dim3 grid((unsigned)(M / MT), (unsigned)items);
     ProfScope p(name, st);
@@ -410,13 +402,13 @@ moe_status launch_int4(const FfnArgs& a, hipStream_t st, const char* name) {
 }
 
 template <int MODE, int MT, int NT, int WM, int R>
-moe_status launch(const FfnArgs& a, hipStream_t st, const char* name) {
-    using TL = Tile<MT, NT, WM, R>;
-    const int M = (MODE == kGateUp) ? 2 * a.f : a.d;  // weight rows (gate and up together)
+moe_status launch_int4(const FfnArgs& a, hipStream_t st, const char* name) {
+    using TL = Tile4<MT, NT, WM, R>;
+    const int M = (MODE == kGateUp) ? 2 * a.f : a.d;
     const int64_t tk = (int64_t)a.T * a.k;
     const int64_t items = (tk + NT - 1) / NT + std::min<int64_t>(a.E, tk) + (a.shared_w ? (a.T + NT - 1) / NT : 0);
     if (items > 65535) return set_error(MOE_ESHAPE, "%s: %lld token tiles exceed one launch", name, (long long)items);
-    auto kern = ffn_mfma_kernel<MODE, MT, NT, WM, R>;
+    auto kern = ffn_mfma_int4_kernel<MODE, MT, NT, WM, R>;
     MOE_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, TL::kLds));
     dim3 grid((unsigned)(M / MT), (unsigned)items);
     ProfScope p(name, st);
@@ -461,9 +453,9 @@ moe_status ffn_mfma(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st
     }
     if (w != MOE_BF16) return MOE_EDTYPE;
     if ((2 * a.f) % MT || a.d % MT) return MOE_EDTYPE;
-    moe_status r = launch<kGateUp, MT, NT, WM, R>(a, st, "ffn_mfma_gateup_bf16");
+    moe_status r = launch_areg<kGateUp, MT, NT, WM, R>(a, st, "ffn_mfma_gateup_bf16");
     if (r != MOE_OK) return r;
-    return launch<kDown, MT, NT, WM, R>(a, st, "ffn_mfma_down_bf16");
+    return launch_areg<kDown, MT, NT, WM, R>(a, st, "ffn_mfma_down_bf16");
 }
 
 }  // namespace moe
