@@ -304,14 +304,18 @@ __device__ void select_and_gate(const float* s_logit, int E, int k, const int32_
         }
     }
     __syncthreads();
-    // gates: softmax over the selected logits in binary64, rounded once
+    // gates: softmax over the selected logits in binary64, rounded once.  Thread j forms its own
+    // term exp(v_j - max) once; every thread then sums the k terms in ascending order.
+    __shared__ double s_term[1024];
+    double m = -INFINITY;
+    for (int i = 0; i < k; ++i) m = fmax(m, (double)s_val[i]);
+    for (int j = tid; j < k; j += nth) s_term[j] = exp((double)s_val[j] - m);
+    __syncthreads();
     for (int j = tid; j < k; j += nth) {
-        double m = -INFINITY;
-        for (int i = 0; i < k; ++i) m = fmax(m, (double)s_val[i]);
         double den = 0.0;
-        for (int i = 0; i < k; ++i) den += exp((double)s_val[i] - m);
+        for (int i = 0; i < k; ++i) den += s_term[i];
         idx_out[j] = s_sel[j];
-        w_out[j] = (float)(exp((double)s_val[j] - m) / den);
+        w_out[j] = (float)(s_term[j] / den);
     }
 }
 
