@@ -78,6 +78,26 @@ def test_host_validation_needs_no_gpu(moe):
     assert L.moe_expert_ffn_grouped(ctypes.c_void_p(256), 1, 4, 2048, 768, 128, 8, vp, vp, vp, vp, 128,
                                     ctypes.c_void_p(256), 9437184, 1, None, ctypes.c_void_p(256),
                                     ctypes.c_void_p(256), ws_need - 1, None) == moe._lib.MOE_ENOMEM
+    # the decode step checks its arguments before any call: no cache, no layers, bad shapes
+    # (after slot_table: topk_idx .. ws = 9 buffers, ws_bytes, host_idx, compute, copy)
+    bufs = [None] * 9
+
+    def step(cache, n, layers, k, host_idx):
+        return L.moe_decode_step(cache, n, layers, 1, 256, 128, 8, k, 1, 1, vp, 4, 4096, vp, *bufs, 0, host_idx,
+                                 None, None)
+
+    assert step(None, 1, vp, 2, vp) == moe._lib.MOE_EINVAL
+    c = moe.SlotCache(2, 8, 4)  # policy-only cache: a real handle, no device memory
+    try:
+        assert step(c.h, 1, None, 2, vp) == moe._lib.MOE_EINVAL
+        layers = np.zeros(1, dtype=moe.DECODE_LAYER)
+        assert moe.DECODE_LAYER.itemsize == 6 * 8 + 2 * 4  # moe_decode_layer: six pointers, two int32
+        assert step(c.h, 1, layers.ctypes.data, 9, vp) == moe._lib.MOE_ESHAPE  # k > E
+        # a layer without its input is refused before anything is enqueued
+        assert step(c.h, 1, layers.ctypes.data, 2, vp) == moe._lib.MOE_EINVAL
+        assert step(c.h, 0, layers.ctypes.data, 2, vp) == 0  # zero layers: nothing to do
+    finally:
+        c.close()
 
 
 def _unpack_dense(img, R, K, dt):
