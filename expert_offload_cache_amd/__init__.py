@@ -176,6 +176,25 @@ def decode_step(cache, layers: np.ndarray, T: int, d: int, f: int, E: int, k: in
                                 _s(compute), _s(copy)))
 
 
+
+def decode_step_hybrid(cache, layers: np.ndarray, d: int, f: int, E: int, k: int, act: int, wdt: str, slot_pool,
+                       n_slots: int, slot_stride: int, slot_table, route_bufs, perm_bufs, y_perm, ws, host_idx,
+                       host_x, host_y, host_table, dev_table, cpu_rate: float, pcie_rate: float, copy_too: bool,
+                       compute, copy, cpu_threads: int = 0) -> int:
+    """One batch-1 decode step of every layer in `layers` with hybrid miss handling
+    (moe_decode_step_hybrid).  host_idx/host_x/host_y/host_table: pinned host tensors; dev_table:
+    device int32 [E].  -> number of experts run on the host."""
+    idx, w, logits = route_bufs
+    c, o, p, ip = perm_bufs
+    n_cpu = ctypes.c_int64(0)
+    check(lib().moe_decode_step_hybrid(cache.h, len(layers), layers.ctypes.data, d, f, E, k, act, WDT[wdt],
+                                       _p(slot_pool), n_slots, slot_stride, _p(slot_table), _p(idx), _p(w),
+                                       _p(logits), _p(c), _p(o), _p(p), _p(ip), _p(y_perm), _p(ws), ws.numel(),
+                                       host_idx.data_ptr(), host_x.data_ptr(), host_y.data_ptr(),
+                                       host_table.data_ptr(), _p(dev_table), float(cpu_rate), float(pcie_rate),
+                                       int(bool(copy_too)), cpu_threads, ctypes.byref(n_cpu), _s(compute), _s(copy)))
+    return n_cpu.value
+
 # ---------------------------------------------------------------------------------------------
 # expert-slot cache
 # ---------------------------------------------------------------------------------------------

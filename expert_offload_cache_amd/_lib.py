@@ -28,6 +28,9 @@ SIGNATURES = {
     "moe_combine": (_st, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
     "moe_decode_step": (_st, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _sz, _vp, _vp, _vp,
                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
+    "moe_decode_step_hybrid": (_st, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _sz, _vp, _vp,
+                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp,
+                                     ctypes.c_double, ctypes.c_double, _i32, _i32, _vp, _vp, _vp]),
     "moe_cache_create": (_st, [_i32, _i32, _i32, _sz, _vp, _vp, _vp, ctypes.POINTER(_vp)]),
     "moe_cache_lookup": (_st, [_vp, _i32, _vp, _i32, _vp, _vp]),
     "moe_cache_fill": (_st, [_vp, _vp, _vp]),

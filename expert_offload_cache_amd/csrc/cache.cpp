@@ -510,6 +510,17 @@ moe_status moe_cache_slot_of(const moe_cache* c, int layer, int expert, int32_t*
     return MOE_OK;
 }
 
+}  // extern "C"
+
+namespace moe {
+// Pinned host image of (layer, expert), or nullptr (policy-only cache).  Library-internal.
+const void* cache_host_image(const moe_cache* c, int layer, int expert) {
+    if (!c || !c->host || layer < 0 || layer >= c->L || expert < 0 || expert >= c->E) return nullptr;
+    return c->host[(size_t)layer * c->E + expert];
+}
+}  // namespace moe
+
+extern "C" {
 void moe_cache_destroy(moe_cache* c) {
     if (!c) return;
     if (!c->policy_only) {

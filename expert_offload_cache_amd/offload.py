@@ -246,8 +246,9 @@ class OffloadStack:
         `first_step` numbers the trace's first row (it selects the activations), so a trace can be
         replayed in pieces, e.g. around a resize.
 
-        `native` (the plain mode): each step is one moe_decode_step call, which makes the same
-        library calls per layer without the Python marshalling between them.
+        `native` (plain and hybrid modes): each step is one moe_decode_step (or
+        moe_decode_step_hybrid) call, which makes the same library calls per layer without the
+        Python marshalling between them; native=False runs the same calls from this loop.
 
         `split_launch`: a layer with misses runs its hit experts before waiting for the copies (the
         misses marked as produced elsewhere), then the missed experts after them, then the combine.
@@ -270,8 +271,8 @@ class OffloadStack:
         done = torch.cuda.Event()
         outs = []
         nb = self.x_dec[0].shape[0]
-        if native and not hybrid and not split_launch:
-            return self._decode_native(forced, steps, first_step, keep_outputs)
+        if native and not split_launch:
+            return self._decode_native(forced, steps, first_step, keep_outputs, hybrid)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         if hybrid or split_launch:
@@ -360,10 +361,10 @@ class OffloadStack:
         el = time.perf_counter() - t0
         return (el, outs) if keep_outputs else el
 
-    def _decode_native(self, forced, steps: int, first_step: int, keep_outputs: bool):
-        """decode() in the plain mode, one moe_decode_step call per step."""
+    def _decode_native(self, forced, steps: int, first_step: int, keep_outputs: bool, hybrid=None):
+        """decode() in the plain or hybrid mode, one moe_decode_step(_hybrid) call per step."""
         import torch
-        from . import DECODE_LAYER, decode_step
+        from . import DECODE_LAYER, decode_step, decode_step_hybrid
 
         L, E, k, d = self.L, self.E, self.k, self.d
         nb = self.x_dec[0].shape[0]
@@ -383,13 +384,25 @@ class OffloadStack:
         arr["y"] = np.array([y.data_ptr() for y in ys], dtype=np.uint64)[None, :]
         arr["layer"] = np.arange(L, dtype=np.int32)[None, :]
         outs = []
+        if hybrid:
+            host_x = torch.empty((1, d), dtype=torch.int16, pin_memory=True)
+            host_y = torch.empty((k, d), dtype=torch.float32, pin_memory=True)
+            host_tab = torch.full((E,), -1, dtype=torch.int32, pin_memory=True)
+            dev_tab = torch.empty(E, dtype=torch.int32, device=self.device)
+            copy_too = hybrid[2] if len(hybrid) > 2 else True
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         with torch.cuda.stream(self.compute):
             for s in range(steps):
-                decode_step(self.cache, arr[s], 1, d, self.f, E, k, self.act_code, self.wl.wdt, self.slot_pool,
-                            self.n_slots, self.stride, self.slot_table, b["route"], b["perm"], b["y_perm"], ws,
-                            self._host_idx, self.compute, self.copy)
+                if hybrid:
+                    self.cpu_experts += decode_step_hybrid(
+                        self.cache, arr[s], d, self.f, E, k, self.act_code, self.wl.wdt, self.slot_pool, self.n_slots,
+                        self.stride, self.slot_table, b["route"], b["perm"], b["y_perm"], ws, self._host_idx, host_x,
+                        host_y, host_tab, dev_tab, hybrid[0], hybrid[1], copy_too, self.compute, self.copy)
+                else:
+                    decode_step(self.cache, arr[s], 1, d, self.f, E, k, self.act_code, self.wl.wdt, self.slot_pool,
+                                self.n_slots, self.stride, self.slot_table, b["route"], b["perm"], b["y_perm"], ws,
+                                self._host_idx, self.compute, self.copy)
                 if keep_outputs:
                     outs += [(first_step + s, l, ys[l].clone()) for l in range(L)]
         self.compute.synchronize()

@@ -266,6 +266,28 @@ MOE_API moe_status moe_decode_step(moe_cache* cache, int n_layers, const moe_dec
                                    int32_t* inv_perm, float* y_perm, void* ws, size_t ws_bytes, int32_t* host_idx,
                                    moe_stream compute, moe_stream copy);
 
+/* moe_decode_step with hybrid miss handling (FreeToken RTX 5090 page, miss split; stork.ai
+ * article, miss policy), one token per step (T = 1, bf16 activations).  Per layer, after the ids
+ * and x reach the host (host_idx: k int32, host_x: d bf16, both pinned): the layer's m misses are
+ * split, the host taking the n highest-numbered ones, n minimising max((m-n)/pcie_rate, n/cpu_rate)
+ * (rates in expert images per second; ties to fewer on the host); the other ids (all of them
+ * with copy_too, whose host experts are then also inserted, their copies deferred through
+ * moe_cache_fill_split) go to moe_cache_lookup and a fill; the layer's table row is staged in
+ * host_table (pinned, E int32) and copied to dev_table (device, E int32) with the host experts
+ * marked MOE_SLOT_ELSEWHERE; the GPU experts are enqueued; each host expert runs
+ * moe_cpu_expert_ffn on its pinned image (cpu_threads, 0 = all) into host_y (pinned, k*d f32) and
+ * its row is copied into y_perm; then moe_combine and mark_read.  *n_cpu_out (if not NULL) is
+ * increased by the number of host-run experts.  Other arguments as moe_decode_step. */
+MOE_API moe_status moe_decode_step_hybrid(moe_cache* cache, int n_layers, const moe_decode_layer* layers, int d,
+                                          int f, int E, int k, moe_dtype act, moe_dtype w, const void* slot_pool,
+                                          int n_slots, size_t slot_stride, const int32_t* slot_table,
+                                          int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts,
+                                          int32_t* offsets, int32_t* perm, int32_t* inv_perm, float* y_perm,
+                                          void* ws, size_t ws_bytes, int32_t* host_idx, void* host_x, float* host_y,
+                                          int32_t* host_table, int32_t* dev_table, double cpu_rate,
+                                          double pcie_rate, int copy_too, int cpu_threads, int64_t* n_cpu_out,
+                                          moe_stream compute, moe_stream copy);
+
 /* Host execution of one routed expert, the CPU side of hybrid miss handling (FreeToken RTX 5090
  * page, miss split: a miss runs on the GPU after a PCIe copy or on the CPU, split by the measured
  * host and PCIe bandwidths).  slot_image: host, the expert's packed slot (moe_pack_expert layout,

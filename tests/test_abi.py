@@ -96,6 +96,19 @@ def test_host_validation_needs_no_gpu(moe):
         # a layer without its input is refused before anything is enqueued
         assert step(c.h, 1, layers.ctypes.data, 2, vp) == moe._lib.MOE_EINVAL
         assert step(c.h, 0, layers.ctypes.data, 2, vp) == 0  # zero layers: nothing to do
+
+        # the hybrid step: (after slot_table) 9 buffers, ws_bytes, host_idx, host_x, host_y,
+        # host_table, dev_table, cpu_rate, pcie_rate, copy_too, threads, n_cpu_out, compute, copy
+        def hstep(n, k, act, host):
+            return L.moe_decode_step_hybrid(c.h, n, layers.ctypes.data, 256, 128, 8, k, act, 1, vp, 4, 4096, vp,
+                                            *bufs, 0, host, host, host, host, host, 1.0, 1.0, 1, 0, None, None,
+                                            None)
+
+        assert hstep(1, 2, 1, None) == moe._lib.MOE_EINVAL  # no pinned staging buffers
+        assert hstep(1, 2, 0, vp) == moe._lib.MOE_ESHAPE  # f32 activations
+        assert hstep(1, 9, 1, vp) == moe._lib.MOE_ESHAPE  # k > E
+        assert hstep(1, 2, 1, vp) == moe._lib.MOE_EINVAL  # a layer without its input
+        assert hstep(0, 2, 1, vp) == 0
     finally:
         c.close()
 

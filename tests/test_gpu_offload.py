@@ -260,6 +260,33 @@ def test_hybrid_miss_split(copy_too):
     assert worst <= 2e-2
 
 
+@pytest.mark.parametrize("copy_too", [True, False])
+def test_native_hybrid_matches_the_call_by_call_loop(copy_too):
+    """moe_decode_step_hybrid makes the hybrid loop's calls: outputs, the cache's hit/miss
+    sequence, copy plan and the number of host-run experts are bitwise those of the Python loop."""
+    need_gpu()
+    from expert_offload_cache_amd.offload import OffloadStack
+
+    wl, trace = _wl(), _trace()
+    rates = (1.0, 1.0, copy_too)
+    got = []
+    for native in (True, False):
+        stack = OffloadStack(wl, L, 16, seed=0, n_images=IMAGES, prefill_tokens=T_PRE)
+        try:
+            stack.prefill()
+            _, dec = stack.decode(trace, keep_outputs=True, hybrid=rates, native=native)
+            got.append((stack.cache.trace(), stack.cache.copy_log(), stack.cache.stats(), stack.cpu_experts,
+                        [(s, l, y_to_f64(y)) for s, l, y in dec]))
+        finally:
+            stack.close()
+    (t0, c0, st0, n0, d0), (t1, c1, st1, n1, d1) = got
+    assert np.array_equal(t0, t1) and np.array_equal(c0, c1) and st0 == st1
+    assert n0 == n1 > 0
+    assert len(d0) == len(d1) == STEPS * L
+    for (s0, l0, y0), (s1, l1, y1) in zip(d0, d1):
+        assert (s0, l0) == (s1, l1) and np.array_equal(y0, y1)
+
+
 def test_hybrid_split_rule():
     from expert_offload_cache_amd.offload import hybrid_split
 
