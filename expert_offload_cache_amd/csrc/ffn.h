@@ -27,9 +27,12 @@ constexpr size_t kPlanBytes = 1 << 16;
 
 // decode path: grouped GEMV kernels (ffn_gemv.hip)
 moe_status ffn_gemv(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st);
-// decode path, bf16 x bf16 on the matrix cores (ffn_gemv_mfma.hip); MOE_EDTYPE (nothing launched)
-// for shapes it does not cover
-moe_status ffn_gemv_mfma(const FfnArgs& a, hipStream_t st);
+// The decode kernels below launch one projection (mode kGateUp = 0 or kDown = 1) and return
+// MOE_EDTYPE, with nothing launched, for shapes they do not cover.
+// bf16 x bf16, weights held in registers, inputs split over the waves (ffn_gemv_mfma.hip)
+moe_status ffn_gemv_mfma(const FfnArgs& a, int mode, hipStream_t st);
+// bf16 or int4 weights x bf16 activations, K streamed through each wave (ffn_gemv_ks.hip)
+moe_status ffn_gemv_ks(const FfnArgs& a, int mode, moe_dtype w, hipStream_t st);
 // prefill path: MFMA grouped GEMM (ffn_mfma.hip); returns MOE_EDTYPE when it does not apply
 moe_status ffn_mfma(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st);
 

@@ -1,6 +1,8 @@
 // Grouped SwiGLU experts for few tokens per expert (decode): streaming GEMV over expert slots on
-// the vector ALUs.  It serves int4 and binary32 weights, and bf16 shapes the matrix-core decode
-// kernel (ffn_gemv_mfma.hip) does not cover (more than 8 fragments a wave).
+// the vector ALUs, and the dispatch between the decode kernels.  Each projection goes to the
+// K-streaming matrix-core kernel (ffn_gemv_ks.hip) where its launch plan applies, else for bf16
+// to the split-input matrix-core kernel (ffn_gemv_mfma.hip), else to the kernel below, which
+// serves binary32 weights, int4 weights for single tokens, and shapes the others do not cover.
 //
 // Expert weights are reached through the slot table (FreeToken GGUF page, "MoE backends",
 // offload backend: GPU expert slots; FreeToken linux guide, memory tier table).  The expert
@@ -289,13 +291,21 @@ moe_status launch(const FfnArgs& a, hipStream_t st, const char* name) {
 moe_status ffn_gemv(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st) {
     moe_status r;
     if (w == MOE_BF16 && act == MOE_BF16) {
-        r = ffn_gemv_mfma(a, st);
-        if (r != MOE_EDTYPE) return r;
-        r = launch<kGateUp, MOE_BF16, true>(a, st, "ffn_gemv_gateup_bf16");
-        if (r == MOE_OK) r = launch<kDown, MOE_BF16, true>(a, st, "ffn_gemv_down_bf16");
+        // each projection: the K-streaming kernel where it applies, else the split-input
+        // matrix-core kernel, else the vector-ALU kernel
+        r = ffn_gemv_ks(a, kGateUp, MOE_BF16, st);
+        if (r == MOE_EDTYPE) r = ffn_gemv_mfma(a, kGateUp, st);
+        if (r == MOE_EDTYPE) r = launch<kGateUp, MOE_BF16, true>(a, st, "ffn_gemv_gateup_bf16");
+        if (r != MOE_OK) return r;
+        r = ffn_gemv_ks(a, kDown, MOE_BF16, st);
+        if (r == MOE_EDTYPE) r = ffn_gemv_mfma(a, kDown, st);
+        if (r == MOE_EDTYPE) r = launch<kDown, MOE_BF16, true>(a, st, "ffn_gemv_down_bf16");
     } else if (w == MOE_INT4_G128 && act == MOE_BF16) {
-        r = launch<kGateUp, MOE_INT4_G128, true>(a, st, "ffn_gemv_gateup_int4");
-        if (r == MOE_OK) r = launch<kDown, MOE_INT4_G128, true>(a, st, "ffn_gemv_down_int4");
+        r = ffn_gemv_ks(a, kGateUp, MOE_INT4_G128, st);
+        if (r == MOE_EDTYPE) r = launch<kGateUp, MOE_INT4_G128, true>(a, st, "ffn_gemv_gateup_int4");
+        if (r != MOE_OK) return r;
+        r = ffn_gemv_ks(a, kDown, MOE_INT4_G128, st);
+        if (r == MOE_EDTYPE) r = launch<kDown, MOE_INT4_G128, true>(a, st, "ffn_gemv_down_int4");
     } else if (w == MOE_F32 && act == MOE_F32) {
         r = launch<kGateUp, MOE_F32, false>(a, st, "ffn_gemv_gateup_f32");
         if (r == MOE_OK) r = launch<kDown, MOE_F32, false>(a, st, "ffn_gemv_down_f32");

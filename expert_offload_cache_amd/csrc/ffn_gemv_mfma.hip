@@ -250,12 +250,14 @@ moe_status launch(const FfnArgs& a, hipStream_t st, const char* name) {
 
 }  // namespace
 
-moe_status ffn_gemv_mfma(const FfnArgs& a, hipStream_t st) {
+moe_status ffn_gemv_mfma(const FfnArgs& a, int mode, hipStream_t st) {
     // shapes beyond 8 fragments a wave (gate/up K > 2048 inputs, down K > 4096) are not covered
-    if (!mplan_for(kGateUp, a.f, a.d, a.T).fpw || !mplan_for(kDown, a.d, a.f, a.T).fpw) return MOE_EDTYPE;
-    moe_status r = launch<kGateUp>(a, st, "ffn_gemv_gateup_bf16");
-    if (r == MOE_OK) r = launch<kDown>(a, st, "ffn_gemv_down_bf16");
-    return r;
+    if (mode == kGateUp) {
+        if (!mplan_for(kGateUp, a.f, a.d, a.T).fpw) return MOE_EDTYPE;
+        return launch<kGateUp>(a, st, "ffn_gemv_gateup_bf16");
+    }
+    if (!mplan_for(kDown, a.d, a.f, a.T).fpw) return MOE_EDTYPE;
+    return launch<kDown>(a, st, "ffn_gemv_down_bf16");
 }
 
 }  // namespace moe

@@ -38,8 +38,17 @@ SMALL = [
     ("bf16", "bf16", 128, 64, 4, 4, 1, True),
     # decode path on the matrix cores: several 16-token groups per workgroup (shared expert: 3)
     ("bf16", "bf16", 384, 64, 4, 2, 40, True),
-    # gate/up K = 4096 inputs: beyond the matrix-core decode shapes, the VALU kernel runs
+    # gate/up K = 4096 inputs: the K-streaming kernel (beyond the split-input kernel's shapes)
     ("bf16", "bf16", 4096, 64, 4, 2, 3, False),
+    # gate/up K = 4096 inputs with more than 16 tokens: the VALU kernel runs it
+    ("bf16", "bf16", 4096, 64, 4, 2, 20, False),
+    # 20 down row blocks: the 32-token down plan does not divide them, the split-input kernel runs
+    ("bf16", "bf16", 320, 96, 8, 2, 9, True),
+    # int4 decode: K-streaming for both projections, experts spanning several 16-token items
+    ("bf16", "int4", 512, 512, 8, 2, 20, True),
+    # int4, one token: the VALU kernel
+    ("bf16", "int4", 512, 256, 8, 3, 1, True),
+    # int4, f = 128: the down projection's input split does not apply, the VALU kernel runs it
     ("bf16", "int4", 256, 128, 8, 2, 5, True),
     ("bf16", "int4", 512, 256, 16, 4, 67, False),
     # int4 with many tokens per expert: the int4 MFMA grouped GEMM (down: an odd number of groups)
