@@ -87,7 +87,7 @@ def cpu_baseline(wl, li, T, budget_s):
         moe_layer(xb, li.w_router, li.bias, wl.act, wl.k, wl.E, li.experts)
         calls += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or calls >= 50:
+        if el >= budget_s or calls >= 1000:
             break
     return {"value": calls * T / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{calls} layer calls of {T} tokens of the headline layer (float64 numpy/BLAS oracle, {el:.1f} s)"}
