@@ -17,13 +17,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (c >= d) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        const float gj = g[(size_t)t * k + j];
-        const float4 v = *(const float4*)(yp + (size_t)inv[(size_t)t * k + j] * d + c);
-        acc.x = __builtin_fmaf(gj, v.x, acc.x);
-        acc.y = __builtin_fmaf(gj, v.y, acc.y);
-        acc.z = __builtin_fmaf(gj, v.z, acc.z);
-        acc.w = __builtin_fmaf(gj, v.w, acc.w);
+    // 8 experts at a time: their indices and gates, then their rows, are loaded together; the
+    // products are added in ascending j as before
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        int idx[8];
+        float gj[8];
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = min(j0 + u, k - 1);
+            idx[u] = inv[(size_t)t * k + j];
+            gj[u] = g[(size_t)t * k + j];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = *(const float4*)(yp + (size_t)idx[u] * d + c);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (j0 + u < k) {
+                acc.x = __builtin_fmaf(gj[u], v[u].x, acc.x);
+                acc.y = __builtin_fmaf(gj[u], v[u].y, acc.y);
+                acc.z = __builtin_fmaf(gj[u], v[u].z, acc.z);
+                acc.w = __builtin_fmaf(gj[u], v[u].w, acc.w);
+            }
+        }
     }
     if (has_shared) {
         const float4 v = *(const float4*)(yp + ((size_t)T * k + t) * d + c);

@@ -130,8 +130,9 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
         ks = ks_base + min(ks, nsw - 1);
 #pragma unroll
         for (int j = 0; j < G; ++j)
+            if (j == 0 || 16 * j < nt)  // token groups the item does not fill are not loaded
 #pragma unroll
-            for (int v = 0; v < XV; ++v) x[j][v] = *(const u32x4_t*)(xp[j] + (size_t)ks * (XV * 64) + v * 64);
+                for (int v = 0; v < XV; ++v) x[j][v] = *(const u32x4_t*)(xp[j] + (size_t)ks * (XV * 64) + v * 64);
         if constexpr (kInt4) {
 #pragma unroll
             for (int u = 0; u < RA; ++u)
@@ -153,9 +154,10 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
         __attribute__((always_inline)) {
         if constexpr (!kInt4) {
 #pragma unroll
-            for (int u = 0; u < RA; ++u)
+            for (int j = 0; j < G; ++j)
+                if (j == 0 || 16 * j < nt)
 #pragma unroll
-                for (int j = 0; j < G; ++j) acc[u][j] = mfma_bf16(w[u], x[j][0], acc[u][j]);
+                    for (int u = 0; u < RA; ++u) acc[u][j] = mfma_bf16(w[u], x[j][0], acc[u][j]);
         } else {
             f32x4_t px[G], pm[RA][G];
 #pragma unroll
@@ -173,10 +175,12 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
                     int4_word_to_bf16(wd, wb);
                     const u32x4_t bw = {wb[0], wb[1], wb[2], wb[3]};
 #pragma unroll
-                    for (int j = 0; j < G; ++j) pm[u][j] = mfma_bf16(x[j][st], bw, pm[u][j]);
+                    for (int j = 0; j < G; ++j)
+                        if (j == 0 || 16 * j < nt) pm[u][j] = mfma_bf16(x[j][st], bw, pm[u][j]);
                 }
 #pragma unroll
-                for (int j = 0; j < G; ++j) px[j] = mfma_bf16(x[j][st], ones, px[j]);
+                for (int j = 0; j < G; ++j)
+                    if (j == 0 || 16 * j < nt) px[j] = mfma_bf16(x[j][st], ones, px[j]);
             }
 #pragma unroll
             for (int u = 0; u < RA; ++u) {

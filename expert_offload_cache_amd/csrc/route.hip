@@ -22,6 +22,8 @@
 
 #include "moe_common.h"
 
+#include <algorithm>
+
 namespace moe {
 namespace {
 
@@ -287,17 +289,17 @@ __device__ void select_and_gate(const float* s_logit, int E, int k, const int32_
             s_val[j] = s_logit[min(max(id, 0), E - 1)];
         }
     } else {
-        for (int e = tid; e < E; e += nth) {
+        // P adjacent lanes share an expert, each counting the experts i = p (mod P) that beat it;
+        // the partial counts are summed over the P lanes
+        const int P = nth >= 4 * E ? 4 : nth >= 2 * E ? 2 : 1;
+        for (int b = tid; b < E * P; b += nth) {
+            const int e = b / P, p = b - e * P;
             const float v = s_logit[e];
             int r = 0;
-            int i = 0;
-            for (; i + 4 <= E; i += 4) {
-                const float4 o = *(const float4*)(s_logit + i);
-                r += better(o.x, i, v, e) + better(o.y, i + 1, v, e) + better(o.z, i + 2, v, e) +
-                     better(o.w, i + 3, v, e);
-            }
-            for (; i < E; ++i) r += better(s_logit[i], i, v, e);
-            if (r < k) {
+            for (int i = p; i < E; i += P) r += better(s_logit[i], i, v, e);
+            if (P >= 2) r += __shfl_xor(r, 1, 64);
+            if (P >= 4) r += __shfl_xor(r, 2, 64);
+            if (p == 0 && r < k) {
                 s_sel[r] = e;
                 s_val[r] = v;
             }
@@ -319,8 +321,8 @@ __device__ void select_and_gate(const float* s_logit, int E, int k, const int32_
     }
 }
 
-// prefill: one block per token, logits already in global memory
-__global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logits, int T, int E, int k,
+// one block per token, logits already in global memory
+__global__ __launch_bounds__(1024) void route_topk(const float* __restrict__ logits, int T, int E, int k,
                                                   const int32_t* __restrict__ forced,
                                                   int32_t* __restrict__ topk_idx,
                                                   float* __restrict__ topk_w) {
@@ -379,6 +381,80 @@ __global__ __launch_bounds__(256) void route_logits_wave(const void* __restrict_
     if (lane == 0) logits[(size_t)t * E + e] = bias ? acc + bias[e] : acc;
 }
 
+// decode, bf16: one wave per tile of TB tokens x EB experts.  Lane j owns segment j of every
+// row of the tile, so each activation and router row is read once per tile instead of once per
+// (token, expert) pair; every logit still sums its segment in ascending index and joins the 64
+// segment sums with the neighbours-first butterfly, the order of route_logits_wave.
+template <int TB, int EB, int CG>
+__global__ __launch_bounds__(256) void route_logits_wave_tile(const uint16_t* __restrict__ x,
+                                                              const uint16_t* __restrict__ w,
+                                                              const float* __restrict__ bias, int T, int d, int E,
+                                                              float* __restrict__ logits) {
+    const int lane = threadIdx.x & 63;
+    const int ntt = (T + TB - 1) / TB, nte = (E + EB - 1) / EB;
+    const long g = (long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (g >= (long)ntt * nte) return;
+    const int t0 = (int)(g / nte) * TB, e0 = (int)(g % nte) * EB;
+    const int S = d / 64;  // segment length, a multiple of 8 (checked by the caller)
+    const int nv = S / 8;
+    const size_t seg = (size_t)lane * S;
+    const uint4* xr[TB];
+    const uint4* wr[EB];
+#pragma unroll
+    for (int i = 0; i < TB; ++i) xr[i] = (const uint4*)(x + (size_t)min(t0 + i, T - 1) * d + seg);
+#pragma unroll
+    for (int j = 0; j < EB; ++j) wr[j] = (const uint4*)(w + (size_t)min(e0 + j, E - 1) * d + seg);
+    float acc[TB][EB];
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+#pragma unroll
+        for (int j = 0; j < EB; ++j) acc[i][j] = 0.f;
+    // chunks of 8 inputs, CG at a time: issue the group's loads, then the products in index order
+    for (int c0 = 0; c0 < nv; c0 += CG) {
+        uint4 xv[CG][TB], wv[CG][EB];
+#pragma unroll
+        for (int c = 0; c < CG; ++c) {
+            const int cc = min(c0 + c, nv - 1);
+#pragma unroll
+            for (int i = 0; i < TB; ++i) xv[c][i] = xr[i][cc];
+#pragma unroll
+            for (int j = 0; j < EB; ++j) wv[c][j] = wr[j][cc];
+        }
+#pragma unroll
+        for (int c = 0; c < CG; ++c) {
+            if (c0 + c < nv) {
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+#pragma unroll
+                    for (int i = 0; i < TB; ++i) {
+                        const uint32_t xs = h == 0 ? xv[c][i].x : h == 1 ? xv[c][i].y : h == 2 ? xv[c][i].z : xv[c][i].w;
+#pragma unroll
+                        for (int j = 0; j < EB; ++j) {
+                            const uint32_t ws = h == 0 ? wv[c][j].x : h == 1 ? wv[c][j].y : h == 2 ? wv[c][j].z : wv[c][j].w;
+                            acc[i][j] = madd<true>(acc[i][j], bf16_lo(xs), bf16_lo(ws));
+                            acc[i][j] = madd<true>(acc[i][j], bf16_hi(xs), bf16_hi(ws));
+                        }
+                    }
+                }
+            }
+        }
+    }
+    // join each logit's 64 segment sums; lane i * EB + j writes logit (t0 + i, e0 + j)
+    float out = 0.f;
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+#pragma unroll
+        for (int j = 0; j < EB; ++j) {
+            const float v = wave_tree_sum(acc[i][j]);
+            if (lane == i * EB + j) out = v;
+        }
+    const int i = lane / EB, j = lane % EB;
+    if (lane < TB * EB && t0 + i < T && e0 + j < E) {
+        const int e = e0 + j;
+        logits[(size_t)(t0 + i) * E + e] = bias ? out + bias[e] : out;
+    }
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -396,7 +472,15 @@ extern "C" moe_status moe_route(const void* x, moe_dtype act, int T, int d, cons
     MOE_CHECK(T <= (1 << 24), MOE_ESHAPE, "moe_route: T=%d too large", T);
     hipStream_t st = (hipStream_t)s;
     const bool bf = act == MOE_BF16;
-    if (T <= 64) {
+    if (T >= 32 && T <= 64 && bf && d <= 2048 && (d / 64) % 8 == 0 && E >= 4) {
+        // 4 tokens x 4 experts a wave (measured faster than one wave a pair at 64 tokens and
+        // d <= 2048, slower at 4-16 tokens or wider rows, where the pair-per-wave kernel has more
+        // waves)
+        const long tiles = (long)((T + 3) / 4) * ((E + 3) / 4);
+        ProfScope p("route_logits_wave", st);
+        route_logits_wave_tile<4, 4, 4><<<(unsigned)((tiles + 3) / 4), 256, 0, st>>>(
+            (const uint16_t*)x, (const uint16_t*)w_router, bias, T, d, E, logits);
+    } else if (T <= 64) {
         const long waves = (long)T * E;
         ProfScope p("route_logits_wave", st);
         if (bf) route_logits_wave<true><<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(x, w_router, bias, T, d, E, logits);
@@ -415,7 +499,9 @@ extern "C" moe_status moe_route(const void* x, moe_dtype act, int T, int d, cons
     if (r != MOE_OK) return r;
     {
         ProfScope p("route_topk", st);
-        route_topk<<<T, 256, 0, st>>>(logits, T, E, k, forced_idx, topk_idx, topk_w);
+        // up to 4 threads per expert share its comparisons
+        const int nth = std::min(1024, std::max(64, (E * 4 + 63) / 64 * 64));
+        route_topk<<<T, nth, 0, st>>>(logits, T, E, k, forced_idx, topk_idx, topk_w);
     }
     return check_launch("route_topk");
 }
