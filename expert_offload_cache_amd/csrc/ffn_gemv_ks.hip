@@ -14,7 +14,10 @@
 //     so the loads of a wave complete in the order they are used and each wave keeps R - 1
 //     stages in flight from start to end;
 //   * the partial sums never leave the wave: SiLU(g)*u (bf16) or the down output is formed in
-//     registers and stored directly; the kernel uses no LDS and no barrier.
+//     registers and stored directly.  LDS is used only where the inputs are split over S waves
+//     (one join at the end) and by the staged-rows variant (XL): items of at most 4 tokens copy
+//     their activation rows to LDS once, so only weight loads go through the in-order load
+//     queue.
 // The waves of a workgroup take consecutive row-block ranges of the same (expert, chunk) item.
 //
 // Operands of v_mfma_f32_16x16x32_bf16 (lane l: row or token l%16, inputs 8(l/16)..+7 of the 32):
@@ -56,10 +59,14 @@ struct KsFrag<MOE_INT4_G128> {
     static constexpr int kIn = 128, kXv = 4;
 };
 
-template <int MODE, int W, int RA, int G, int R, int S>
+constexpr int kXlTok = 4;  // most tokens an item may hold when its activation rows are staged in LDS
+
+template <int MODE, int W, int RA, int G, int R, int S, bool XL>
 __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
     static_assert(MODE == kDown || RA % 2 == 0, "gate/up rows come in gate/up pairs");
     static_assert(kKsWaves % S == 0, "input split");
+    static_assert(!XL || G == 1, "staged activation rows: one token group");
+    extern __shared__ __align__(16) uint8_t smem[];
     constexpr int XV = KsFrag<W>::kXv;
     constexpr int NTG = 16 * G;
     constexpr bool kInt4 = (W == MOE_INT4_G128);
@@ -121,6 +128,30 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
         xp[j] = in_base + (size_t)row * K * 2 + q * 16;
     }
 
+    // XL: the item's activation rows (at most kXlTok) are staged in LDS once, so only weight
+    // loads go through the in-order load queue and the stages read their activations from LDS
+    if constexpr (XL) {
+        const int vpr = K * 2 / 16;  // 16-byte vectors a row
+        const int total = nt * vpr;
+        for (int v0 = 0; v0 < total; v0 += 8 * 64 * kKsWaves) {
+            u32x4_t t[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int v = min(v0 + u * 64 * kKsWaves + (int)threadIdx.x, total - 1);
+                const int i = v / vpr;
+                const int row = (MODE == kGateUp) ? (shared ? (i0 + i) : (a.perm[p0 + i0 + i] / a.k)) : (p0 + i0 + i);
+                t[u] = *(const u32x4_t*)(in_base + (size_t)row * K * 2 + (size_t)(v - i * vpr) * 16);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int v = v0 + u * 64 * kKsWaves + (int)threadIdx.x;
+                if (v < total) ((u32x4_t*)smem)[v] = t[u];
+            }
+        }
+        __syncthreads();
+    }
+    const uint8_t* s_xrow = smem + (size_t)min(r16, nt - 1) * K * 2 + q * 16;  // XL: this lane's row
+
     u32x4_t wst[R][RA], xst[R][G][XV];
     uint32_t sst[R][kInt4 ? RA : 1];
     // local stage ks into register set (w, x, s); past the end of the share its last stage is
@@ -130,7 +161,7 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
         ks = ks_base + min(ks, nsw - 1);
 #pragma unroll
         for (int j = 0; j < G; ++j)
-            if (j == 0 || 16 * j < nt)  // token groups the item does not fill are not loaded
+            if (!XL && (j == 0 || 16 * j < nt))  // token groups the item does not fill are not loaded
 #pragma unroll
                 for (int v = 0; v < XV; ++v) x[j][v] = *(const u32x4_t*)(xp[j] + (size_t)ks * (XV * 64) + v * 64);
         if constexpr (kInt4) {
@@ -150,8 +181,12 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
         for (int j = 0; j < G; ++j) acc[u][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const u32x4_t ones = {kOnes, kOnes, kOnes, kOnes};
 
-    auto compute = [&](const u32x4_t (&w)[RA], const u32x4_t (&x)[G][XV], const uint32_t (&s)[kInt4 ? RA : 1])
+    auto compute = [&](int ks, const u32x4_t (&w)[RA], u32x4_t (&x)[G][XV], const uint32_t (&s)[kInt4 ? RA : 1])
         __attribute__((always_inline)) {
+        if constexpr (XL) {
+#pragma unroll
+            for (int v = 0; v < XV; ++v) x[0][v] = *(const u32x4_t*)(s_xrow + (size_t)(ks_base + ks) * (XV * 64) + v * 64);
+        }
         if constexpr (!kInt4) {
 #pragma unroll
             for (int j = 0; j < G; ++j)
@@ -200,13 +235,13 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             issue(ks0 + r + R - 1, wst[(r + R - 1) % R], xst[(r + R - 1) % R], sst[(r + R - 1) % R]);
-            if (ks0 + r < nsw) compute(wst[r], xst[r], sst[r]);
+            if (ks0 + r < nsw) compute(ks0 + r, wst[r], xst[r], sst[r]);
         }
     }
     if constexpr (S > 1) {
         // join the S shares in LDS in share order; the first wave of each group stores
-        extern __shared__ __align__(16) uint8_t smem[];
-        f32x4_t* red = (f32x4_t*)smem + (size_t)wv * RA * G * 64;
+        uint8_t* jb = smem + (XL ? (size_t)min(a.T, kXlTok) * K * 2 : 0);
+        f32x4_t* red = (f32x4_t*)jb + (size_t)wv * RA * G * 64;
 #pragma unroll
         for (int u = 0; u < RA; ++u)
 #pragma unroll
@@ -215,7 +250,7 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
         if (si != 0) return;
 #pragma unroll
         for (int w2 = 1; w2 < S; ++w2) {
-            const f32x4_t* o = (const f32x4_t*)smem + (size_t)(wv + w2) * RA * G * 64;
+            const f32x4_t* o = (const f32x4_t*)jb + (size_t)(wv + w2) * RA * G * 64;
 #pragma unroll
             for (int u = 0; u < RA; ++u)
 #pragma unroll
@@ -274,21 +309,23 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
 
 // One launch shape: RA row blocks a wave, G token groups an item, R stages in flight, inputs split
 // over S waves.  An unsupported shape returns MOE_EDTYPE with nothing launched.
-template <int MODE, int W, int RA, int G, int R, int S>
+template <int MODE, int W, int RA, int G, int R, int S, bool XL = false>
 static moe_status launch_ks(const FfnArgs& a, hipStream_t st, const char* name) {
     const int M = (MODE == kGateUp) ? a.f : a.d;            // output rows
     const int K = (MODE == kGateUp) ? a.d : a.f;
     const int per_wave = (MODE == kGateUp) ? RA / 2 : RA;    // output row blocks a wave
     const int groups = kKsWaves / S;                         // row-block groups a workgroup
     if ((M / 16) % (per_wave * groups) != 0 || (K / KsFrag<W>::kIn) % S != 0) return MOE_EDTYPE;
+    if (XL && (a.T > kXlTok || (size_t)kXlTok * K * 2 > 65536)) return MOE_EDTYPE;
     const int ntg = 16 * G;
     const int64_t tk = (int64_t)a.T * a.k;
     const int64_t items = (tk + ntg - 1) / ntg + std::min<int64_t>(a.E, tk) + (a.shared_w ? (a.T + ntg - 1) / ntg : 0);
     if (items > 65535) return set_error(MOE_ESHAPE, "%s: %lld work items exceed one launch", name, (long long)items);
     dim3 grid((unsigned)(M / 16 / (per_wave * groups)), (unsigned)items), block(64 * kKsWaves);
-    const size_t lds = S > 1 ? (size_t)kKsWaves * RA * G * 1024 : 0;
+    // staged rows: as many as an item can hold (min(T, kXlTok)); then the S-way join buffer
+    const size_t lds = (XL ? (size_t)std::min(a.T, kXlTok) * K * 2 : 0) + (S > 1 ? (size_t)kKsWaves * RA * G * 1024 : 0);
     ProfScope ps(name, st);
-    ffn_gemv_ks_kernel<MODE, W, RA, G, R, S><<<grid, block, lds, st>>>(a);
+    ffn_gemv_ks_kernel<MODE, W, RA, G, R, S, XL><<<grid, block, lds, st>>>(a);
     return check_launch(name);
 }
 
@@ -300,14 +337,19 @@ static moe_status launch_ks(const FfnArgs& a, hipStream_t st, const char* name) 
 //     reads each expert once and is faster;
 //   bf16 down: one row block a wave with 5 stages in flight for up to 4 tokens, else two row
 //     blocks a wave over 32-token items;
-//   int4: two waves split the inputs from 2 tokens on; a single token stays on the vector-ALU
-//     kernel (equal time).
+//   int4 gate/up: two waves split the inputs from 2 tokens on; a single token stays on the
+//     vector-ALU kernel (equal time);
+//   int4 down: up to 4 tokens, one row block a wave with 7 stages in flight and the item's h rows
+//     staged in LDS; above that two waves split the inputs.
 static int ks_plan(int mode, moe_dtype w, int T) {
     if (w == MOE_BF16) {
         if (mode == kGateUp) return T <= 16 ? 0 : -1;
         return T <= 4 ? 0 : 1;
     }
-    if (w == MOE_INT4_G128) return T >= 2 ? 0 : -1;
+    if (w == MOE_INT4_G128) {
+        if (mode == kGateUp) return T >= 2 ? 0 : -1;
+        return T <= kXlTok ? 1 : 0;
+    }
     return -1;
 }
 
@@ -320,6 +362,10 @@ moe_status ffn_gemv_ks(const FfnArgs& a, int mode, moe_dtype w, hipStream_t st) 
         return launch_ks<kDown, MOE_BF16, 2, 2, 4, 1>(a, st, "ffn_gemv_down_bf16");
     }
     if (mode == kGateUp) return launch_ks<kGateUp, MOE_INT4_G128, 2, 1, 4, 2>(a, st, "ffn_gemv_gateup_int4");
+    if (plan == 1) {
+        const moe_status r = launch_ks<kDown, MOE_INT4_G128, 1, 1, 8, 1, true>(a, st, "ffn_gemv_down_int4");
+        if (r != MOE_EDTYPE) return r;  // rows too long to stage: the plan below
+    }
     return launch_ks<kDown, MOE_INT4_G128, 2, 1, 3, 2>(a, st, "ffn_gemv_down_int4");
 }
 
