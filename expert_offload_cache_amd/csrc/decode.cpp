@@ -3,11 +3,11 @@
 // picks the experts, the GPU-resident ones are used from their slots and a miss is copied from
 // the pinned host pool first; FreeToken GGUF page, offload backend).
 //
-// Per layer, on the compute stream: route -> permute -> ids copied to pinned host memory and the
-// stream waited for (the cache decides on the host, with no lookahead) -> distinct ids, lookup,
-// fill (copies on the copy stream, compute waits) -> grouped experts through the layer's
-// slot-table row -> combine -> mark_read.  The same calls, in the same order, as a caller would
-// make one by one; only the host-side marshalling between them is gone.
+// Per layer, on the compute stream: route -> ids copied to pinned host memory -> permute; the host
+// waits for the copy only (the cache decides on the host, with no lookahead), so the permutation
+// runs while it decides -> distinct ids, lookup, fill (copies on the copy stream, compute waits)
+// -> grouped experts through the layer's slot-table row -> combine -> mark_read.  The same calls
+// as a caller would make one by one; only the host-side marshalling between them is gone.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -16,6 +16,18 @@
 #include "moe_common.h"
 
 using namespace moe;
+
+namespace {
+// Event marking the ids' arrival in host memory (created per call, released on every return).
+struct IdsEvent {
+    hipEvent_t e = nullptr;
+    hipError_t status;
+    IdsEvent() : status(hipEventCreateWithFlags(&e, hipEventDisableTiming)) {}
+    ~IdsEvent() {
+        if (e) (void)hipEventDestroy(e);
+    }
+};
+}  // namespace
 
 extern "C" moe_status moe_decode_step(moe_cache* cache, int n_layers, const moe_decode_layer* layers, int T, int d,
                                       int f, int E, int k, moe_dtype act, moe_dtype w, const void* slot_pool,
@@ -27,18 +39,24 @@ extern "C" moe_status moe_decode_step(moe_cache* cache, int n_layers, const moe_
     MOE_CHECK(n_layers >= 0 && T >= 1 && k >= 1 && k <= E, MOE_ESHAPE,
               "moe_decode_step: need n_layers >= 0, T >= 1, 1 <= k <= E (n_layers=%d T=%d k=%d E=%d)", n_layers, T,
               k, E);
+    for (int i = 0; i < n_layers; ++i)  // every layer is checked before anything is enqueued
+        MOE_CHECK(layers[i].x && layers[i].w_router && layers[i].y, MOE_EINVAL,
+                  "moe_decode_step: layer %d: NULL pointer", i);
+    if (n_layers == 0) return MOE_OK;
     hipStream_t cs = (hipStream_t)compute;
     std::vector<int32_t> ids((size_t)T * k), slots((size_t)T * k);
+    IdsEvent ev;
+    MOE_HIP(ev.status);
     for (int i = 0; i < n_layers; ++i) {
         const moe_decode_layer& ly = layers[i];
-        MOE_CHECK(ly.x && ly.w_router && ly.y, MOE_EINVAL, "moe_decode_step: layer %d: NULL pointer", i);
         moe_status r = moe_route(ly.x, act, T, d, ly.w_router, ly.bias, E, k, ly.forced_idx, topk_idx, topk_w,
                                  logits, compute);
         if (r != MOE_OK) return r;
+        MOE_HIP(hipMemcpyAsync(host_idx, topk_idx, sizeof(int32_t) * (size_t)T * k, hipMemcpyDeviceToHost, cs));
+        MOE_HIP(hipEventRecord(ev.e, cs));
         r = moe_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, nullptr, 0, compute);
         if (r != MOE_OK) return r;
-        MOE_HIP(hipMemcpyAsync(host_idx, topk_idx, sizeof(int32_t) * (size_t)T * k, hipMemcpyDeviceToHost, cs));
-        MOE_HIP(hipStreamSynchronize(cs));
+        MOE_HIP(hipEventSynchronize(ev.e));
         std::copy(host_idx, host_idx + (size_t)T * k, ids.begin());
         std::sort(ids.begin(), ids.end());
         const int n = (int)(std::unique(ids.begin(), ids.end()) - ids.begin());
@@ -93,19 +111,26 @@ extern "C" moe_status moe_decode_step_hybrid(
               "moe_decode_step_hybrid: need n_layers >= 0, 1 <= k <= E and bf16 activations");
     hipStream_t cs = (hipStream_t)compute;
     const int T = 1;  // one token: a pair's row of y_perm is the rank of its expert id
+    for (int i = 0; i < n_layers; ++i)  // every layer is checked before anything is enqueued
+        MOE_CHECK(layers[i].x && layers[i].w_router && layers[i].y, MOE_EINVAL,
+                  "moe_decode_step_hybrid: layer %d: NULL pointer", i);
+    if (n_layers == 0) return MOE_OK;
     std::vector<int32_t> ids(k), slots(k), miss, on_cpu, gpu_ids;
     int64_t n_cpu_total = 0;
+    IdsEvent ev;
+    MOE_HIP(ev.status);
     for (int i = 0; i < n_layers; ++i) {
         const moe_decode_layer& ly = layers[i];
-        MOE_CHECK(ly.x && ly.w_router && ly.y, MOE_EINVAL, "moe_decode_step_hybrid: layer %d: NULL pointer", i);
         moe_status r = moe_route(ly.x, act, T, d, ly.w_router, ly.bias, E, k, ly.forced_idx, topk_idx, topk_w,
                                  logits, compute);
         if (r != MOE_OK) return r;
-        r = moe_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, nullptr, 0, compute);
-        if (r != MOE_OK) return r;
         MOE_HIP(hipMemcpyAsync(host_idx, topk_idx, sizeof(int32_t) * k, hipMemcpyDeviceToHost, cs));
         MOE_HIP(hipMemcpyAsync(host_x, ly.x, sizeof(uint16_t) * d, hipMemcpyDeviceToHost, cs));
-        MOE_HIP(hipStreamSynchronize(cs));  // also retires the previous layer's table and row copies
+        MOE_HIP(hipEventRecord(ev.e, cs));
+        r = moe_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, nullptr, 0, compute);
+        if (r != MOE_OK) return r;
+        // the event also retires the previous layer's table and row copies (earlier on the stream)
+        MOE_HIP(hipEventSynchronize(ev.e));
         std::copy(host_idx, host_idx + k, ids.begin());
         std::sort(ids.begin(), ids.end());
         const int n = (int)(std::unique(ids.begin(), ids.end()) - ids.begin());

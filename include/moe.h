@@ -242,13 +242,15 @@ MOE_API void moe_cache_destroy(moe_cache* c);
 /* ------------------------------------------------------------------------------------------
  * moe_decode_step -- one decode step of an offloaded stack, every layer in one call (FreeToken
  * linux guide, "MoE memory handling"; FreeToken GGUF page, offload backend).  For each layer,
- * in order, on `compute`: moe_route (forced_idx may be NULL) and moe_permute into the given
- * buffers; topk_idx copied to host_idx (pinned, T*k int32) and `compute` synchronised; the
- * distinct ids, ascending, to moe_cache_lookup(layer); moe_cache_fill(copy, compute);
- * moe_expert_ffn_grouped through slot_table row `layer` (the cache's slot table, device [L*E]);
- * moe_combine into y (act dtype); moe_cache_mark_read(layer).  Outputs, cache decisions and
- * statistics are those of the same calls made one by one.  Buffers as in those calls; y_perm
- * [T*k (+T), d] f32; ws: moe_workspace_bytes(T, ...) bytes.  Returns the first error. */
+ * in order, on `compute`: moe_route (forced_idx may be NULL); topk_idx copied to host_idx
+ * (pinned, T*k int32); moe_permute into the given buffers; the host waits for the copy only (the
+ * permutation runs meanwhile); the distinct ids, ascending, to moe_cache_lookup(layer);
+ * moe_cache_fill(copy, compute); moe_expert_ffn_grouped through slot_table row `layer` (the
+ * cache's slot table, device [L*E]); moe_combine into y (act dtype); moe_cache_mark_read(layer).
+ * Outputs, cache decisions and statistics are those of the same calls made one by one.  Buffers
+ * as in those calls; y_perm [T*k (+T), d] f32; ws: moe_workspace_bytes(T, ...) bytes.  Every
+ * layer's x, w_router and y are checked (MOE_EINVAL) before anything is enqueued; later errors
+ * return at once, the layers before them enqueued.  Returns the first error. */
 typedef struct {
     const void* x;             /* [T, d] act: this layer's input (device) */
     const void* w_router;      /* [E, d] act */
