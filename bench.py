@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--offload-layers", type=int, default=12,
                     help="stacked layers in the pinned pool (24 need ~80 GB of pinned host memory)")
     ap.add_argument("--offload-steps", type=int, default=2048)
+    ap.add_argument("--cpu-extended", action="store_true",
+                    help="also time the oracle on every workload at all and at one BLAS thread, and the LRU "
+                         "simulator on one core (adds about two minutes of host work)")
     return ap.parse_args()
 
 
@@ -91,6 +94,53 @@ def cpu_baseline(wl, li, T, budget_s):
             break
     return {"value": calls * T / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{calls} layer calls of {T} tokens of the headline layer (float64 numpy/BLAS oracle, {el:.1f} s)"}
+
+
+def cpu_extended(budget_s: float = 3.0):
+    """The oracle as it stands on each workload's layer, with the BLAS pool at all host threads and
+    at one thread (bounded samples of layer calls), plus the LRU simulator's decode steps/s on one
+    core over the 24-layer routing trace at 40 % and 58 % capacity."""
+    import synth
+    from oracle.layer import moe_layer
+    from oracle.lru import LRUSim
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    nthreads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    cases = [("tiny_fp32", (16,)), ("qwen_a3b_decode_bf16", (1, 4, 16, 64)), ("dsv4_decode_int4", (1, 2, 8)),
+             ("dsv4_prefill_bf16", (512,))]
+    out = {"blas_threads": nthreads, "layers": {}}
+    for name, Ts in cases:
+        wl = synth.WORKLOADS[name]
+        li = synth.layer_inputs(wl, max(Ts), seed=0)
+        for T in Ts:
+            x = synth.layer_inputs(wl, T, seed=0, with_experts=False).x
+            row = {}
+            for label, limit in (("all_threads", None), ("one_thread", 1)):
+                if T >= 512 and limit == 1:
+                    continue  # one call takes minutes on one thread
+                with threadpool_limits(limits=limit):
+                    calls, t0 = 0, time.perf_counter()
+                    while True:
+                        moe_layer(x, li.w_router, li.bias, wl.act, wl.k, wl.E, li.experts, li.shared)
+                        calls += 1
+                        el = time.perf_counter() - t0
+                        if el >= budget_s:
+                            break
+                row[label] = {"tokens_per_s": calls * T / el, "calls": calls, "seconds": el}
+            out["layers"][f"{name} T={T}"] = row
+            log(f"oracle {name} T={T}: {row}")
+    wl = synth.WORKLOADS["dsv4_offload_int4"]
+    L, E, steps = 24, wl.E, 2048
+    trace = synth.routing_trace(0, steps, L, E, wl.k)
+    for frac in (0.40, 0.58):
+        sim = LRUSim(int(round(frac * L * E)))
+        t0 = time.perf_counter()
+        for st in range(steps):
+            for l in range(L):
+                sim.request(l, trace[st, l])
+        el = time.perf_counter() - t0
+        out[f"lru_sim_{frac:.2f}"] = {"decode_steps_per_s": steps / el, "layers": L, "cores": 1}
+    return out
 
 
 def replicate(base, R):
@@ -386,6 +436,8 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores")
         cpu = cpu_baseline(wl, li, Tmain, args.cpu_seconds)
+    if args.cpu_extended:
+        extra["cpu_extended"] = cpu_extended()
     line = {
         "metric": "MoE-layer tokens/s (decode, grouped GEMV HBM roofline)",
         "value": Tmain * m["steps"] / m["el"], "unit": "tokens/s", "n_gpus": 1, "steps": m["steps"],
