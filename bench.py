@@ -273,6 +273,77 @@ def prefill_figures(moe, wl, layer, Ts, stream, w_bytes=2.0):
     return out
 
 
+def prefill_split(moe, wl, layer, T, stream, heavy_min=256, reps=10):
+    """The prefill FFN split into a heavy launch (experts with at least `heavy_min` tokens, plus the
+    shared expert), graded against the matrix peak, and a tail launch (the other experts), graded
+    against HBM: the same grouped call run on disjoint expert sets (the other set's counts zeroed;
+    experts with no tokens are skipped).  Timed one after the other with per-kernel HIP events, then
+    both launches at once on two streams (wall time by events)."""
+    import torch
+    import synth
+
+    x = layer.x_to_device(synth.layer_inputs(wl, T, seed=0, with_experts=False).x)
+    with torch.cuda.stream(stream):
+        ref = layer.forward(x, stream=stream)
+    stream.synchronize()
+    counts = ref["counts"]
+    c = counts.cpu().numpy()
+    heavy = c >= heavy_min
+    sets = {"heavy": (counts * torch.from_numpy(heavy.astype(np.int32)).to(counts.device), layer.shared),
+            "tail": (counts * torch.from_numpy((~heavy).astype(np.int32)).to(counts.device), None)}
+    ws = {key: layer.workspace(T) for key in sets}
+    yp = {key: torch.empty_like(ref["y_perm"]) for key in sets}
+
+    def run(key, st):
+        cnt, shw = sets[key]
+        moe.expert_ffn_grouped(x, ref["perm"], ref["offsets"], cnt, layer.slot_of_expert, layer.pool, layer.n_slots,
+                               layer.stride, layer.wdt, wl.f, wl.k, shared_w=shw, y_perm=yp[key], ws=ws[key],
+                               stream=st)
+
+    out = {"heavy_min_tokens": heavy_min, "routed_heavy_experts": int(heavy.sum()),
+           "routed_tail_experts": int(((c > 0) & ~heavy).sum())}
+    wb = 2.0 if layer.wdt == "bf16" else 0.5 + 2.0 / 128
+    for key in sets:
+        for _ in range(2):
+            run(key, stream)
+        stream.synchronize()
+        moe.profile_reset()
+        moe.profile_enable(True)
+        for _ in range(reps):
+            run(key, stream)
+        stream.synchronize()
+        moe.profile_collect()
+        moe.profile_enable(False)
+        kern = {name: ms / n * 1e3 for name, (ms, n) in moe.profile_results().items()}
+        us = sum(kern.values())
+        if key == "heavy":
+            rows = int(c[heavy].sum()) + T
+            n_exp = int(heavy.sum()) + 1
+        else:
+            rows = int(c[~heavy].sum())
+            n_exp = out["routed_tail_experts"]
+        flops = 2.0 * rows * 3 * wl.f * wl.d
+        wbytes = n_exp * 3 * wl.d * wl.f * wb
+        out[key] = {"tokens_x_experts": rows, "experts": n_exp, "ffn_us": us, "TFLOPs": flops / us / 1e6,
+                    "mfma_frac": flops / us / 1e6 / MFMA_BF16_PEAK_TFS, "weight_GBps": wbytes / us / 1e3,
+                    "hbm_frac": wbytes / us / 1e3 / HBM_PEAK_GBS, "kernels_us": kern}
+    # both at once on two streams
+    other = torch.cuda.Stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    other.wait_event(e0)
+    for _ in range(reps):
+        run("heavy", stream)
+        run("tail", other)
+    stream.wait_stream(other)
+    e1.record(stream)
+    e1.synchronize()
+    out["concurrent_us"] = e0.elapsed_time(e1) * 1e3 / reps
+    out["sequential_us"] = out["heavy"]["ffn_us"] + out["tail"]["ffn_us"]
+    return out
+
+
 def bench_prefill(moe, stream):
     import torch
     import synth
@@ -283,6 +354,7 @@ def bench_prefill(moe, stream):
     li = synth.layer_inputs(wl, 1, seed=0)
     layer = DeviceLayer.from_inputs(li)
     out = prefill_figures(moe, wl, layer, wl.T_list, stream)
+    out["heavy_tail_split"] = {str(T): prefill_split(moe, wl, layer, T, stream) for T in wl.T_list}
     del layer
     torch.cuda.empty_cache()
     return out
