@@ -38,6 +38,9 @@ SMALL = [
     ("bf16", "bf16", 128, 64, 4, 4, 1, True),
     # decode path on the matrix cores: several 16-token groups per workgroup (shared expert: 3)
     ("bf16", "bf16", 384, 64, 4, 2, 40, True),
+    # router logits in 4 x 4 token-expert tiles (32-64 tokens): a partial last token tile (33)
+    # and a partial last expert tile (6 experts)
+    ("bf16", "bf16", 512, 128, 6, 2, 33, True),
     # gate/up K = 4096 inputs: the K-streaming kernel (beyond the split-input kernel's shapes)
     ("bf16", "bf16", 4096, 64, 4, 2, 3, False),
     # gate/up K = 4096 inputs with more than 16 tokens: the VALU kernel runs it
