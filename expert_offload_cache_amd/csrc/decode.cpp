@@ -1,4 +1,4 @@
-// Native decode driver of the offloaded stack: one call runs every MoE layer of one decode step
+// Native decode loop of the offloaded stack: one call runs every MoE layer of one decode step
 // through the slot cache (FreeToken linux guide, "MoE memory handling": per layer the router
 // picks the experts, the GPU-resident ones are used from their slots and a miss is copied from
 // the pinned host pool first; FreeToken GGUF page, offload backend).
