@@ -177,6 +177,19 @@ def decode_step(cache, layers: np.ndarray, T: int, d: int, f: int, E: int, k: in
 
 
 
+def decode_step_split(cache, layers: np.ndarray, T: int, d: int, f: int, E: int, k: int, act: int, wdt: str,
+                      slot_pool, n_slots: int, slot_stride: int, slot_table, route_bufs, perm_bufs, y_perm, ws,
+                      host_idx, host_tables, dev_tables, compute, copy):
+    """One decode step of every layer in `layers` with split launches (moe_decode_step_split).
+    host_tables: pinned int32 [2, E]; dev_tables: device int32 [2, E]."""
+    idx, w, logits = route_bufs
+    c, o, p, ip = perm_bufs
+    check(lib().moe_decode_step_split(cache.h, len(layers), layers.ctypes.data, T, d, f, E, k, act, WDT[wdt],
+                                      _p(slot_pool), n_slots, slot_stride, _p(slot_table), _p(idx), _p(w),
+                                      _p(logits), _p(c), _p(o), _p(p), _p(ip), _p(y_perm), _p(ws), ws.numel(),
+                                      host_idx.data_ptr(), host_tables.data_ptr(), _p(dev_tables), _s(compute),
+                                      _s(copy)))
+
 def decode_step_hybrid(cache, layers: np.ndarray, d: int, f: int, E: int, k: int, act: int, wdt: str, slot_pool,
                        n_slots: int, slot_stride: int, slot_table, route_bufs, perm_bufs, y_perm, ws, host_idx,
                        host_x, host_y, host_table, dev_table, cpu_rate: float, pcie_rate: float, copy_too: bool,

@@ -28,6 +28,8 @@ SIGNATURES = {
     "moe_combine": (_st, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
     "moe_decode_step": (_st, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _sz, _vp, _vp, _vp,
                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
+    "moe_decode_step_split": (_st, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _sz, _vp,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp]),
     "moe_decode_step_hybrid": (_st, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _sz, _vp, _vp,
                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp,
                                      ctypes.c_double, ctypes.c_double, _i32, _i32, _vp, _vp, _vp]),

@@ -178,3 +178,84 @@ extern "C" moe_status moe_decode_step_hybrid(
     if (n_cpu_out) *n_cpu_out += n_cpu_total;
     return MOE_OK;
 }
+
+extern "C" moe_status moe_decode_step_split(moe_cache* cache, int n_layers, const moe_decode_layer* layers, int T,
+                                            int d, int f, int E, int k, moe_dtype act, moe_dtype w,
+                                            const void* slot_pool, int n_slots, size_t slot_stride,
+                                            const int32_t* slot_table, int32_t* topk_idx, float* topk_w,
+                                            float* logits, int32_t* counts, int32_t* offsets, int32_t* perm,
+                                            int32_t* inv_perm, float* y_perm, void* ws, size_t ws_bytes,
+                                            int32_t* host_idx, int32_t* host_tables, int32_t* dev_tables,
+                                            moe_stream compute, moe_stream copy) {
+    MOE_CHECK(cache && layers && slot_table && host_idx && host_tables && dev_tables, MOE_EINVAL,
+              "moe_decode_step_split: NULL pointer");
+    MOE_CHECK(n_layers >= 0 && T >= 1 && k >= 1 && k <= E, MOE_ESHAPE,
+              "moe_decode_step_split: need n_layers >= 0, T >= 1, 1 <= k <= E (n_layers=%d T=%d k=%d E=%d)",
+              n_layers, T, k, E);
+    for (int i = 0; i < n_layers; ++i)  // every layer is checked before anything is enqueued
+        MOE_CHECK(layers[i].x && layers[i].w_router && layers[i].y, MOE_EINVAL,
+                  "moe_decode_step_split: layer %d: NULL pointer", i);
+    if (n_layers == 0) return MOE_OK;
+    hipStream_t cs = (hipStream_t)compute;
+    std::vector<int32_t> ids((size_t)T * k), slots((size_t)T * k);
+    std::vector<char> missed((size_t)T * k);
+    IdsEvent ev;
+    MOE_HIP(ev.status);
+    for (int i = 0; i < n_layers; ++i) {
+        const moe_decode_layer& ly = layers[i];
+        moe_status r = moe_route(ly.x, act, T, d, ly.w_router, ly.bias, E, k, ly.forced_idx, topk_idx, topk_w,
+                                 logits, compute);
+        if (r != MOE_OK) return r;
+        MOE_HIP(hipMemcpyAsync(host_idx, topk_idx, sizeof(int32_t) * (size_t)T * k, hipMemcpyDeviceToHost, cs));
+        MOE_HIP(hipEventRecord(ev.e, cs));
+        r = moe_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, nullptr, 0, compute);
+        if (r != MOE_OK) return r;
+        // also retires the previous layer's table copy (earlier on the stream)
+        MOE_HIP(hipEventSynchronize(ev.e));
+        std::copy(host_idx, host_idx + (size_t)T * k, ids.begin());
+        std::sort(ids.begin(), ids.end());
+        const int n = (int)(std::unique(ids.begin(), ids.end()) - ids.begin());
+        int n_missed = 0;
+        for (int j = 0; j < n; ++j) {
+            int32_t sl = -1;
+            r = moe_cache_slot_of(cache, ly.layer, ids[j], &sl);
+            if (r != MOE_OK) return r;
+            missed[j] = sl < 0;
+            n_missed += missed[j];
+        }
+        int32_t n_miss = 0;
+        r = moe_cache_lookup(cache, ly.layer, ids.data(), n, slots.data(), &n_miss);
+        if (r != MOE_OK) return r;
+        if (n_missed == 0) {
+            r = moe_cache_fill(cache, copy, compute);
+            if (r == MOE_OK)
+                r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts,
+                                           slot_table + (size_t)ly.layer * E, n_slots, slot_pool, slot_stride, w,
+                                           ly.shared_w, y_perm, ws, ws_bytes, compute);
+        } else {
+            // row 0: the resident experts (missed ones produced elsewhere), row 1: the missed ones
+            int32_t* hit_row = host_tables;
+            int32_t* miss_row = host_tables + E;
+            std::fill(host_tables, host_tables + 2 * (size_t)E, -1);
+            for (int j = 0; j < n; ++j) {
+                hit_row[ids[j]] = missed[j] ? MOE_SLOT_ELSEWHERE : slots[j];
+                miss_row[ids[j]] = missed[j] ? slots[j] : MOE_SLOT_ELSEWHERE;
+            }
+            MOE_HIP(hipMemcpyAsync(dev_tables, host_tables, sizeof(int32_t) * 2 * (size_t)E, hipMemcpyHostToDevice,
+                                   cs));
+            // the resident experts run while the misses are copied in
+            r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, dev_tables, n_slots,
+                                       slot_pool, slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, compute);
+            if (r == MOE_OK) r = moe_cache_fill(cache, copy, compute);
+            if (r == MOE_OK)
+                r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, dev_tables + E, n_slots,
+                                           slot_pool, slot_stride, w, nullptr, y_perm, ws, ws_bytes, compute);
+        }
+        if (r != MOE_OK) return r;
+        r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
+        if (r != MOE_OK) return r;
+        r = moe_cache_mark_read(cache, ly.layer, compute);
+        if (r != MOE_OK) return r;
+    }
+    return MOE_OK;
+}

@@ -246,8 +246,8 @@ class OffloadStack:
         `first_step` numbers the trace's first row (it selects the activations), so a trace can be
         replayed in pieces, e.g. around a resize.
 
-        `native` (plain and hybrid modes): each step is one moe_decode_step (or
-        moe_decode_step_hybrid) call, which makes the same library calls per layer without the
+        `native`: each step is one moe_decode_step (moe_decode_step_hybrid,
+        moe_decode_step_split) call, which makes the same library calls per layer without the
         Python marshalling between them; native=False runs the same calls from this loop.
 
         `split_launch`: a layer with misses runs its hit experts before waiting for the copies (the
@@ -271,8 +271,8 @@ class OffloadStack:
         done = torch.cuda.Event()
         outs = []
         nb = self.x_dec[0].shape[0]
-        if native and not split_launch:
-            return self._decode_native(forced, steps, first_step, keep_outputs, hybrid)
+        if native and not (hybrid and split_launch):
+            return self._decode_native(forced, steps, first_step, keep_outputs, hybrid, split_launch)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         if hybrid or split_launch:
@@ -361,10 +361,11 @@ class OffloadStack:
         el = time.perf_counter() - t0
         return (el, outs) if keep_outputs else el
 
-    def _decode_native(self, forced, steps: int, first_step: int, keep_outputs: bool, hybrid=None):
-        """decode() in the plain or hybrid mode, one moe_decode_step(_hybrid) call per step."""
+    def _decode_native(self, forced, steps: int, first_step: int, keep_outputs: bool, hybrid=None,
+                       split_launch: bool = False):
+        """decode() in the plain, hybrid or split-launch mode, one native call per step."""
         import torch
-        from . import DECODE_LAYER, decode_step, decode_step_hybrid
+        from . import DECODE_LAYER, decode_step, decode_step_hybrid, decode_step_split
 
         L, E, k, d = self.L, self.E, self.k, self.d
         nb = self.x_dec[0].shape[0]
@@ -390,6 +391,9 @@ class OffloadStack:
             host_tab = torch.full((E,), -1, dtype=torch.int32, pin_memory=True)
             dev_tab = torch.empty(E, dtype=torch.int32, device=self.device)
             copy_too = hybrid[2] if len(hybrid) > 2 else True
+        if split_launch:
+            host_tabs = torch.full((2, E), -1, dtype=torch.int32, pin_memory=True)
+            dev_tabs = torch.empty((2, E), dtype=torch.int32, device=self.device)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         with torch.cuda.stream(self.compute):
@@ -399,6 +403,10 @@ class OffloadStack:
                         self.cache, arr[s], d, self.f, E, k, self.act_code, self.wl.wdt, self.slot_pool, self.n_slots,
                         self.stride, self.slot_table, b["route"], b["perm"], b["y_perm"], ws, self._host_idx, host_x,
                         host_y, host_tab, dev_tab, hybrid[0], hybrid[1], copy_too, self.compute, self.copy)
+                elif split_launch:
+                    decode_step_split(self.cache, arr[s], 1, d, self.f, E, k, self.act_code, self.wl.wdt,
+                                      self.slot_pool, self.n_slots, self.stride, self.slot_table, b["route"], b["perm"],
+                                      b["y_perm"], ws, self._host_idx, host_tabs, dev_tabs, self.compute, self.copy)
                 else:
                     decode_step(self.cache, arr[s], 1, d, self.f, E, k, self.act_code, self.wl.wdt, self.slot_pool,
                                 self.n_slots, self.stride, self.slot_table, b["route"], b["perm"], b["y_perm"], ws,

@@ -268,6 +268,23 @@ MOE_API moe_status moe_decode_step(moe_cache* cache, int n_layers, const moe_dec
                                    int32_t* inv_perm, float* y_perm, void* ws, size_t ws_bytes, int32_t* host_idx,
                                    moe_stream compute, moe_stream copy);
 
+/* moe_decode_step with split launches (the hit/miss overlap of the pages' decode: FreeToken linux
+ * guide, mechanism table, resident experts used while misses stream in).  A layer without misses
+ * runs as in moe_decode_step.  A layer with misses stages two table rows in host_tables (pinned,
+ * 2*E int32) and copies them to dev_tables (device, 2*E int32): row 0 holds the resident experts'
+ * slots with the missed ones MOE_SLOT_ELSEWHERE, row 1 the missed experts' new slots with the
+ * resident ones MOE_SLOT_ELSEWHERE; the resident experts (and the shared expert) are enqueued with
+ * row 0 before moe_cache_fill, so they run while the copies do, then the missed experts with row 1,
+ * then moe_combine and mark_read.  Outputs and cache decisions are bitwise those of
+ * moe_decode_step.  Other arguments as moe_decode_step. */
+MOE_API moe_status moe_decode_step_split(moe_cache* cache, int n_layers, const moe_decode_layer* layers, int T, int d,
+                                         int f, int E, int k, moe_dtype act, moe_dtype w, const void* slot_pool,
+                                         int n_slots, size_t slot_stride, const int32_t* slot_table,
+                                         int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts,
+                                         int32_t* offsets, int32_t* perm, int32_t* inv_perm, float* y_perm, void* ws,
+                                         size_t ws_bytes, int32_t* host_idx, int32_t* host_tables,
+                                         int32_t* dev_tables, moe_stream compute, moe_stream copy);
+
 /* moe_decode_step with hybrid miss handling (FreeToken RTX 5090 page, miss split; stork.ai
  * article, miss policy), one token per step (T = 1, bf16 activations).  Per layer, after the ids
  * and x reach the host (host_idx: k int32, host_x: d bf16, both pinned): the layer's m misses are

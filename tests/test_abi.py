@@ -109,6 +109,17 @@ def test_host_validation_needs_no_gpu(moe):
         assert hstep(1, 9, 1, vp) == moe._lib.MOE_ESHAPE  # k > E
         assert hstep(1, 2, 1, vp) == moe._lib.MOE_EINVAL  # a layer without its input
         assert hstep(0, 2, 1, vp) == 0
+
+        # the split-launch step: (after slot_table) 9 buffers, ws_bytes, host_idx, host_tables,
+        # dev_tables, compute, copy
+        def sstep(n, k, host):
+            return L.moe_decode_step_split(c.h, n, layers.ctypes.data, 1, 256, 128, 8, k, 1, 1, vp, 4, 4096, vp,
+                                           *bufs, 0, host, host, host, None, None)
+
+        assert sstep(1, 2, None) == moe._lib.MOE_EINVAL  # no staging buffers
+        assert sstep(1, 9, vp) == moe._lib.MOE_ESHAPE  # k > E
+        assert sstep(1, 2, vp) == moe._lib.MOE_EINVAL  # a layer without its input
+        assert sstep(0, 2, vp) == 0
     finally:
         c.close()
 

@@ -169,6 +169,30 @@ def test_split_launch_matches_plain_decode(runs):
         assert (s0, l0) == (s1, l1) and np.array_equal(y0, y_to_f64(y1))
 
 
+def test_native_split_matches_the_call_by_call_loop(runs):
+    """moe_decode_step_split makes the split-launch loop's calls: outputs, the hit/miss sequence
+    and copy plan are bitwise those of the Python loop (and of the plain decode)."""
+    from expert_offload_cache_amd.offload import OffloadStack
+
+    _, ref = runs[16]
+    got = []
+    for native in (True, False):
+        stack = OffloadStack(_wl(), L, 16, seed=0, n_images=IMAGES, prefill_tokens=T_PRE)
+        try:
+            stack.prefill()
+            _, dec = stack.decode(_trace(), keep_outputs=True, split_launch=True, native=native)
+            got.append((stack.cache.trace(), stack.cache.copy_log(), stack.cache.stats(),
+                        [(s, l, y_to_f64(y)) for s, l, y in dec]))
+        finally:
+            stack.close()
+    (t0, c0, st0, d0), (t1, c1, st1, d1) = got
+    assert np.array_equal(t0, t1) and np.array_equal(c0, c1) and st0 == st1
+    assert np.array_equal(t0, ref["trace"]) and st0["dec_miss"] > 0
+    assert len(d0) == len(d1) == len(ref["dec"])
+    for (s0, l0, y0), (s1, l1, y1), (s2, l2, y2) in zip(d0, d1, ref["dec"]):
+        assert (s0, l0) == (s1, l1) == (s2, l2) and np.array_equal(y0, y1) and np.array_equal(y0, y2)
+
+
 def test_resize_mid_trace():
     """Shrink then grow between decode steps: outputs bitwise equal to a fixed-capacity run, and
     hits, slots and moves equal to the simulator's."""
