@@ -459,7 +459,7 @@ def main():
     gu_name = kname(m["kern"], "gateup")
     gu_us = m["kern"].get(gu_name)
     achieved = m["avg"]["gateup"] / (gu_us * 1e-6) / 1e9 if gu_us else None
-    traffic = traffic_for("expert_offload_cache_amd/csrc/ffn_gemv_mfma.hip")
+    traffic = traffic_for("expert_offload_cache_amd/csrc/ffn_gemv_ks.hip")
     roofline = {"bound": "hbm", "kernel": gu_name, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": traffic,
                 "bytes_per_launch": m["avg"]["gateup"], "avg_launch_us": gu_us}

@@ -43,9 +43,13 @@ SMALL = [
     ("bf16", "bf16", 512, 128, 6, 2, 33, True),
     # gate/up K = 4096 inputs: the K-streaming kernel (beyond the split-input kernel's shapes)
     ("bf16", "bf16", 4096, 64, 4, 2, 3, False),
-    # gate/up K = 4096 inputs with more than 16 tokens: the VALU kernel runs it
+    # gate/up K = 4096 inputs with more than 16 tokens: the K-streaming kernel's 32-token plan
     ("bf16", "bf16", 4096, 64, 4, 2, 20, False),
-    # 20 down row blocks: the 32-token down plan does not divide them, the split-input kernel runs
+    # 66 input fragments: neither matrix-core gate/up plan divides them, the VALU kernel runs it;
+    # 132 down row blocks: the split-input down kernel
+    ("bf16", "bf16", 2112, 64, 4, 2, 20, False),
+    # 10 gate/up input fragments and 20 down row blocks: the streaming plans do not divide them,
+    # the split-input kernel runs both projections
     ("bf16", "bf16", 320, 96, 8, 2, 9, True),
     # int4 decode: K-streaming for both projections, experts spanning several 16-token items
     ("bf16", "int4", 512, 512, 8, 2, 20, True),
