@@ -13,7 +13,7 @@ import numpy as np
 
 from ._lib import (MOE_BF16, MOE_F32, MOE_INT4_G128, MoeError, check, lib)
 
-__all__ = ["route", "permute", "expert_ffn_grouped", "combine", "slot_bytes", "pack_expert",
+__all__ = ["route", "permute", "route_permute", "expert_ffn_grouped", "combine", "slot_bytes", "pack_expert",
            "workspace_bytes", "SlotCache", "pinned_alloc", "pinned_free", "profile_enable",
            "profile_collect", "profile_results", "profile_reset", "MoeError", "WDT", "lib"]
 
@@ -83,6 +83,24 @@ def permute(topk_idx, E: int, out=None, stream=None):
     c, o, p, ip = out
     check(lib().moe_permute(_p(topk_idx), T, k, E, _p(c), _p(o), _p(p), _p(ip), None, 0, _s(stream)))
     return c, o, p, ip
+
+
+def route_permute(x, w_router, bias, k: int, forced_idx=None, out=None, stream=None):
+    """route then permute as one call -> (topk_idx, topk_w, logits, counts, offsets, perm, inv_perm)."""
+    torch = _torch()
+    _contig(x, w_router, bias, forced_idx)
+    T, d = x.shape
+    E = w_router.shape[0]
+    if out is None:
+        dev = x.device
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty((T, E), dtype=torch.float32, device=dev), torch.empty(E, dtype=torch.int32, device=dev),
+               torch.empty(E + 1, dtype=torch.int32, device=dev), torch.empty(T * k, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev))
+    idx, w, logits, c, o, p, ip = out
+    check(lib().moe_route_permute(_p(x), _act(x), T, d, _p(w_router), _p(bias), E, k, _p(forced_idx), _p(idx),
+                                  _p(w), _p(logits), _p(c), _p(o), _p(p), _p(ip), _s(stream)))
+    return out
 
 
 def workspace_bytes(T, d, f, E, k, has_shared, act: int, wdt: int) -> int:

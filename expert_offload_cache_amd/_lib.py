@@ -22,6 +22,7 @@ SIGNATURES = {
     "moe_pack_expert": (_st, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_route": (_st, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "moe_permute": (_st, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_route_permute": (_st, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _i32] + [_vp] * 9),
     "moe_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_expert_ffn_grouped": (_st, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _sz,
                                      _i32, _vp, _vp, _vp, _sz, _vp]),

@@ -3,11 +3,11 @@
 // picks the experts, the GPU-resident ones are used from their slots and a miss is copied from
 // the pinned host pool first; FreeToken GGUF page, offload backend).
 //
-// Per layer, on the compute stream: route -> ids copied to pinned host memory -> permute; the host
-// waits for the copy only (the cache decides on the host, with no lookahead), so the permutation
-// runs while it decides -> distinct ids, lookup, fill (copies on the copy stream, compute waits)
-// -> grouped experts through the layer's slot-table row -> combine -> mark_read.  The same calls
-// as a caller would make one by one; only the host-side marshalling between them is gone.
+// Per layer, on the compute stream: route + permute (one call) -> ids copied to pinned host
+// memory; the host waits for the copy (the cache decides on the host, with no lookahead) ->
+// distinct ids, lookup, fill (copies on the copy stream, compute waits) -> grouped experts
+// through the layer's slot-table row -> combine -> mark_read.  The same calls as a caller would
+// make one by one; only the host-side marshalling between them is gone.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -49,13 +49,11 @@ extern "C" moe_status moe_decode_step(moe_cache* cache, int n_layers, const moe_
     MOE_HIP(ev.status);
     for (int i = 0; i < n_layers; ++i) {
         const moe_decode_layer& ly = layers[i];
-        moe_status r = moe_route(ly.x, act, T, d, ly.w_router, ly.bias, E, k, ly.forced_idx, topk_idx, topk_w,
-                                 logits, compute);
+        moe_status r = moe_route_permute(ly.x, act, T, d, ly.w_router, ly.bias, E, k, ly.forced_idx, topk_idx,
+                                         topk_w, logits, counts, offsets, perm, inv_perm, compute);
         if (r != MOE_OK) return r;
         MOE_HIP(hipMemcpyAsync(host_idx, topk_idx, sizeof(int32_t) * (size_t)T * k, hipMemcpyDeviceToHost, cs));
         MOE_HIP(hipEventRecord(ev.e, cs));
-        r = moe_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, nullptr, 0, compute);
-        if (r != MOE_OK) return r;
         MOE_HIP(hipEventSynchronize(ev.e));
         std::copy(host_idx, host_idx + (size_t)T * k, ids.begin());
         std::sort(ids.begin(), ids.end());
@@ -121,14 +119,12 @@ extern "C" moe_status moe_decode_step_hybrid(
     MOE_HIP(ev.status);
     for (int i = 0; i < n_layers; ++i) {
         const moe_decode_layer& ly = layers[i];
-        moe_status r = moe_route(ly.x, act, T, d, ly.w_router, ly.bias, E, k, ly.forced_idx, topk_idx, topk_w,
-                                 logits, compute);
+        moe_status r = moe_route_permute(ly.x, act, T, d, ly.w_router, ly.bias, E, k, ly.forced_idx, topk_idx,
+                                         topk_w, logits, counts, offsets, perm, inv_perm, compute);
         if (r != MOE_OK) return r;
         MOE_HIP(hipMemcpyAsync(host_idx, topk_idx, sizeof(int32_t) * k, hipMemcpyDeviceToHost, cs));
         MOE_HIP(hipMemcpyAsync(host_x, ly.x, sizeof(uint16_t) * d, hipMemcpyDeviceToHost, cs));
         MOE_HIP(hipEventRecord(ev.e, cs));
-        r = moe_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, nullptr, 0, compute);
-        if (r != MOE_OK) return r;
         // the event also retires the previous layer's table and row copies (earlier on the stream)
         MOE_HIP(hipEventSynchronize(ev.e));
         std::copy(host_idx, host_idx + k, ids.begin());
@@ -203,13 +199,11 @@ extern "C" moe_status moe_decode_step_split(moe_cache* cache, int n_layers, cons
     MOE_HIP(ev.status);
     for (int i = 0; i < n_layers; ++i) {
         const moe_decode_layer& ly = layers[i];
-        moe_status r = moe_route(ly.x, act, T, d, ly.w_router, ly.bias, E, k, ly.forced_idx, topk_idx, topk_w,
-                                 logits, compute);
+        moe_status r = moe_route_permute(ly.x, act, T, d, ly.w_router, ly.bias, E, k, ly.forced_idx, topk_idx,
+                                         topk_w, logits, counts, offsets, perm, inv_perm, compute);
         if (r != MOE_OK) return r;
         MOE_HIP(hipMemcpyAsync(host_idx, topk_idx, sizeof(int32_t) * (size_t)T * k, hipMemcpyDeviceToHost, cs));
         MOE_HIP(hipEventRecord(ev.e, cs));
-        r = moe_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, nullptr, 0, compute);
-        if (r != MOE_OK) return r;
         // also retires the previous layer's table copy (earlier on the stream)
         MOE_HIP(hipEventSynchronize(ev.e));
         std::copy(host_idx, host_idx + (size_t)T * k, ids.begin());

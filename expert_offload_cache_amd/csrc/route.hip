@@ -18,9 +18,12 @@
 // A second kernel selects and gates, one block per token.
 // Selection is by rank: expert e is chosen iff fewer than k experts beat it (larger logit, or
 // equal logit and lower id), and that count is its output position.
+// moe_route_permute runs the same logits kernels; for one token a single block then selects,
+// gates and sorts (moe_permute's counting sort), which saves a launch.
 #include <hip/hip_runtime.h>
 
 #include "moe_common.h"
+#include "select_permute.h"
 
 #include <algorithm>
 
@@ -275,10 +278,6 @@ __global__ __launch_bounds__(256) void route_logits_split(const uint16_t* __rest
 // rank(e) = number of experts that beat e (larger logit, or equal logit and lower id); the
 // selected experts are those with rank < k and rank is their output position, so every thread
 // finds its own answer without a chain of cross-lane reductions.
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-    return v > bv || (v == bv && i < bi);
-}
-
 __device__ void select_and_gate(const float* s_logit, int E, int k, const int32_t* forced_row, int* s_sel,
                                 float* s_val, int32_t* idx_out, float* w_out) {
     const int tid = threadIdx.x, nth = blockDim.x;
@@ -334,6 +333,42 @@ __global__ __launch_bounds__(1024) void route_topk(const float* __restrict__ log
     __syncthreads();
     select_and_gate(s_logit, E, k, forced ? forced + (size_t)t * k : nullptr, s_sel, s_val,
                     topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
+}
+
+// For one token (batch-1 decode) one block selects and gates (select_and_gate, as route_topk;
+// with more tokens it takes them in turn) and then sorts the T*k pairs with moe_permute's
+// counting sort from the ids it kept in LDS: one launch instead of two.  (A sort by the last of route_topk's blocks would need a
+// device-scope release and acquire, which write back and invalidate an XCD's L2.)
+// Dynamic LDS: WAVES * E ints for the sort, then T * k ids.
+// tokens for which one block selects and sorts: each further token adds its selection's latency
+// (about 3 us on MI355X), and at 2 tokens the two kernels were already faster
+constexpr int kOneBlockMaxT = 1;
+
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void route_topk_permute(const float* __restrict__ logits, int T, int E,
+                                                                 int k, const int32_t* __restrict__ forced,
+                                                                 int nbits, int32_t* __restrict__ topk_idx,
+                                                                 float* __restrict__ topk_w,
+                                                                 int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ perm,
+                                                                 int32_t* __restrict__ inv_perm) {
+    __shared__ __align__(16) float s_logit[1024];
+    __shared__ int s_sel[1024];
+    __shared__ float s_val[1024];
+    __shared__ int32_t s_wave[WAVES];
+    extern __shared__ int32_t dyn[];
+    int32_t* run = dyn;
+    int32_t* s_ids = dyn + WAVES * E;
+    for (int t = 0; t < T; ++t) {
+        for (int e = threadIdx.x; e < E; e += blockDim.x) s_logit[e] = logits[(size_t)t * E + e];
+        __syncthreads();
+        select_and_gate(s_logit, E, k, forced ? forced + (size_t)t * k : nullptr, s_sel, s_val,
+                        topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
+        for (int j = threadIdx.x; j < k; j += blockDim.x) s_ids[t * k + j] = s_sel[j];
+        __syncthreads();  // the next token overwrites s_logit, s_sel and the gate terms
+    }
+    permute_block<WAVES>(s_ids, T * k, E, nbits, counts, offsets, perm, inv_perm, run, s_wave);
 }
 
 // decode: one wave per (token, expert); lane j owns segment j of the row, issues all of its
@@ -455,23 +490,20 @@ __global__ __launch_bounds__(256) void route_logits_wave_tile(const uint16_t* __
     }
 }
 
-}  // namespace
-}  // namespace moe
+moe_status check_route_args(const char* fn, const void* x, moe_dtype act, int T, int d, const void* w_router,
+                             int E, int k, const void* topk_idx, const void* topk_w, const void* logits) {
+    MOE_CHECK(act == MOE_F32 || act == MOE_BF16, MOE_EDTYPE, "%s: activations must be F32 or BF16", fn);
+    MOE_CHECK(E >= 1 && E <= 1024 && k >= 1 && k <= E, MOE_ESHAPE, "%s: need 1 <= k <= E <= 1024 (k=%d E=%d)", fn,
+              k, E);
+    MOE_CHECK(d >= 64 && d <= 16384 && d % 64 == 0, MOE_ESHAPE, "%s: d=%d must be a multiple of 64 in [64,16384]",
+              fn, d);
+    MOE_CHECK(x && w_router && topk_idx && topk_w && logits, MOE_EINVAL, "%s: NULL pointer", fn);
+    MOE_CHECK(T <= (1 << 24), MOE_ESHAPE, "%s: T=%d too large", fn, T);
+    return MOE_OK;
+}
 
-using namespace moe;
-
-extern "C" moe_status moe_route(const void* x, moe_dtype act, int T, int d, const void* w_router,
-                                const float* bias, int E, int k, const int32_t* forced_idx,
-                                int32_t* topk_idx, float* topk_w, float* logits, moe_stream s) {
-    MOE_CHECK(T >= 0, MOE_ESHAPE, "moe_route: T=%d < 0", T);
-    if (T == 0) return MOE_OK;
-    MOE_CHECK(act == MOE_F32 || act == MOE_BF16, MOE_EDTYPE, "moe_route: activations must be F32 or BF16");
-    MOE_CHECK(E >= 1 && E <= 1024 && k >= 1 && k <= E, MOE_ESHAPE, "moe_route: need 1 <= k <= E <= 1024 (k=%d E=%d)", k, E);
-    MOE_CHECK(d >= 64 && d <= 16384 && d % 64 == 0, MOE_ESHAPE, "moe_route: d=%d must be a multiple of 64 in [64,16384]", d);
-    MOE_CHECK(x && w_router && topk_idx && topk_w && logits, MOE_EINVAL, "moe_route: NULL pointer");
-    MOE_CHECK(T <= (1 << 24), MOE_ESHAPE, "moe_route: T=%d too large", T);
-    hipStream_t st = (hipStream_t)s;
-    const bool bf = act == MOE_BF16;
+moe_status launch_route_logits(const void* x, bool bf, int T, int d, const void* w_router, const float* bias,
+                               int E, float* logits, hipStream_t st) {
     if (T >= 32 && T <= 64 && bf && d <= 2048 && (d / 64) % 8 == 0 && E >= 4) {
         // 4 tokens x 4 experts a wave (measured faster than one wave a pair at 64 tokens and
         // d <= 2048, slower at 4-16 tokens or wider rows, where the pair-per-wave kernel has more
@@ -495,13 +527,71 @@ extern "C" moe_status moe_route(const void* x, moe_dtype act, int T, int d, cons
         if (bf) route_logits_tiled<true><<<grid, 256, 0, st>>>(x, w_router, bias, T, d, E, logits);
         else route_logits_tiled<false><<<grid, 256, 0, st>>>(x, w_router, bias, T, d, E, logits);
     }
-    moe_status r = check_launch("route_logits");
-    if (r != MOE_OK) return r;
-    {
-        ProfScope p("route_topk", st);
-        // up to 4 threads per expert share its comparisons
-        const int nth = std::min(1024, std::max(64, (E * 4 + 63) / 64 * 64));
-        route_topk<<<T, nth, 0, st>>>(logits, T, E, k, forced_idx, topk_idx, topk_w);
-    }
+    return check_launch("route_logits");
+}
+
+moe_status launch_route_topk(const float* logits, int T, int E, int k, const int32_t* forced_idx,
+                             int32_t* topk_idx, float* topk_w, hipStream_t st) {
+    ProfScope p("route_topk", st);
+    // up to 4 threads per expert share its comparisons
+    const int nth = std::min(1024, std::max(64, (E * 4 + 63) / 64 * 64));
+    route_topk<<<T, nth, 0, st>>>(logits, T, E, k, forced_idx, topk_idx, topk_w);
     return check_launch("route_topk");
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_route(const void* x, moe_dtype act, int T, int d, const void* w_router,
+                                const float* bias, int E, int k, const int32_t* forced_idx,
+                                int32_t* topk_idx, float* topk_w, float* logits, moe_stream s) {
+    MOE_CHECK(T >= 0, MOE_ESHAPE, "moe_route: T=%d < 0", T);
+    if (T == 0) return MOE_OK;
+    moe_status r = check_route_args("moe_route", x, act, T, d, w_router, E, k, topk_idx, topk_w, logits);
+    if (r != MOE_OK) return r;
+    hipStream_t st = (hipStream_t)s;
+    r = launch_route_logits(x, act == MOE_BF16, T, d, w_router, bias, E, logits, st);
+    if (r != MOE_OK) return r;
+    return launch_route_topk(logits, T, E, k, forced_idx, topk_idx, topk_w, st);
+}
+
+extern "C" moe_status moe_route_permute(const void* x, moe_dtype act, int T, int d, const void* w_router,
+                                        const float* bias, int E, int k, const int32_t* forced_idx,
+                                        int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts,
+                                        int32_t* offsets, int32_t* perm, int32_t* inv_perm, moe_stream s) {
+    MOE_CHECK(T >= 0, MOE_ESHAPE, "moe_route_permute: T=%d < 0", T);
+    if (T == 0) return moe_permute(nullptr, 0, k, E, counts, offsets, perm, inv_perm, nullptr, 0, s);
+    moe_status r = check_route_args("moe_route_permute", x, act, T, d, w_router, E, k, topk_idx, topk_w, logits);
+    if (r != MOE_OK) return r;
+    MOE_CHECK((int64_t)T * k <= (1 << 24), MOE_ESHAPE, "moe_route_permute: T*k too large");
+    MOE_CHECK(counts && offsets && perm && inv_perm, MOE_EINVAL, "moe_route_permute: NULL pointer");
+    hipStream_t st = (hipStream_t)s;
+    r = launch_route_logits(x, act == MOE_BF16, T, d, w_router, bias, E, logits, st);
+    if (r != MOE_OK) return r;
+    // the top-k block's waves: a power of two with 4 threads an expert (as route_topk)
+    int waves = 1;
+    while (waves < 16 && waves * 64 < 4 * E) waves *= 2;
+    const size_t dyn_bytes = sizeof(int32_t) * ((size_t)waves * E + (size_t)T * k);
+    if (T > kOneBlockMaxT || dyn_bytes > 40960) {
+        r = launch_route_topk(logits, T, E, k, forced_idx, topk_idx, topk_w, st);
+        if (r != MOE_OK) return r;
+        return moe_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, nullptr, 0, s);
+    }
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    ProfScope p("route_topk_permute", st);
+#define RTP(W)                                                                                              \
+    route_topk_permute<W><<<1, 64 * W, dyn_bytes, st>>>(logits, T, E, k, forced_idx, nbits, topk_idx, topk_w, \
+                                                         counts, offsets, perm, inv_perm)
+    switch (waves) {
+        case 1: RTP(1); break;
+        case 2: RTP(2); break;
+        case 4: RTP(4); break;
+        case 8: RTP(8); break;
+        default: RTP(16); break;
+    }
+#undef RTP
+    return check_launch("route_topk_permute");
 }

@@ -8,7 +8,7 @@ from typing import Optional
 
 import numpy as np
 
-from . import combine, expert_ffn_grouped, pack_expert, permute, route, slot_bytes, workspace_bytes, WDT
+from . import combine, expert_ffn_grouped, pack_expert, route_permute, slot_bytes, workspace_bytes, WDT
 from ._lib import MOE_BF16, MOE_F32
 
 
@@ -80,8 +80,8 @@ class DeviceLayer:
     def forward(self, x, forced_idx=None, ws=None, stream=None, slot_of_expert=None):
         """x: device tensor [T, d].  Returns a dict of every intermediate and y [T, d]."""
         T = x.shape[0]
-        idx, w, logits = route(x, self.w_router, self.bias, self.k, forced_idx=forced_idx, stream=stream)
-        counts, offsets, perm, inv = permute(idx, self.E, stream=stream)
+        idx, w, logits, counts, offsets, perm, inv = route_permute(x, self.w_router, self.bias, self.k,
+                                                                  forced_idx=forced_idx, stream=stream)
         if ws is None:
             ws = self.workspace(T)
         soe = self.slot_of_expert if slot_of_expert is None else slot_of_expert

@@ -3,7 +3,7 @@ all layers, decode with a per-layer device->host id read-back, prefill that doub
 next layer's experts (FreeToken linux guide, "MoE memory handling" and its mechanism table;
 FreeToken GGUF page, offload backend; FreeToken RTX 5090 page, memory hierarchy and prefill).
 
-Marshalling and orchestration only: every step runs in libmoe (moe_route, moe_permute,
+Marshalling and orchestration only: every step runs in libmoe (moe_route_permute,
 moe_expert_ffn_grouped, moe_combine, moe_cache_*), on two HIP streams (compute, copy).
 
 Pool contents: `n_images` distinct seeded expert images are packed once and key (layer, expert)
@@ -19,8 +19,8 @@ from typing import Optional
 
 import numpy as np
 
-from . import (MoeError, SlotCache, combine, expert_ffn_grouped, pack_expert, permute, pinned_alloc, pinned_free,
-               route, slot_bytes, workspace_bytes, WDT)
+from . import (MoeError, SlotCache, combine, expert_ffn_grouped, pack_expert, pinned_alloc, pinned_free,
+               route_permute, slot_bytes, workspace_bytes, WDT)
 from ._lib import MOE_BF16, MOE_F32
 from .layer import _expert_arrays, _to_device
 
@@ -186,10 +186,9 @@ class OffloadStack:
         """One layer on the compute stream up to the grouped experts' inputs: route + permute."""
         T = x.shape[0]
         b = self._buffers(T)
-        idx, w, _ = route(x, self.w_router[l], self.bias[l], self.k, forced_idx=forced, out=b["route"],
-                          stream=self.compute)
-        perm = permute(idx, self.E, out=b["perm"], stream=self.compute)
-        return idx, w, perm
+        idx, w, _, *perm = route_permute(x, self.w_router[l], self.bias[l], self.k, forced_idx=forced,
+                                         out=b["route"] + b["perm"], stream=self.compute)
+        return idx, w, tuple(perm)
 
     def _experts(self, l: int, x, w, perm, table=None, do_combine: bool = True, with_shared: bool = True):
         """Grouped experts through layer l's slot-table row (or `table`), then the combine (compute
@@ -241,7 +240,7 @@ class OffloadStack:
                hybrid: Optional[tuple] = None, split_launch: bool = False, native: bool = True):
         """Batch-1 decode over a routing trace [steps, L, k]: each layer's ids are forced from the
         trace (gates are the renormalised softmax of the router logits at those ids); per layer
-        route -> ids back to the host -> cache lookup + fill -> permute/GEMV/combine.
+        route + permute -> ids back to the host -> cache lookup + fill -> GEMV/combine.
 
         `first_step` numbers the trace's first row (it selects the activations), so a trace can be
         replayed in pieces, e.g. around a resize.

@@ -128,6 +128,20 @@ MOE_API moe_status moe_permute(const int32_t* topk_idx, int T, int k, int E, int
                                size_t ws_bytes, moe_stream s);
 
 /* ------------------------------------------------------------------------------------------
+ * moe_route_permute -- moe_route followed by moe_permute on its topk_idx, as one call
+ * (FreeToken linux guide, "MoE memory handling": per layer the router picks the experts and
+ * the runtime gathers each expert's tokens).  Every output is bitwise what the two calls give
+ * for the same arguments: logits, topk_idx, topk_w as moe_route; counts, offsets, perm,
+ * inv_perm as moe_permute.  For T = 1 (and E <= 512) one block selects, gates and sorts, one
+ * launch fewer than the two calls; other shapes run the two calls' kernels.  Arguments, shapes,
+ * ownership and errors are those of the two calls; a non-OK status means nothing was enqueued.
+ * With T = 0 only counts and offsets are written (zeros). */
+MOE_API moe_status moe_route_permute(const void* x, moe_dtype act, int T, int d, const void* w_router,
+                                     const float* bias, int E, int k, const int32_t* forced_idx,
+                                     int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts,
+                                     int32_t* offsets, int32_t* perm, int32_t* inv_perm, moe_stream s);
+
+/* ------------------------------------------------------------------------------------------
  * moe_expert_ffn_grouped -- every expert with n_e > 0 runs once on its n_e rows (SwiGLU, the
  * plain reading of the expert form: h = silu(x W_g^T) * (x W_u^T), y = h W_d^T, no biases).
  * Expert e's weights are read from the slot slot_of_expert[e] of slot_pool (FreeToken GGUF
@@ -242,9 +256,9 @@ MOE_API void moe_cache_destroy(moe_cache* c);
 /* ------------------------------------------------------------------------------------------
  * moe_decode_step -- one decode step of an offloaded stack, every layer in one call (FreeToken
  * linux guide, "MoE memory handling"; FreeToken GGUF page, offload backend).  For each layer,
- * in order, on `compute`: moe_route (forced_idx may be NULL); topk_idx copied to host_idx
- * (pinned, T*k int32); moe_permute into the given buffers; the host waits for the copy only (the
- * permutation runs meanwhile); the distinct ids, ascending, to moe_cache_lookup(layer);
+ * in order, on `compute`: moe_route_permute (forced_idx may be NULL) into the given buffers;
+ * topk_idx copied to host_idx (pinned, T*k int32); the host waits for that copy; the distinct
+ * ids, ascending, to moe_cache_lookup(layer);
  * moe_cache_fill(copy, compute); moe_expert_ffn_grouped through slot_table row `layer` (the
  * cache's slot table, device [L*E]); moe_combine into y (act dtype); moe_cache_mark_read(layer).
  * Outputs, cache decisions and statistics are those of the same calls made one by one.  Buffers

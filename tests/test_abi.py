@@ -61,6 +61,17 @@ def test_host_validation_needs_no_gpu(moe):
     assert L.moe_route(None, 1, 4, 128, vp, None, 8, 2, None, vp, vp, vp, None) == moe._lib.MOE_EINVAL
     assert b"NULL" in L.moe_last_error()
     assert L.moe_permute(vp, 4, 2, 2000, vp, vp, vp, vp, None, 0, None) == moe._lib.MOE_ESHAPE
+    # route + permute in one call: the route checks, then the permute buffers
+    rp = L.moe_route_permute
+    assert rp(vp, 1, -1, 128, vp, None, 8, 2, None, vp, vp, vp, vp, vp, vp, vp, None) == moe._lib.MOE_ESHAPE
+    assert rp(vp, 1, 4, 100, vp, None, 8, 2, None, vp, vp, vp, vp, vp, vp, vp, None) == moe._lib.MOE_ESHAPE
+    assert rp(vp, 1, 4, 128, vp, None, 8, 9, None, vp, vp, vp, vp, vp, vp, vp, None) == moe._lib.MOE_ESHAPE
+    assert rp(vp, 7, 4, 128, vp, None, 8, 2, None, vp, vp, vp, vp, vp, vp, vp, None) == moe._lib.MOE_EDTYPE
+    assert rp(vp, 1, 4, 128, None, None, 8, 2, None, vp, vp, vp, vp, vp, vp, vp, None) == moe._lib.MOE_EINVAL
+    assert rp(vp, 1, 4, 128, vp, None, 8, 2, None, vp, vp, vp, vp, vp, None, vp, None) == moe._lib.MOE_EINVAL
+    assert b"moe_route_permute" in L.moe_last_error()
+    assert rp(vp, 1, 4, 128, vp, None, 8, 2, None, vp, vp, vp, vp, vp, vp, None, None) == moe._lib.MOE_EINVAL
+    assert rp(vp, 1, 0, 128, vp, None, 2000, 2, None, vp, vp, vp, vp, vp, vp, vp, None) == moe._lib.MOE_ESHAPE
     assert L.moe_combine(vp, vp, vp, 4, 2, 6, 0, vp, 1, None) == moe._lib.MOE_ESHAPE
     a = ctypes.c_void_p(256)
     # int4 weights need bf16 activations; dense weights must match the activation dtype

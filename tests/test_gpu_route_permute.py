@@ -107,3 +107,98 @@ def test_permute_bit_exact(T, E, k, kind):
     assert np.array_equal(go.cpu().numpy(), o)
     assert np.array_equal(gp.cpu().numpy(), p)
     assert np.array_equal(gip.cpu().numpy(), ip)
+
+
+RP_CASES = [
+    # (act, d, E, k, T, bias, kind): moe_route_permute; for T = 1 one block selects and sorts
+    # (when its LDS holds E and the ids), other shapes run the two calls' kernels
+    ("f32", 64, 8, 2, 1, None, "rand"),        # one wave
+    ("f32", 64, 8, 2, 2, 1.1, "rand"),
+    ("f32", 64, 8, 2, 16, None, "rand"),
+    ("bf16", 2048, 128, 8, 1, 1.1, "rand"),    # Qwen-A3B shaped decode, 8 waves
+    ("bf16", 2048, 128, 8, 2, 1.1, "rand"),
+    ("bf16", 2048, 128, 8, 4, 1.1, "rand"),
+    ("bf16", 2048, 128, 8, 64, 1.1, "rand"),
+    ("bf16", 4096, 256, 6, 1, 1.1, "rand"),    # DeepSeek-V4-Flash shaped decode, 16 waves
+    ("bf16", 4096, 256, 6, 2, 1.1, "rand"),
+    ("bf16", 4096, 256, 6, 8, 1.1, "rand"),
+    ("bf16", 512, 100, 16, 2, None, "rand"),   # ragged E
+    ("bf16", 256, 16, 16, 2, 1.1, "rand"),     # k = E
+    ("bf16", 512, 40, 3, 1, 1.1, "rand"),      # 3 waves rounded to 4
+    ("bf16", 512, 100, 16, 1, None, "rand"),
+    ("bf16", 256, 16, 16, 1, 1.1, "rand"),
+    ("bf16", 256, 64, 8, 1, None, "ties"),
+    ("bf16", 256, 64, 8, 1, None, "flat"),
+    ("bf16", 4096, 256, 6, 1, 1.1, "forced"),
+    ("bf16", 256, 64, 8, 2, None, "ties"),     # pairs of equal logits: lower id first
+    ("bf16", 256, 64, 8, 40, None, "ties"),
+    ("bf16", 256, 64, 8, 2, None, "flat"),     # every logit +0: experts 0..k-1, equal gates
+    ("bf16", 4096, 256, 6, 2, 1.1, "forced"),  # replayed ids
+    ("bf16", 4096, 256, 6, 37, 1.1, "forced"),
+    ("bf16", 512, 512, 64, 1, 1.1, "rand"),    # largest E the one block holds, k = 64
+    ("bf16", 512, 512, 64, 2, 1.1, "rand"),
+    ("bf16", 512, 513, 8, 1, 1.1, "rand"),     # past it: two launches
+    ("bf16", 1024, 1024, 8, 2, None, "rand"),
+    ("bf16", 2048, 128, 8, 65, 1.1, "rand"),
+    ("bf16", 4096, 256, 6, 512, 1.1, "rand"),  # prefill batch
+]
+
+
+@pytest.mark.parametrize("act,d,E,k,T,bias,kind", RP_CASES)
+def test_route_permute_matches_the_two_calls_and_the_oracle(act, d, E, k, T, bias, kind):
+    need_gpu()
+    import expert_offload_cache_amd as moe
+
+    print(f"route_permute act={act} d={d} E={E} k={k} T={T} {kind}", flush=True)
+    gen = synth.normal_bf16 if act == "bf16" else synth.normal_f32
+    x = gen(13, synth.stream_id(synth.KIND_X, 1, T), (T, d), 1.0)
+    if kind == "ties":
+        w = np.repeat(gen(13, synth.stream_id(synth.KIND_ROUTER, 1, E), (E // 2, d), 0.02), 2, axis=0)
+    elif kind == "flat":
+        w = np.zeros_like(gen(13, synth.stream_id(synth.KIND_ROUTER, 1, E), (E, d), 0.02))
+    else:
+        w = gen(13, synth.stream_id(synth.KIND_ROUTER, 1, E), (E, d), 0.02)
+    b = synth.router_bias(13, E, bias) if bias else None
+    forced = synth.forced_topk(13, T, E, k) if kind == "forced" else None
+    lg = router_logits(x, w, b, act)
+    idx = forced if forced is not None else topk_select(lg, k)
+    g = renorm_gates(lg, idx)
+    c, o, p, ip = o_permute(idx, E)
+
+    xd, wd = to_dev(x, act), to_dev(w, act)
+    bd = None if b is None else to_dev(b, "f32")
+    fd = None if forced is None else to_dev(forced, "i32")
+    out = moe.route_permute(xd, wd, bd, k, forced_idx=fd)
+    moe.route_permute(xd, wd, bd, k, forced_idx=fd, out=out)  # again into the same buffers
+    got = [a.cpu().numpy() for a in out]
+    gi, gw, gl = moe.route(xd, wd, bd, k, forced_idx=fd)
+    two = [gi, gw, gl] + list(moe.permute(gi, E))
+    two = [a.cpu().numpy() for a in two]
+    for name, a, r in zip(["topk_idx", "topk_w", "logits", "counts", "offsets", "perm", "inv_perm"], got, two):
+        assert a.shape == r.shape and np.array_equal(a.view(np.uint32), r.view(np.uint32)), name
+    assert np.array_equal(got[2].view(np.uint32), lg.view(np.uint32)), "logits differ from the oracle"
+    assert np.array_equal(got[0], idx)
+    assert np.max(np.abs(got[1].astype(np.float64) - g) / g) <= 1e-6
+    for a, r in zip(got[3:], (c, o, p, ip)):
+        assert np.array_equal(a, r)
+    if kind == "ties":
+        assert np.all(got[0][:, 0] % 2 == 0)  # of an equal pair the even (lower) id comes first
+    if kind == "flat":
+        assert np.array_equal(got[0], np.tile(np.arange(k, dtype=np.int32), (T, 1)))
+        assert np.all(got[1] == np.float32(1.0 / k))
+
+
+def test_route_permute_empty_batch():
+    need_gpu()
+    import torch
+
+    import expert_offload_cache_amd as moe
+
+    E, k, d = 128, 8, 2048
+    x = torch.empty((0, d), dtype=torch.bfloat16, device="cuda")
+    w = to_dev(synth.normal_bf16(1, 1, (E, d), 0.02), "bf16")
+    out = moe.route_permute(x, w, None, k)
+    torch.cuda.synchronize()
+    assert out[0].shape == (0, k) and out[5].numel() == 0
+    assert np.array_equal(out[3].cpu().numpy(), np.zeros(E, np.int32))
+    assert np.array_equal(out[4].cpu().numpy(), np.zeros(E + 1, np.int32))
