@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-int4", action="store_true")
     ap.add_argument("--no-offload", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the decode steps as replays of a HIP graph per layer (layer_us_graph)")
     ap.add_argument("--offload-layers", type=int, default=12,
                     help="stacked layers in the pinned pool (24 need ~80 GB of pinned host memory)")
     ap.add_argument("--offload-steps", type=int, default=2048)
@@ -156,9 +158,11 @@ def replicate(base, R):
     return layers
 
 
-def time_layer(moe, wl, layers, T, steps, warmup, stream, forced=None):
-    """Wall time of `steps` layer forwards rotating over the replicas, then a second pass with
-    the library's per-kernel HIP-event timing.  -> (seconds, {kernel: avg us}, per-replica counts)."""
+def time_layer(moe, wl, layers, T, steps, warmup, stream, forced=None, graph=False):
+    """Wall time of `steps` layer forwards rotating over the replicas (eager calls); with `graph`
+    also of the same steps as replays of one HIP graph per replica holding the same calls; then a
+    pass with the library's per-kernel HIP-event timing (eager).  -> (eager seconds,
+    {kernel: avg us}, per-replica counts, graph-replay seconds or None)."""
     import torch
     import synth
 
@@ -181,6 +185,25 @@ def time_layer(moe, wl, layers, T, steps, warmup, stream, forced=None):
         run(steps, keep=True)
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
+    el_graph = None
+    if graph:
+        graphs = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                layers[r].forward(xs[r], ws=wss[r], forced_idx=forced)
+            graphs.append(g)
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                graphs[i % R].replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                graphs[i % R].replay()
+            torch.cuda.synchronize()
+            el_graph = time.perf_counter() - t0
+        del graphs
+    with torch.cuda.stream(stream):
         moe.profile_reset()
         moe.profile_enable(True)
         run(steps)
@@ -188,7 +211,7 @@ def time_layer(moe, wl, layers, T, steps, warmup, stream, forced=None):
         moe.profile_collect()
         moe.profile_enable(False)
     kern = {name: ms / n * 1e3 for name, (ms, n) in moe.profile_results().items()}
-    return el, kern, [c.cpu().numpy() for c in outs]
+    return el, kern, [c.cpu().numpy() for c in outs], el_graph
 
 
 def kname(kern, part):
@@ -223,10 +246,11 @@ def bench_decode(args, moe, stream):
     for T in tlist:
         steps = args.steps if T == Tmain else max(20, args.steps // 4)
         log(f"decode T={T}: {steps} timed steps")
-        el, kern, counts = time_layer(moe, wl, layers, T, steps, args.warmup, stream)
+        el, kern, counts, el_graph = time_layer(moe, wl, layers, T, steps, args.warmup, stream,
+                                                graph=args.graph)
         byts = [algorithmic_bytes(c, T, wl.d, wl.f, wl.k, wl.E) for c in counts]
         avg = {key: float(np.mean([b[key] for b in byts])) for key in ("U", "gateup", "down", "layer")}
-        res[T] = dict(el=el, steps=steps, avg=avg, kern=kern)
+        res[T] = dict(el=el, el_graph=el_graph, steps=steps, avg=avg, kern=kern)
     del layers
     return wl, li, res
 
@@ -239,7 +263,7 @@ def prefill_figures(moe, wl, layer, Ts, stream, w_bytes=2.0):
     out = {}
     for T in Ts:
         steps = 10
-        el, kern, counts = time_layer(moe, wl, [layer], T, steps, 2, stream)
+        el, kern, counts, _ = time_layer(moe, wl, [layer], T, steps, 2, stream)
         c = counts[0]
         rows = T * wl.k + T
         U = int((c > 0).sum()) + 1
@@ -261,7 +285,7 @@ def prefill_figures(moe, wl, layer, Ts, stream, w_bytes=2.0):
         log(f"{wl.name} prefill T={T}: {out[str(T)]['tokens_per_s']:.0f} tok/s, FFN {out[str(T)]['ffn_TFLOPs']:.0f} TF/s")
     T = Ts[-1]
     forced = torch.from_numpy(np.tile(np.arange(wl.k, dtype=np.int32), (T, 1))).to("cuda")
-    el, kern, _ = time_layer(moe, wl, [layer], T, 10, 2, stream, forced=forced)
+    el, kern, _, _ = time_layer(moe, wl, [layer], T, 10, 2, stream, forced=forced)
     rows = T * wl.k + T
     fl_gu, fl_dn = 2.0 * rows * 2 * wl.f * wl.d, 2.0 * rows * wl.d * wl.f
     gu, dn = kern.get(kname(kern, "gateup")), kern.get(kname(kern, "down"))
@@ -360,7 +384,7 @@ def bench_prefill(moe, stream):
     return out
 
 
-def bench_int4(moe, stream, replicas=4):
+def bench_int4(moe, stream, replicas=4, graph=False):
     import torch
     import synth
     from expert_offload_cache_amd.layer import DeviceLayer
@@ -373,12 +397,13 @@ def bench_int4(moe, stream, replicas=4):
     wb = 0.5 + 2.0 / 128  # int4 weight bytes per element, with its bf16 group scale
     for T in wl.T_list:
         steps = 100
-        el, kern, counts = time_layer(moe, wl, layers, T, steps, 10, stream)
+        el, kern, counts, el_graph = time_layer(moe, wl, layers, T, steps, 10, stream, graph=graph)
         b = [algorithmic_bytes(c, T, wl.d, wl.f, wl.k, wl.E, w_bytes=wb, shared=True) for c in counts]
         gu_b = float(np.mean([x["gateup"] for x in b]))
         dn_b = float(np.mean([x["down"] for x in b]))
         gu, dn = kern.get(kname(kern, "gateup")), kern.get(kname(kern, "down"))
         out[str(T)] = {"tokens_per_s": T * steps / el, "layer_us": el / steps * 1e6,
+                       "layer_us_graph": el_graph / steps * 1e6 if el_graph else None,
                        "gateup_us": gu, "down_us": dn, "gateup_GBps": gu_b / gu / 1e3,
                        "ffn_GBps": (gu_b + dn_b) / (gu + dn) / 1e3, "kernels_us": kern}
         log(f"int4 decode T={T}: {out[str(T)]['tokens_per_s']:.0f} tok/s, FFN {out[str(T)]['ffn_GBps']:.0f} GB/s")
@@ -470,6 +495,8 @@ def main():
         ffn_us = (gu or 0) + (dn or 0)
         sweep[str(T)] = {
             "tokens_per_s": T * r["steps"] / r["el"], "layer_us": r["el"] / r["steps"] * 1e6,
+            "layer_us_graph": r["el_graph"] / r["steps"] * 1e6 if r["el_graph"] else None,
+
             "touched_experts": r["avg"]["U"], "gateup_us": gu, "down_us": dn,
             "gateup_GBps": r["avg"]["gateup"] / (gu * 1e-6) / 1e9 if gu else None,
             "ffn_GBps": (r["avg"]["gateup"] + r["avg"]["down"]) / (ffn_us * 1e-6) / 1e9 if ffn_us else None,
@@ -480,7 +507,7 @@ def main():
 
     extra = {"hbm_copy_GBps": hbm_copy_GBps()}
     for name, enabled, fn in (("prefill_bf16", not args.no_prefill, lambda: bench_prefill(moe, stream)),
-                              ("decode_int4", not args.no_int4, lambda: bench_int4(moe, stream))):
+                              ("decode_int4", not args.no_int4, lambda: bench_int4(moe, stream, graph=args.graph))):
         if enabled:
             try:
                 extra[name] = fn()
@@ -517,7 +544,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "qwen3.6-35b-a3b shaped decode MoE layer", "tokens": Tmain, "d_model": wl.d,
                    "experts": wl.E, "top_k": wl.k, "d_ff": wl.f, "weights": "bf16", "router_bias": "zipf(1.1)",
-                   "hbm_replicas": args.replicas, "parallelism": "single gpu"},
+                   "hbm_replicas": args.replicas, "parallelism": "single gpu", "launch": "eager calls"},
         "roofline": roofline, "cpu_baseline": cpu, "sweep": sweep, **extra,
     }
     print(json.dumps(line))
