@@ -169,12 +169,13 @@ def time_layer(moe, wl, layers, T, steps, warmup, stream, forced=None, graph=Fal
     R = len(layers)
     base = layers[0]
     xs = [base.x_to_device(synth.layer_inputs(wl, T, seed=0, batch=b, with_experts=False).x) for b in range(R)]
-    wss = [base.workspace(T) for _ in range(R)]
+    bufs = [base.buffers(T) for _ in range(R)]  # outputs allocated once per replica, as a serving loop
+    wss = [b["ws"] for b in bufs]
     outs = []
 
     def run(n, keep=False):
         for i in range(n):
-            o = layers[i % R].forward(xs[i % R], ws=wss[i % R], stream=stream, forced_idx=forced)
+            o = layers[i % R].forward(xs[i % R], stream=stream, forced_idx=forced, bufs=bufs[i % R])
             if keep and i < R:
                 outs.append(o["counts"])
 

@@ -118,8 +118,8 @@ def expert_ffn_grouped(x, perm, offsets, counts, slot_of_expert, slot_pool, n_sl
     rows = T * k + (T if shared_w is not None else 0)
     if y_perm is None:
         y_perm = torch.empty((rows, d), dtype=torch.float32, device=x.device)
-    need = workspace_bytes(T, d, f, E, k, shared_w is not None, act, WDT[wdt])
     if ws is None:
+        need = workspace_bytes(T, d, f, E, k, shared_w is not None, act, WDT[wdt])
         ws = torch.zeros(need, dtype=torch.uint8, device=x.device)
     check(lib().moe_expert_ffn_grouped(_p(x), act, T, d, f, E, k, _p(perm), _p(offsets), _p(counts),
                                        _p(slot_of_expert), n_slots, _p(slot_pool), slot_stride, WDT[wdt],

@@ -77,16 +77,36 @@ class DeviceLayer:
         n = workspace_bytes(T, self.d, self.f, self.E, self.k, self.shared is not None, self.act_code, WDT[self.wdt])
         return torch.zeros(n, dtype=torch.uint8, device=self.device)
 
-    def forward(self, x, forced_idx=None, ws=None, stream=None, slot_of_expert=None):
-        """x: device tensor [T, d].  Returns a dict of every intermediate and y [T, d]."""
+    def buffers(self, T: int):
+        """Outputs of a T-token forward allocated once (a serving loop's buffers): forward(...,
+        bufs=...) writes into them, so each call overwrites the previous call's results."""
+        import torch
+
+        dev, k, E, d = self.device, self.k, self.E, self.d
+        rows = T * k + (T if self.shared is not None else 0)
+        i32 = dict(dtype=torch.int32, device=dev)
+        return dict(
+            route=(torch.empty((T, k), **i32), torch.empty((T, k), dtype=torch.float32, device=dev),
+                   torch.empty((T, E), dtype=torch.float32, device=dev), torch.empty(E, **i32),
+                   torch.empty(E + 1, **i32), torch.empty(T * k, **i32), torch.empty(T * k, **i32)),
+            y_perm=torch.empty((rows, d), dtype=torch.float32, device=dev),
+            y=torch.empty((T, d), dtype=torch.bfloat16 if self.act == "bf16" else torch.float32, device=dev),
+            ws=self.workspace(T))
+
+    def forward(self, x, forced_idx=None, ws=None, stream=None, slot_of_expert=None, bufs=None):
+        """x: device tensor [T, d].  Returns a dict of every intermediate and y [T, d].  With
+        `bufs` (from buffers(T)) the outputs are written there instead of new tensors."""
         T = x.shape[0]
+        b = bufs or {}
         idx, w, logits, counts, offsets, perm, inv = route_permute(x, self.w_router, self.bias, self.k,
-                                                                  forced_idx=forced_idx, stream=stream)
+                                                                  forced_idx=forced_idx, out=b.get("route"),
+                                                                  stream=stream)
         if ws is None:
-            ws = self.workspace(T)
+            ws = b["ws"] if "ws" in b else self.workspace(T)
         soe = self.slot_of_expert if slot_of_expert is None else slot_of_expert
         y_perm, ws = expert_ffn_grouped(x, perm, offsets, counts, soe, self.pool, self.n_slots, self.stride,
-                                        self.wdt, self.f, self.k, shared_w=self.shared, ws=ws, stream=stream)
-        y = combine(y_perm, w, inv, self.k, self.shared is not None, x.dtype, stream=stream)
+                                        self.wdt, self.f, self.k, shared_w=self.shared, y_perm=b.get("y_perm"),
+                                        ws=ws, stream=stream)
+        y = combine(y_perm, w, inv, self.k, self.shared is not None, x.dtype, y=b.get("y"), stream=stream)
         return dict(y=y, topk_idx=idx, topk_w=w, logits=logits, counts=counts, offsets=offsets, perm=perm,
                     inv_perm=inv, y_perm=y_perm, ws=ws)

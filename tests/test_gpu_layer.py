@@ -115,6 +115,29 @@ def test_qwen_a3b_decode_layer(qwen_layer, T):
     assert err.max() <= 2e-2
 
 
+@pytest.mark.parametrize("T", [1, 64])
+def test_forward_into_preallocated_buffers(qwen_layer, T):
+    """forward(..., bufs=layer.buffers(T)) writes bitwise what a forward with fresh outputs
+    returns, call after call with different inputs."""
+    import torch
+
+    wl, _, layer = qwen_layer
+    print(f"preallocated buffers T={T}", flush=True)
+    bufs = layer.buffers(T)
+    keys = ("y", "topk_idx", "topk_w", "logits", "counts", "offsets", "perm", "inv_perm", "y_perm")
+    for b in (1, 2, 1):
+        x = layer.x_to_device(synth.layer_inputs(wl, T, seed=0, batch=b, with_experts=False).x)
+        fresh = layer.forward(x)
+        got = layer.forward(x, bufs=bufs)
+        torch.cuda.synchronize()
+        assert got["y"].data_ptr() == bufs["y"].data_ptr()
+        for key in keys:
+            a, r = got[key], fresh[key]
+            if a.dtype == torch.bfloat16:
+                a, r = a.view(torch.int16), r.view(torch.int16)
+            assert torch.equal(a, r), f"batch {b}: {key}"
+
+
 def test_determinism_and_slot_order_invariance(qwen_layer):
     """Two runs are bitwise identical; a different slot order gives bitwise identical outputs."""
     import torch
