@@ -32,6 +32,10 @@ ROUTE_CASES = [
     ("bf16", 2048, 128, 8, 100, 1.1),     # subtree-split prefill kernel, ragged tokens
     ("bf16", 2048, 100, 4, 97, None),     # ... ragged experts, no bias
     ("bf16", 6144, 96, 4, 130, 1.1),      # ... three chunks per segment
+    ("bf16", 1024, 256, 8, 33, 1.1),      # tiled decode logits, 2 chunks of 8 a lane
+    ("bf16", 1024, 512, 8, 5, None),      # one wave a pair, 512 experts
+    ("bf16", 2048, 100, 4, 3, None),      # ragged experts
+    ("bf16", 2048, 256, 8, 2, 1.1),
 ]
 
 
@@ -141,6 +145,15 @@ RP_CASES = [
     ("bf16", 1024, 1024, 8, 2, None, "rand"),
     ("bf16", 2048, 128, 8, 65, 1.1, "rand"),
     ("bf16", 4096, 256, 6, 512, 1.1, "rand"),  # prefill batch
+    # more ties, equal logits and replayed ids on both paths
+    ("bf16", 1024, 64, 8, 1, None, "ties"),
+    ("bf16", 1024, 64, 8, 1, None, "flat"),
+    ("bf16", 1024, 64, 8, 9, None, "ties"),
+    ("bf16", 2048, 128, 8, 1, 1.1, "forced"),
+    ("bf16", 2048, 128, 8, 5, 1.1, "forced"),
+    ("bf16", 1024, 512, 16, 1, 1.1, "rand"),
+    ("bf16", 2048, 100, 4, 1, None, "rand"),
+    ("bf16", 1024, 256, 8, 64, 1.1, "rand"),
 ]
 
 
