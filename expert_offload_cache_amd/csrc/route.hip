@@ -295,6 +295,8 @@ __device__ void select_and_gate(const float* s_logit, int E, int k, const int32_
             const int e = b / P, p = b - e * P;
             const float v = s_logit[e];
             int r = 0;
+            // unrolled so that the LDS reads issue back to back (an integer count: order-free)
+#pragma unroll 8
             for (int i = p; i < E; i += P) r += better(s_logit[i], i, v, e);
             if (P >= 2) r += __shfl_xor(r, 1, 64);
             if (P >= 4) r += __shfl_xor(r, 2, 64);
@@ -309,11 +311,13 @@ __device__ void select_and_gate(const float* s_logit, int E, int k, const int32_
     // term exp(v_j - max) once; every thread then sums the k terms in ascending order.
     __shared__ double s_term[1024];
     double m = -INFINITY;
+#pragma unroll 8
     for (int i = 0; i < k; ++i) m = fmax(m, (double)s_val[i]);
     for (int j = tid; j < k; j += nth) s_term[j] = exp((double)s_val[j] - m);
     __syncthreads();
     for (int j = tid; j < k; j += nth) {
         double den = 0.0;
+#pragma unroll 8
         for (int i = 0; i < k; ++i) den += s_term[i];
         idx_out[j] = s_sel[j];
         w_out[j] = (float)(s_term[j] / den);
