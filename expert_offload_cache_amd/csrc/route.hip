@@ -509,12 +509,12 @@ moe_status check_route_args(const char* fn, const void* x, moe_dtype act, int T,
 moe_status launch_route_logits(const void* x, bool bf, int T, int d, const void* w_router, const float* bias,
                                int E, float* logits, hipStream_t st) {
     if (T >= 32 && T <= 64 && bf && d <= 2048 && (d / 64) % 8 == 0 && E >= 4) {
-        // 4 tokens x 4 experts a wave (measured faster than one wave a pair at 64 tokens and
-        // d <= 2048, slower at 4-16 tokens or wider rows, where the pair-per-wave kernel has more
-        // waves)
-        const long tiles = (long)((T + 3) / 4) * ((E + 3) / 4);
+        // 4 tokens x 2 experts a wave (measured faster than one wave a pair and than 4 x 4 tiles
+        // at 64 tokens and d <= 2048; slower at 4-16 tokens or wider rows, where the pair-per-wave
+        // kernel has more waves)
+        const long tiles = (long)((T + 3) / 4) * ((E + 1) / 2);
         ProfScope p("route_logits_wave", st);
-        route_logits_wave_tile<4, 4, 4><<<(unsigned)((tiles + 3) / 4), 256, 0, st>>>(
+        route_logits_wave_tile<4, 2, 4><<<(unsigned)((tiles + 3) / 4), 256, 0, st>>>(
             (const uint16_t*)x, (const uint16_t*)w_router, bias, T, d, E, logits);
     } else if (T <= 64) {
         const long waves = (long)T * E;
