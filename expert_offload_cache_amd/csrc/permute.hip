@@ -44,7 +44,8 @@ extern "C" moe_status moe_permute(const int32_t* topk_idx, int T, int k, int E, 
     hipStream_t st = (hipStream_t)s;
     ProfScope p("permute", st);
     const int N = T * k;
-    if (N <= 4096) permute_kernel<4><<<1, 256, 0, st>>>(topk_idx, N, E, nbits, counts, offsets, perm, inv_perm);
+    // 8 waves up to 4096 pairs (4.1 us at 512 pairs against 4.5 with 4 waves, 6.8 with 2), 16 above
+    if (N <= 4096) permute_kernel<8><<<1, 512, 0, st>>>(topk_idx, N, E, nbits, counts, offsets, perm, inv_perm);
     else permute_kernel<16><<<1, 1024, 0, st>>>(topk_idx, N, E, nbits, counts, offsets, perm, inv_perm);
     return check_launch("permute");
 }
