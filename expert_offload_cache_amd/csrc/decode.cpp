@@ -123,7 +123,6 @@ extern "C" moe_status moe_decode_step_hybrid(
                                          topk_w, logits, counts, offsets, perm, inv_perm, compute);
         if (r != MOE_OK) return r;
         MOE_HIP(hipMemcpyAsync(host_idx, topk_idx, sizeof(int32_t) * k, hipMemcpyDeviceToHost, cs));
-        MOE_HIP(hipMemcpyAsync(host_x, ly.x, sizeof(uint16_t) * d, hipMemcpyDeviceToHost, cs));
         MOE_HIP(hipEventRecord(ev.e, cs));
         // the event also retires the previous layer's table and row copies (earlier on the stream)
         MOE_HIP(hipEventSynchronize(ev.e));
@@ -138,6 +137,27 @@ extern "C" moe_status moe_decode_step_hybrid(
             if (sl < 0) miss.push_back(ids[j]);
         }
         const int n_cpu = hybrid_split((int)miss.size(), cpu_rate, pcie_rate);
+        if (n_cpu == 0) {
+            // nothing for the host in this layer: the plain step (the cache's own slot-table row,
+            // no table or activation copies), with the same cache decisions and outputs
+            int32_t n_miss = 0;
+            r = moe_cache_lookup(cache, ly.layer, ids.data(), n, slots.data(), &n_miss);
+            if (r != MOE_OK) return r;
+            r = moe_cache_fill(cache, copy, compute);
+            if (r != MOE_OK) return r;
+            r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts,
+                                       slot_table + (size_t)ly.layer * E, n_slots, slot_pool, slot_stride, w,
+                                       ly.shared_w, y_perm, ws, ws_bytes, compute);
+            if (r != MOE_OK) return r;
+            r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
+            if (r != MOE_OK) return r;
+            r = moe_cache_mark_read(cache, ly.layer, compute);
+            if (r != MOE_OK) return r;
+            continue;
+        }
+        // the host's experts need the activation row; it crosses while the cache decides
+        MOE_HIP(hipMemcpyAsync(host_x, ly.x, sizeof(uint16_t) * d, hipMemcpyDeviceToHost, cs));
+        MOE_HIP(hipEventRecord(ev.e, cs));
         on_cpu.assign(miss.end() - n_cpu, miss.end());  // the highest-numbered misses
         gpu_ids.clear();
         for (int j = 0; j < n; ++j)
@@ -156,6 +176,7 @@ extern "C" moe_status moe_decode_step_hybrid(
                                    slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, compute);
         if (r != MOE_OK) return r;
         // the host's experts run while the copies and the GPU's experts do
+        MOE_HIP(hipEventSynchronize(ev.e));  // host_x has arrived
         for (int e : on_cpu) {
             const int row = (int)(std::lower_bound(ids.begin(), ids.begin() + n, e) - ids.begin());
             const void* img = cache_host_image(cache, ly.layer, e);

@@ -301,9 +301,11 @@ MOE_API moe_status moe_decode_step_split(moe_cache* cache, int n_layers, const m
 
 /* moe_decode_step with hybrid miss handling (FreeToken RTX 5090 page, miss split; stork.ai
  * article, miss policy), one token per step (T = 1, bf16 activations).  Per layer, after the ids
- * and x reach the host (host_idx: k int32, host_x: d bf16, both pinned): the layer's m misses are
+ * reach the host (host_idx: k int32, pinned): the layer's m misses are
  * split, the host taking the n highest-numbered ones, n minimising max((m-n)/pcie_rate, n/cpu_rate)
- * (rates in expert images per second; ties to fewer on the host); the other ids (all of them
+ * (rates in expert images per second; ties to fewer on the host).  A layer with n = 0 runs as in
+ * moe_decode_step (the slot-table row as is).  Otherwise x is copied to host_x (d bf16, pinned)
+ * while the cache decides, and the other ids (all of them
  * with copy_too, whose host experts are then also inserted, their copies deferred through
  * moe_cache_fill_split) go to moe_cache_lookup and a fill; the layer's table row is staged in
  * host_table (pinned, E int32) and copied to dev_table (device, E int32) with the host experts
