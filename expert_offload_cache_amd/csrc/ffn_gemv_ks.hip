@@ -337,11 +337,12 @@ static moe_status launch_ks(const FfnArgs& a, hipStream_t st, const char* name) 
 // Launch shape by projection, weight type and batch (-1: leave the launch to the other decode
 // kernels).  Chosen by measurement on MI355X over the decode workloads (Qwen3-30B-A3B-like bf16
 // and DeepSeek-V4-Flash-like int4 layers, 1 to 64 tokens):
-//   bf16 gate/up: four waves split the inputs of each gate/up pair, interleaved (wave s takes
-//     stages s, s+4, ...: the group reads 4 KB of adjacent fragments at a time, measured 1-2 us
-//     faster than contiguous shares), over 16-token items up to 16 tokens and 32-token items
-//     above (faster than the split-input kernel at 64 tokens although the experts holding more
-//     than 32 tokens read their weights twice);
+//   bf16 gate/up: four waves split the inputs of a wave's row blocks, interleaved (wave s takes
+//     stages s, s+4, ...: the group reads adjacent fragments at a time, measured 1-2 us faster
+//     than contiguous shares); one gate/up pair a wave over 16-token items up to 16 tokens, two
+//     pairs a wave over 32-token items above (58.8 against 60.4 us at 64 tokens for one pair;
+//     faster than the split-input kernel at 64 tokens although the experts holding more than 32
+//     tokens read their weights twice);
 //   bf16 down: one row block a wave with 5 stages in flight for up to 4 tokens, else two row
 //     blocks a wave over 32-token items;
 //   int4 gate/up: two waves split the inputs from 2 tokens on; a single token stays on the
@@ -365,7 +366,7 @@ moe_status ffn_gemv_ks(const FfnArgs& a, int mode, moe_dtype w, hipStream_t st) 
     if (plan < 0) return MOE_EDTYPE;
     if (w == MOE_BF16 && mode == kGateUp) {
         if (plan == 0) return launch_ks<kGateUp, MOE_BF16, 2, 1, 4, 4, false, true>(a, st, "ffn_gemv_gateup_bf16");
-        return launch_ks<kGateUp, MOE_BF16, 2, 2, 4, 4, false, true>(a, st, "ffn_gemv_gateup_bf16");
+        return launch_ks<kGateUp, MOE_BF16, 4, 2, 4, 4, false, true>(a, st, "ffn_gemv_gateup_bf16");
     }
     if (w == MOE_BF16) {
         if (plan == 0) return launch_ks<kDown, MOE_BF16, 1, 1, 6, 1>(a, st, "ffn_gemv_down_bf16");
