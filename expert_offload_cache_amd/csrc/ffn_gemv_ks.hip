@@ -345,17 +345,19 @@ static moe_status launch_ks(const FfnArgs& a, hipStream_t st, const char* name) 
 //     tokens read their weights twice);
 //   bf16 down: one row block a wave with 5 stages in flight for up to 4 tokens, else two row
 //     blocks a wave over 32-token items;
-//   int4 gate/up: two waves split the inputs from 2 tokens on; a single token stays on the
-//     vector-ALU kernel (equal time);
+//   int4 gate/up: two waves split the inputs of a gate/up pair from 2 tokens on, and from 8 tokens
+//     one wave takes two pairs over all inputs with two stages in flight (65.6 against 67.9 us
+//     at 8 tokens); a single token stays on the vector-ALU kernel (equal time);
 //   int4 down: up to 4 tokens, one row block a wave with 7 stages in flight and the item's h rows
-//     staged in LDS; above that two waves split the inputs.
+//     staged in LDS; above that four row blocks a wave with one stage in flight ahead (33.8
+//     against 41.7 us at 8 tokens for two waves splitting the inputs of two row blocks).
 static int ks_plan(int mode, moe_dtype w, int T) {
     if (w == MOE_BF16) {
         if (mode == kGateUp) return T <= 16 ? 0 : 1;
         return T <= 4 ? 0 : 1;
     }
     if (w == MOE_INT4_G128) {
-        if (mode == kGateUp) return T >= 2 ? 0 : -1;
+        if (mode == kGateUp) return T >= 8 ? 1 : T >= 2 ? 0 : -1;
         return T <= kXlTok ? 1 : 0;
     }
     return -1;
@@ -372,10 +374,20 @@ moe_status ffn_gemv_ks(const FfnArgs& a, int mode, moe_dtype w, hipStream_t st) 
         if (plan == 0) return launch_ks<kDown, MOE_BF16, 1, 1, 6, 1>(a, st, "ffn_gemv_down_bf16");
         return launch_ks<kDown, MOE_BF16, 2, 2, 4, 1>(a, st, "ffn_gemv_down_bf16");
     }
-    if (mode == kGateUp) return launch_ks<kGateUp, MOE_INT4_G128, 2, 1, 4, 2>(a, st, "ffn_gemv_gateup_int4");
+    // a plan whose row blocks do not divide the matrix returns EDTYPE before launching: the next
+    if (mode == kGateUp) {
+        if (plan == 1) {
+            const moe_status r = launch_ks<kGateUp, MOE_INT4_G128, 4, 1, 3, 1>(a, st, "ffn_gemv_gateup_int4");
+            if (r != MOE_EDTYPE) return r;
+        }
+        return launch_ks<kGateUp, MOE_INT4_G128, 2, 1, 4, 2>(a, st, "ffn_gemv_gateup_int4");
+    }
     if (plan == 1) {
         const moe_status r = launch_ks<kDown, MOE_INT4_G128, 1, 1, 8, 1, true>(a, st, "ffn_gemv_down_int4");
         if (r != MOE_EDTYPE) return r;  // rows too long to stage: the plan below
+    } else {
+        const moe_status r = launch_ks<kDown, MOE_INT4_G128, 4, 1, 2, 1>(a, st, "ffn_gemv_down_int4");
+        if (r != MOE_EDTYPE) return r;
     }
     return launch_ks<kDown, MOE_INT4_G128, 2, 1, 3, 2>(a, st, "ffn_gemv_down_int4");
 }
