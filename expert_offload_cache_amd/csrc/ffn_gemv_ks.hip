@@ -343,18 +343,21 @@ static moe_status launch_ks(const FfnArgs& a, hipStream_t st, const char* name) 
 //     pairs a wave over 32-token items above (58.8 against 60.4 us at 64 tokens for one pair;
 //     faster than the split-input kernel at 64 tokens although the experts holding more than 32
 //     tokens read their weights twice);
-//   bf16 down: one row block a wave with 5 stages in flight for up to 4 tokens, else two row
+//   bf16 down: one row block a wave with 5 stages in flight for up to 4 tokens, four row blocks
+//     a wave with one stage ahead up to 16 tokens (19.7 against 21.0 us at 16), else two row
 //     blocks a wave over 32-token items;
 //   int4 gate/up: two waves split the inputs of a gate/up pair from 2 tokens on, and from 8 tokens
 //     one wave takes two pairs over all inputs with two stages in flight (65.6 against 67.9 us
 //     at 8 tokens); a single token stays on the vector-ALU kernel (equal time);
-//   int4 down: up to 4 tokens, one row block a wave with 7 stages in flight and the item's h rows
-//     staged in LDS; above that four row blocks a wave with one stage in flight ahead (33.8
-//     against 41.7 us at 8 tokens for two waves splitting the inputs of two row blocks).
+//   int4 down: up to 4 tokens, four waves split the inputs of four row blocks a wave,
+//     interleaved (14.7 against 15.0 us at one token), else one row block a wave with 7 stages in
+//     flight and the item's h rows staged in LDS; above 4 tokens four row blocks a wave with one
+//     stage in flight ahead (33.8 against 41.7 us at 8 tokens for two waves splitting the inputs
+//     of two row blocks).
 static int ks_plan(int mode, moe_dtype w, int T) {
     if (w == MOE_BF16) {
         if (mode == kGateUp) return T <= 16 ? 0 : 1;
-        return T <= 4 ? 0 : 1;
+        return T <= 4 ? 0 : T <= 16 ? 2 : 1;
     }
     if (w == MOE_INT4_G128) {
         if (mode == kGateUp) return T >= 8 ? 1 : T >= 2 ? 0 : -1;
@@ -372,6 +375,10 @@ moe_status ffn_gemv_ks(const FfnArgs& a, int mode, moe_dtype w, hipStream_t st) 
     }
     if (w == MOE_BF16) {
         if (plan == 0) return launch_ks<kDown, MOE_BF16, 1, 1, 6, 1>(a, st, "ffn_gemv_down_bf16");
+        if (plan == 2) {
+            const moe_status r = launch_ks<kDown, MOE_BF16, 4, 2, 2, 1>(a, st, "ffn_gemv_down_bf16");
+            if (r != MOE_EDTYPE) return r;
+        }
         return launch_ks<kDown, MOE_BF16, 2, 2, 4, 1>(a, st, "ffn_gemv_down_bf16");
     }
     // a plan whose row blocks do not divide the matrix returns EDTYPE before launching: the next
@@ -383,7 +390,9 @@ moe_status ffn_gemv_ks(const FfnArgs& a, int mode, moe_dtype w, hipStream_t st) 
         return launch_ks<kGateUp, MOE_INT4_G128, 2, 1, 4, 2>(a, st, "ffn_gemv_gateup_int4");
     }
     if (plan == 1) {
-        const moe_status r = launch_ks<kDown, MOE_INT4_G128, 1, 1, 8, 1, true>(a, st, "ffn_gemv_down_int4");
+        moe_status r = launch_ks<kDown, MOE_INT4_G128, 4, 1, 2, 4, false, true>(a, st, "ffn_gemv_down_int4");
+        if (r != MOE_EDTYPE) return r;
+        r = launch_ks<kDown, MOE_INT4_G128, 1, 1, 8, 1, true>(a, st, "ffn_gemv_down_int4");
         if (r != MOE_EDTYPE) return r;  // rows too long to stage: the plan below
     } else {
         const moe_status r = launch_ks<kDown, MOE_INT4_G128, 4, 1, 2, 1>(a, st, "ffn_gemv_down_int4");
