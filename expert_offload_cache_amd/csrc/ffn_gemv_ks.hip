@@ -346,9 +346,10 @@ static moe_status launch_ks(const FfnArgs& a, hipStream_t st, const char* name) 
 //   bf16 down: one row block a wave with 5 stages in flight for up to 4 tokens, four row blocks
 //     a wave with one stage ahead up to 16 tokens (19.7 against 21.0 us at 16), else two row
 //     blocks a wave over 32-token items;
-//   int4 gate/up: two waves split the inputs of a gate/up pair from 2 tokens on, and from 8 tokens
-//     one wave takes two pairs over all inputs with two stages in flight (65.6 against 67.9 us
-//     at 8 tokens); a single token stays on the vector-ALU kernel (equal time);
+//   int4 gate/up: below 8 tokens four waves split the inputs of two gate/up pairs, interleaved
+//     (21.9 against 22.5 us for the vector-ALU kernel at one token, 29.0 against 31.9 for two
+//     waves splitting one pair at two); from 8 tokens one wave takes two pairs over all inputs
+//     with two stages in flight (65.6 against 67.9 us at 8 tokens);
 //   int4 down: up to 4 tokens, four waves split the inputs of four row blocks a wave,
 //     interleaved (14.7 against 15.0 us at one token), else one row block a wave with 7 stages in
 //     flight and the item's h rows staged in LDS; above 4 tokens four row blocks a wave with one
@@ -360,7 +361,7 @@ static int ks_plan(int mode, moe_dtype w, int T) {
         return T <= 4 ? 0 : T <= 16 ? 2 : 1;
     }
     if (w == MOE_INT4_G128) {
-        if (mode == kGateUp) return T >= 8 ? 1 : T >= 2 ? 0 : -1;
+        if (mode == kGateUp) return T >= 8 ? 1 : 2;
         return T <= kXlTok ? 1 : 0;
     }
     return -1;
@@ -383,10 +384,10 @@ moe_status ffn_gemv_ks(const FfnArgs& a, int mode, moe_dtype w, hipStream_t st) 
     }
     // a plan whose row blocks do not divide the matrix returns EDTYPE before launching: the next
     if (mode == kGateUp) {
-        if (plan == 1) {
-            const moe_status r = launch_ks<kGateUp, MOE_INT4_G128, 4, 1, 3, 1>(a, st, "ffn_gemv_gateup_int4");
-            if (r != MOE_EDTYPE) return r;
-        }
+        moe_status r = plan == 1 ? launch_ks<kGateUp, MOE_INT4_G128, 4, 1, 3, 1>(a, st, "ffn_gemv_gateup_int4")
+                                 : launch_ks<kGateUp, MOE_INT4_G128, 4, 1, 2, 4, false, true>(a, st, "ffn_gemv_gateup_int4");
+        if (r != MOE_EDTYPE) return r;
+        if (a.T < 2) return MOE_EDTYPE;  // one token: the vector-ALU kernel is as fast as the plan below
         return launch_ks<kGateUp, MOE_INT4_G128, 2, 1, 4, 2>(a, st, "ffn_gemv_gateup_int4");
     }
     if (plan == 1) {
