@@ -14,7 +14,7 @@ import numpy as np
 from ._lib import (MOE_BF16, MOE_F32, MOE_INT4_G128, MoeError, check, lib)
 
 __all__ = ["route", "permute", "route_permute", "expert_ffn_grouped", "combine", "slot_bytes", "pack_expert",
-           "workspace_bytes", "SlotCache", "pinned_alloc", "pinned_free", "profile_enable",
+           "workspace_bytes", "hybrid_split", "SlotCache", "pinned_alloc", "pinned_free", "profile_enable",
            "profile_collect", "profile_results", "profile_reset", "MoeError", "WDT", "lib"]
 
 WDT = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4_G128}
@@ -211,7 +211,7 @@ def decode_step_split(cache, layers: np.ndarray, T: int, d: int, f: int, E: int,
 def decode_step_hybrid(cache, layers: np.ndarray, d: int, f: int, E: int, k: int, act: int, wdt: str, slot_pool,
                        n_slots: int, slot_stride: int, slot_table, route_bufs, perm_bufs, y_perm, ws, host_idx,
                        host_x, host_y, host_table, dev_table, cpu_rate: float, pcie_rate: float, copy_too: bool,
-                       compute, copy, cpu_threads: int = 0) -> int:
+                       compute, copy, cpu_threads: int = 0, host_fixed_s: float = 0.0) -> int:
     """One batch-1 decode step of every layer in `layers` with hybrid miss handling
     (moe_decode_step_hybrid).  host_idx/host_x/host_y/host_table: pinned host tensors; dev_table:
     device int32 [E].  -> number of experts run on the host."""
@@ -223,8 +223,17 @@ def decode_step_hybrid(cache, layers: np.ndarray, d: int, f: int, E: int, k: int
                                        _p(logits), _p(c), _p(o), _p(p), _p(ip), _p(y_perm), _p(ws), ws.numel(),
                                        host_idx.data_ptr(), host_x.data_ptr(), host_y.data_ptr(),
                                        host_table.data_ptr(), _p(dev_table), float(cpu_rate), float(pcie_rate),
-                                       int(bool(copy_too)), cpu_threads, ctypes.byref(n_cpu), _s(compute), _s(copy)))
+                                       float(host_fixed_s), int(bool(copy_too)), cpu_threads, ctypes.byref(n_cpu),
+                                       _s(compute), _s(copy)))
     return n_cpu.value
+
+
+def hybrid_split(m: int, cpu_rate: float, pcie_rate: float, host_fixed_s: float = 0.0) -> int:
+    """Misses of a layer the host runs (moe_hybrid_split): of m misses, the n minimising
+    max((m - n) / pcie_rate, host_fixed_s + n / cpu_rate) (m / pcie_rate for n = 0), ties to fewer."""
+    n = ctypes.c_int32()
+    check(lib().moe_hybrid_split(int(m), float(cpu_rate), float(pcie_rate), float(host_fixed_s), ctypes.byref(n)))
+    return n.value
 
 # ---------------------------------------------------------------------------------------------
 # expert-slot cache

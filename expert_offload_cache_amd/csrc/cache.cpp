@@ -178,10 +178,24 @@ static void drop_entry(moe_cache* c, const PendingCopy& p) {
     if (x.key == p.key) {
         c->unlink(p.slot);
         x.key = -1;
+        if (x.pinned) {
+            // the freed slot no longer belongs to the requesting layer: a later mark_read of that
+            // layer must not unpin it (or stamp its read sequence) once another layer owns it
+            std::vector<int32_t>& pl = c->pinned_by_layer[p.key / c->E];
+            pl.erase(std::remove(pl.begin(), pl.end(), p.slot), pl.end());
+        }
         x.pinned = false;
         c->free_slots.push(p.slot);
     }
     c->table_dirty = true;
+}
+
+// Make `compute` wait for copies it has not waited for yet (fill_split's deferred copies).
+static moe_status wait_background(moe_cache* c, hipStream_t compute) {
+    if (c->policy_only || !c->bg_pending) return MOE_OK;
+    MOE_HIP(hipStreamWaitEvent(compute, c->bg_ev, 0));
+    c->bg_pending = false;
+    return MOE_OK;
 }
 
 static hipEvent_t read_event_for(moe_cache* c, int64_t seq) {
@@ -406,7 +420,7 @@ moe_status moe_cache_resize(moe_cache* c, int n_slots, moe_stream copy, moe_stre
             c->free_slots.push(s);
         }
         c->C = n_slots;
-        return MOE_OK;
+        return wait_background(c, (hipStream_t)compute);
     }
     // shrink: keep the n_slots most recently used entries
     c->shrink_seq = c->read_seq;
@@ -460,7 +474,11 @@ moe_status moe_cache_resize(moe_cache* c, int n_slots, moe_stream copy, moe_stre
     for (int s = 0; s < n_slots; ++s)
         if (c->slots[s].key < 0) fresh.push(s);
     c->free_slots.swap(fresh);
-    if (c->policy_only || !c->table_dirty) return MOE_OK;
+    if (c->policy_only || !c->table_dirty) return wait_background(c, (hipStream_t)compute);
+    // Evicted entries leave the table as -1.  Kernels enqueued before this call may still read the
+    // table row of their layer (mark_read is asynchronous), so the upload waits for every read
+    // recorded so far, not only for the reads of the move targets.
+    if (hipEvent_t w = read_event_for(c, c->read_seq)) MOE_HIP(hipStreamWaitEvent(cs, w, 0));
     int i = c->stage_next;
     c->stage_next = (i + 1) % kStage;
     if (c->stage_used[i]) MOE_HIP(hipEventSynchronize(c->stage_ev[i]));
@@ -471,6 +489,7 @@ moe_status moe_cache_resize(moe_cache* c, int n_slots, moe_stream copy, moe_stre
     c->table_dirty = false;
     MOE_HIP(hipEventRecord(c->fill_ev, cs));
     MOE_HIP(hipStreamWaitEvent((hipStream_t)compute, c->fill_ev, 0));
+    c->bg_pending = false;  // the deferred copies ran on cs before fill_ev
     return MOE_OK;
 }
 
@@ -513,6 +532,10 @@ moe_status moe_cache_slot_of(const moe_cache* c, int layer, int expert, int32_t*
 }  // extern "C"
 
 namespace moe {
+// Library-internal: make `compute` wait for deferred (fill_split) copies before a launch that may
+// read their slots ahead of the next fill.
+moe_status cache_wait_background(moe_cache* c, hipStream_t compute) { return wait_background(c, compute); }
+
 // Pinned host image of (layer, expert), or nullptr (policy-only cache).  Library-internal.
 const void* cache_host_image(const moe_cache* c, int layer, int expert) {
     if (!c || !c->host || layer < 0 || layer >= c->L || expert < 0 || expert >= c->E) return nullptr;

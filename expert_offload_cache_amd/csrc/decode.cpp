@@ -76,18 +76,23 @@ extern "C" moe_status moe_decode_step(moe_cache* cache, int n_layers, const moe_
 
 namespace moe {
 const void* cache_host_image(const moe_cache* c, int layer, int expert);  // cache.cpp
+moe_status cache_wait_background(moe_cache* c, hipStream_t compute);     // cache.cpp
 }
 
 namespace {
-// Misses of one layer to run on the host: the n minimising max((m - n) / pcie_rate, n / cpu_rate),
-// ties to fewer on the host (FreeToken RTX 5090 page, miss split; stork.ai article, miss policy).
-int hybrid_split(int m, double cpu_rate, double pcie_rate) {
+// Misses of one layer to run on the host (FreeToken RTX 5090 page, miss split: the split follows the
+// measured host and PCIe bandwidths; stork.ai article, miss policy).  With n of the m misses on the
+// host the layer's miss work takes t(0) = m / pcie_rate, or t(n) = max((m - n) / pcie_rate,
+// host_fixed_s + n / cpu_rate) for n >= 1, where host_fixed_s is the host path's cost that does not
+// grow with n (activation row to the host, thread wake-up, output rows back).  The smallest t wins;
+// ties go to fewer on the host.
+int hybrid_split(int m, double cpu_rate, double pcie_rate, double host_fixed_s) {
     if (cpu_rate <= 0.0 || m <= 0) return 0;
     int best = 0;
     double best_t = m / pcie_rate;
     for (int n = 1; n <= m; ++n) {
-        const double t = std::max((m - n) / pcie_rate, n / cpu_rate);
-        if (t < best_t - 1e-15) {
+        const double t = std::max((m - n) / pcie_rate, host_fixed_s + n / cpu_rate);
+        if (t < best_t) {
             best = n;
             best_t = t;
         }
@@ -96,17 +101,28 @@ int hybrid_split(int m, double cpu_rate, double pcie_rate) {
 }
 }  // namespace
 
+extern "C" moe_status moe_hybrid_split(int m, double cpu_rate, double pcie_rate, double host_fixed_s,
+                                       int32_t* n_host) {
+    MOE_CHECK(n_host, MOE_EINVAL, "moe_hybrid_split: n_host is NULL");
+    MOE_CHECK(m >= 0 && pcie_rate > 0.0 && cpu_rate >= 0.0 && host_fixed_s >= 0.0, MOE_EINVAL,
+              "moe_hybrid_split: need m >= 0, pcie_rate > 0, cpu_rate >= 0, host_fixed_s >= 0");
+    *n_host = hybrid_split(m, cpu_rate, pcie_rate, host_fixed_s);
+    return MOE_OK;
+}
+
 extern "C" moe_status moe_decode_step_hybrid(
     moe_cache* cache, int n_layers, const moe_decode_layer* layers, int d, int f, int E, int k, moe_dtype act,
     moe_dtype w, const void* slot_pool, int n_slots, size_t slot_stride, const int32_t* slot_table, int32_t* topk_idx,
     float* topk_w, float* logits, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, float* y_perm,
     void* ws, size_t ws_bytes, int32_t* host_idx, void* host_x, float* host_y, int32_t* host_table,
-    int32_t* dev_table, double cpu_rate, double pcie_rate, int copy_too, int cpu_threads, int64_t* n_cpu_out,
-    moe_stream compute, moe_stream copy) {
+    int32_t* dev_table, double cpu_rate, double pcie_rate, double host_fixed_s, int copy_too, int cpu_threads,
+    int64_t* n_cpu_out, moe_stream compute, moe_stream copy) {
     MOE_CHECK(cache && layers && slot_table && host_idx && host_x && host_y && host_table && dev_table, MOE_EINVAL,
               "moe_decode_step_hybrid: NULL pointer");
     MOE_CHECK(n_layers >= 0 && k >= 1 && k <= E && act == MOE_BF16, MOE_ESHAPE,
               "moe_decode_step_hybrid: need n_layers >= 0, 1 <= k <= E and bf16 activations");
+    MOE_CHECK(pcie_rate > 0.0 && cpu_rate >= 0.0 && host_fixed_s >= 0.0, MOE_EINVAL,
+              "moe_decode_step_hybrid: need pcie_rate > 0, cpu_rate >= 0, host_fixed_s >= 0");
     hipStream_t cs = (hipStream_t)compute;
     const int T = 1;  // one token: a pair's row of y_perm is the rank of its expert id
     for (int i = 0; i < n_layers; ++i)  // every layer is checked before anything is enqueued
@@ -136,7 +152,7 @@ extern "C" moe_status moe_decode_step_hybrid(
             if (r != MOE_OK) return r;
             if (sl < 0) miss.push_back(ids[j]);
         }
-        const int n_cpu = hybrid_split((int)miss.size(), cpu_rate, pcie_rate);
+        const int n_cpu = hybrid_split((int)miss.size(), cpu_rate, pcie_rate, host_fixed_s);
         if (n_cpu == 0) {
             // nothing for the host in this layer: the plain step (the cache's own slot-table row,
             // no table or activation copies), with the same cache decisions and outputs
@@ -258,8 +274,11 @@ extern "C" moe_status moe_decode_step_split(moe_cache* cache, int n_layers, cons
             }
             MOE_HIP(hipMemcpyAsync(dev_tables, host_tables, sizeof(int32_t) * 2 * (size_t)E, hipMemcpyHostToDevice,
                                    cs));
-            // the resident experts run while the misses are copied in
-            r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, dev_tables, n_slots,
+            // the resident experts run while the misses are copied in; copies deferred by an earlier
+            // split fill (hybrid handling) may have filled some of them, so those are waited for
+            r = cache_wait_background(cache, cs);
+            if (r == MOE_OK)
+                r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, dev_tables, n_slots,
                                        slot_pool, slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, compute);
             if (r == MOE_OK) r = moe_cache_fill(cache, copy, compute);
             if (r == MOE_OK)

@@ -25,6 +25,16 @@ struct FfnArgs {
 constexpr size_t kWsHeader = 256;
 constexpr size_t kPlanBytes = 1 << 16;
 
+// Argument checks of moe_expert_ffn_grouped except the workspace; fills every field of `a` but
+// status, plan and h (left NULL).  T == 0 returns MOE_OK with nothing to run.  `fn` names the
+// caller in error messages.
+moe_status ffn_prepare(FfnArgs& a, const char* fn, const void* x, moe_dtype act, int T, int d, int f, int E, int k,
+                       const int32_t* perm, const int32_t* offsets, const int32_t* counts,
+                       const int32_t* slot_of_expert, int n_slots, const void* slot_pool, size_t slot_stride,
+                       moe_dtype w, const void* shared_w, float* y_perm);
+// Launch the grouped experts: the prefill MFMA GEMM where it applies, else the decode GEMVs.
+moe_status ffn_run(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st);
+
 // decode path: grouped GEMV kernels (ffn_gemv.hip)
 moe_status ffn_gemv(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st);
 // The decode kernels below launch one projection (mode kGateUp = 0 or kDown = 1) and return

@@ -19,24 +19,18 @@ from typing import Optional
 
 import numpy as np
 
-from . import (MoeError, SlotCache, combine, expert_ffn_grouped, pack_expert, pinned_alloc, pinned_free,
-               route_permute, slot_bytes, workspace_bytes, WDT)
+from . import (MoeError, SlotCache, combine, expert_ffn_grouped, hybrid_split, pack_expert, pinned_alloc,
+               pinned_free, route_permute, slot_bytes, workspace_bytes, WDT)
 from ._lib import MOE_BF16, MOE_F32
 from .layer import _expert_arrays, _to_device
 
 
-def hybrid_split(n_miss: int, cpu_rate: float, pcie_rate: float) -> int:
-    """Misses of one layer to run on the host: the n that minimises max((n_miss - n) / pcie_rate,
-    n / cpu_rate), both rates in expert images per second (ties: fewer on the host).  The host
-    takes the highest-numbered misses; they are not inserted into the cache."""
-    if cpu_rate <= 0 or n_miss <= 0:
-        return 0
-    best, best_t = 0, n_miss / pcie_rate
-    for n in range(1, n_miss + 1):
-        t = max((n_miss - n) / pcie_rate, n / cpu_rate)
-        if t < best_t - 1e-15:
-            best, best_t = n, t
-    return best
+def _hybrid_args(hybrid):
+    """hybrid = (cpu_rate, pcie_rate[, copy_too[, host_fixed_s]]) -> the four values."""
+    cpu, pcie = float(hybrid[0]), float(hybrid[1])
+    copy_too = bool(hybrid[2]) if len(hybrid) > 2 else True
+    fixed = float(hybrid[3]) if len(hybrid) > 3 else 0.0
+    return cpu, pcie, copy_too, fixed
 
 
 class OffloadStack:
@@ -252,10 +246,10 @@ class OffloadStack:
         `split_launch`: a layer with misses runs its hit experts before waiting for the copies (the
         misses marked as produced elsewhere), then the missed experts after them, then the combine.
 
-        `hybrid` = (cpu_rate, pcie_rate[, copy_too]) turns on hybrid miss handling: each layer's
-        misses are split by hybrid_split; the host runs its share (moe_cpu_expert_ffn on the pinned
-        images) while the rest is copied and run on the GPU, and the host's rows are copied into
-        y_perm before the combine.  With copy_too (default) the host's misses are also inserted
+        `hybrid` = (cpu_rate, pcie_rate[, copy_too[, host_fixed_s]]) turns on hybrid miss handling:
+        each layer's misses are split by the library's rule (moe_hybrid_split); the host runs its
+        share (moe_cpu_expert_ffn on the pinned images) while the rest is copied and run on the GPU,
+        and the host's rows are copied into y_perm before the combine.  With copy_too (default) the host's misses are also inserted
         and copied after the others, off this layer's critical path (the cache then sees every
         request in full); without it they stay out of the cache.  The number of host-run experts
         is added to self.cpu_experts.
@@ -324,9 +318,9 @@ class OffloadStack:
                         self.cache.fill(self.copy, self.compute)
                         y = self._experts(l, x, w, perm)
                     else:
-                        copy_too = hybrid[2] if len(hybrid) > 2 else True
+                        cpu_rate, pcie_rate, copy_too, fixed_s = _hybrid_args(hybrid)
                         miss = [int(e) for e in ids if self.cache.slot_of(l, int(e)) < 0]
-                        n_cpu = hybrid_split(len(miss), hybrid[0], hybrid[1])
+                        n_cpu = hybrid_split(len(miss), cpu_rate, pcie_rate, fixed_s)
                         on_cpu = miss[len(miss) - n_cpu:] if n_cpu else []
                         gpu_ids = [int(e) for e in ids if copy_too or int(e) not in on_cpu]
                         slots, _ = self.cache.lookup(l, gpu_ids)
@@ -389,7 +383,7 @@ class OffloadStack:
             host_y = torch.empty((k, d), dtype=torch.float32, pin_memory=True)
             host_tab = torch.full((E,), -1, dtype=torch.int32, pin_memory=True)
             dev_tab = torch.empty(E, dtype=torch.int32, device=self.device)
-            copy_too = hybrid[2] if len(hybrid) > 2 else True
+            cpu_rate, pcie_rate, copy_too, fixed_s = _hybrid_args(hybrid)
         if split_launch:
             host_tabs = torch.full((2, E), -1, dtype=torch.int32, pin_memory=True)
             dev_tabs = torch.empty((2, E), dtype=torch.int32, device=self.device)
@@ -401,7 +395,8 @@ class OffloadStack:
                     self.cpu_experts += decode_step_hybrid(
                         self.cache, arr[s], d, self.f, E, k, self.act_code, self.wl.wdt, self.slot_pool, self.n_slots,
                         self.stride, self.slot_table, b["route"], b["perm"], b["y_perm"], ws, self._host_idx, host_x,
-                        host_y, host_tab, dev_tab, hybrid[0], hybrid[1], copy_too, self.compute, self.copy)
+                        host_y, host_tab, dev_tab, cpu_rate, pcie_rate, copy_too, self.compute, self.copy,
+                        host_fixed_s=fixed_s)
                 elif split_launch:
                     decode_step_split(self.cache, arr[s], 1, d, self.f, E, k, self.act_code, self.wl.wdt,
                                       self.slot_pool, self.n_slots, self.stride, self.slot_table, b["route"], b["perm"],
@@ -473,6 +468,84 @@ def host_expert_rate(stack, reps: int = 5) -> float:
     return reps / (time.perf_counter() - t0)
 
 
+def hybrid_rates(wl, seed: int = 0, n: int = 8, reps: int = 20, device="cuda") -> dict:
+    """The inputs of the hybrid split, measured on this machine (FreeToken RTX 5090 page, miss split:
+    host and PCIe bandwidths are to be measured on the actual computer).
+
+    Both paths read host memory, so each rate is measured while the other path is busy: `n` slot
+    images copied pinned -> device on one stream while the host kernel runs `n` other pinned slot
+    images.  The fixed host-path cost is the round trip a layer pays once the host takes any expert:
+    the activation row to the host and one output row back, each waited for (averaged over `reps`).
+    Runs before the stack's pool is pinned, on buffers of its own (freed on return).
+    -> dict(cpu_rate, pcie_rate (expert images per second, under contention), host_fixed_s, and the
+    two rates measured alone)."""
+    import torch
+    import synth
+    from . import cpu_expert_ffn
+
+    d, f = wl.d, wl.f
+    stride = slot_bytes(d, f, wl.wdt)
+    img = pack_expert(wl.wdt, d, f, *_expert_arrays(synth.expert_weights(wl, seed, 0, 0)))
+    src = torch.empty((n, stride), dtype=torch.uint8, pin_memory=True)       # what the copies read
+    host = torch.empty((n, stride), dtype=torch.uint8, pin_memory=True)      # what the host kernel reads
+    src.numpy()[:] = img
+    host.numpy()[:] = img
+    dst = torch.empty((n, stride), dtype=torch.uint8, device=device)
+    st = torch.cuda.Stream(device=device)
+    x = np.zeros((1, d), dtype=np.uint16)
+    x[0, ::7] = 0x3F80
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hbase = host.data_ptr()
+
+    def copies():
+        with torch.cuda.stream(st):
+            e0.record(st)
+            for i in range(n):
+                dst[i].copy_(src[i], non_blocking=True)
+            e1.record(st)
+
+    def run_host():
+        t0 = time.perf_counter()
+        for i in range(n):
+            cpu_expert_ffn(hbase + i * stride, wl.wdt, d, f, x)
+        return time.perf_counter() - t0
+
+    run_host()  # warm the host threads and pages
+    copies()
+    e1.synchronize()
+    copies()
+    e1.synchronize()
+    pcie_alone = n / (e0.elapsed_time(e1) * 1e-3)
+    cpu_alone = n / run_host()
+    copies()
+    t_host = run_host()
+    e1.synchronize()
+    pcie_busy = n / (e0.elapsed_time(e1) * 1e-3)
+    cpu_busy = n / t_host
+    # fixed cost of the host path: activation row down, an output row up, each waited for
+    hx = torch.empty((1, d), dtype=torch.int16, pin_memory=True)
+    hy = torch.zeros((1, d), dtype=torch.float32, pin_memory=True)
+    xd = torch.zeros((1, d), dtype=torch.int16, device=device)
+    yd = torch.empty((1, d), dtype=torch.float32, device=device)
+    ev = torch.cuda.Event()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(st):
+        for _ in range(reps):
+            hx.copy_(xd, non_blocking=True)
+            ev.record(st)
+            ev.synchronize()
+            yd.copy_(hy, non_blocking=True)
+            ev.record(st)
+            ev.synchronize()
+    fixed = (time.perf_counter() - t0) / reps
+    torch.cuda.synchronize()
+    del src, host, dst, hx, hy, xd, yd
+    torch.cuda.empty_cache()
+    return dict(cpu_rate=cpu_busy, pcie_rate=pcie_busy, host_fixed_s=fixed, cpu_rate_alone=cpu_alone,
+                pcie_rate_alone=pcie_alone)
+
+
 def run_trace(wl, layers: int, capacity_fracs=(0.40, 0.58), steps: int = 2048, prefill_tokens: int = 2048,
               seed: int = 0, n_images: Optional[int] = None, log=None, min_layers: Optional[int] = 12):
     """The offload workload: a prefill of `prefill_tokens`, then a `steps`-step batch-1 decode over a
@@ -485,17 +558,25 @@ def run_trace(wl, layers: int, capacity_fracs=(0.40, 0.58), steps: int = 2048, p
 
     log = log or (lambda *a: None)
     pcie = pinned_h2d_GBps()  # before the pool is pinned
+    hr = hybrid_rates(wl, seed)
     n_caps = [int(round(fr * layers * wl.E)) for fr in capacity_fracs]
     stack = OffloadStack(wl, layers, max(n_caps), seed=seed, n_images=n_images, prefill_tokens=prefill_tokens,
                          log=log, min_layers=min_layers)
     requested, layers = layers, stack.L
     trace = synth.routing_trace(seed, steps, layers, wl.E, wl.k)
     caps = [int(round(fr * layers * wl.E)) for fr in capacity_fracs]
-    cpu = host_expert_rate(stack)
     out = {"layers": layers, "layers_requested": requested, "experts_per_layer": wl.E, "slot_bytes": stack.stride,
            "pool_GiB": stack.pool_bytes / 2**30, "steps": steps, "prefill_tokens": prefill_tokens,
-           "pcie_h2d_GBps": pcie, "host_expert_GBps": cpu * stack.stride / 1e9, "runs": []}
-    rates = (cpu, pcie * 1e9 / stack.stride)  # expert images per second: host, PCIe
+           "pcie_h2d_GBps": pcie, "host_expert_GBps": hr["cpu_rate_alone"] * stack.stride / 1e9,
+           "hybrid_split_inputs": {"host_GBps_while_copying": hr["cpu_rate"] * stack.stride / 1e9,
+                                   "pcie_GBps_while_host_runs": hr["pcie_rate"] * stack.stride / 1e9,
+                                   "host_GBps_alone": hr["cpu_rate_alone"] * stack.stride / 1e9,
+                                   "pcie_GBps_alone": hr["pcie_rate_alone"] * stack.stride / 1e9,
+                                   "host_fixed_us": hr["host_fixed_s"] * 1e6},
+           "runs": []}
+    # the host's share stays out of the cache (the pages' direct CPU execution); the variant that
+    # also copies it in (deferred) is measured beside it
+    rates = (hr["cpu_rate"], hr["pcie_rate"], False, hr["host_fixed_s"])
     try:
         for fr, C in zip(capacity_fracs, caps):
             stack.new_cache(C)
@@ -525,6 +606,12 @@ def run_trace(wl, layers: int, capacity_fracs=(0.40, 0.58), steps: int = 2048, p
             r["hybrid_decode_tokens_per_s"] = steps / t_hyb
             r["hybrid_gpu_miss_rate"] = sth["dec_miss"] / max(1, sth["dec_acc"] + stack.cpu_experts)
             r["hybrid_host_experts_per_token"] = stack.cpu_experts / steps
+            # the same split with the host's misses also copied in after the layer's own copies
+            stack.new_cache(C)
+            stack.prefill()
+            stack.cpu_experts = 0
+            r["hybrid_copy_too_decode_tokens_per_s"] = steps / stack.decode(trace, hybrid=rates[:2] + (True,) + rates[3:])
+            r["hybrid_copy_too_host_experts_per_token"] = stack.cpu_experts / steps
             # the same trace with split launches: resident experts overlap the miss copies
             stack.new_cache(C)
             stack.prefill()

@@ -299,11 +299,20 @@ MOE_API moe_status moe_decode_step_split(moe_cache* cache, int n_layers, const m
                                          size_t ws_bytes, int32_t* host_idx, int32_t* host_tables,
                                          int32_t* dev_tables, moe_stream compute, moe_stream copy);
 
+/* The hybrid miss split (FreeToken RTX 5090 page, miss split: a miss is copied over PCIe, run on the
+ * CPU where its weights live, or both, split by the host and PCIe bandwidths measured on the
+ * machine; stork.ai article, miss policy).  Of a layer's m misses the host takes *n_host, the n
+ * minimising t(n): t(0) = m / pcie_rate; t(n) = max((m - n) / pcie_rate, host_fixed_s + n / cpu_rate)
+ * for n >= 1, ties to the smaller n.  Rates are expert images per second (cpu_rate 0 = no host
+ * path); host_fixed_s is the per-layer host-path cost that does not grow with n (activation row to
+ * the host, thread wake-up, output rows back), in seconds.  Host only.  MOE_EINVAL for m < 0,
+ * pcie_rate <= 0, cpu_rate < 0, host_fixed_s < 0 or n_host NULL. */
+MOE_API moe_status moe_hybrid_split(int m, double cpu_rate, double pcie_rate, double host_fixed_s, int32_t* n_host);
+
 /* moe_decode_step with hybrid miss handling (FreeToken RTX 5090 page, miss split; stork.ai
  * article, miss policy), one token per step (T = 1, bf16 activations).  Per layer, after the ids
- * reach the host (host_idx: k int32, pinned): the layer's m misses are
- * split, the host taking the n highest-numbered ones, n minimising max((m-n)/pcie_rate, n/cpu_rate)
- * (rates in expert images per second; ties to fewer on the host).  A layer with n = 0 runs as in
+ * reach the host (host_idx: k int32, pinned): the layer's m misses are split by moe_hybrid_split
+ * (cpu_rate, pcie_rate, host_fixed_s), the host taking the n highest-numbered ones.  A layer with n = 0 runs as in
  * moe_decode_step (the slot-table row as is).  Otherwise x is copied to host_x (d bf16, pinned)
  * while the cache decides, and the other ids (all of them
  * with copy_too, whose host experts are then also inserted, their copies deferred through
@@ -320,8 +329,8 @@ MOE_API moe_status moe_decode_step_hybrid(moe_cache* cache, int n_layers, const 
                                           int32_t* offsets, int32_t* perm, int32_t* inv_perm, float* y_perm,
                                           void* ws, size_t ws_bytes, int32_t* host_idx, void* host_x, float* host_y,
                                           int32_t* host_table, int32_t* dev_table, double cpu_rate,
-                                          double pcie_rate, int copy_too, int cpu_threads, int64_t* n_cpu_out,
-                                          moe_stream compute, moe_stream copy);
+                                          double pcie_rate, double host_fixed_s, int copy_too, int cpu_threads,
+                                          int64_t* n_cpu_out, moe_stream compute, moe_stream copy);
 
 /* Host execution of one routed expert, the CPU side of hybrid miss handling (FreeToken RTX 5090
  * page, miss split: a miss runs on the GPU after a PCIe copy or on the CPU, split by the measured

@@ -109,13 +109,21 @@ def test_host_validation_needs_no_gpu(moe):
         assert step(c.h, 0, layers.ctypes.data, 2, vp) == 0  # zero layers: nothing to do
 
         # the hybrid step: (after slot_table) 9 buffers, ws_bytes, host_idx, host_x, host_y,
-        # host_table, dev_table, cpu_rate, pcie_rate, copy_too, threads, n_cpu_out, compute, copy
-        def hstep(n, k, act, host):
+        # host_table, dev_table, cpu_rate, pcie_rate, host_fixed_s, copy_too, threads, n_cpu_out,
+        # compute, copy
+        def hstep(n, k, act, host, pcie=1.0, fixed=0.0):
             return L.moe_decode_step_hybrid(c.h, n, layers.ctypes.data, 256, 128, 8, k, act, 1, vp, 4, 4096, vp,
-                                            *bufs, 0, host, host, host, host, host, 1.0, 1.0, 1, 0, None, None,
-                                            None)
+                                            *bufs, 0, host, host, host, host, host, 1.0, pcie, fixed, 1, 0, None,
+                                            None, None)
 
         assert hstep(1, 2, 1, None) == moe._lib.MOE_EINVAL  # no pinned staging buffers
+        assert hstep(1, 2, 1, vp, pcie=0.0) == moe._lib.MOE_EINVAL  # no PCIe rate
+        assert hstep(1, 2, 1, vp, fixed=-1.0) == moe._lib.MOE_EINVAL  # negative fixed cost
+        n = ctypes.c_int32(-5)
+        assert L.moe_hybrid_split(3, 1.0, 0.0, 0.0, ctypes.byref(n)) == moe._lib.MOE_EINVAL
+        assert L.moe_hybrid_split(-1, 1.0, 1.0, 0.0, ctypes.byref(n)) == moe._lib.MOE_EINVAL
+        assert L.moe_hybrid_split(3, 1.0, 1.0, 0.0, None) == moe._lib.MOE_EINVAL
+        assert L.moe_hybrid_split(3, 1.0, 1.0, 0.0, ctypes.byref(n)) == 0 and n.value == 1
         assert hstep(1, 2, 0, vp) == moe._lib.MOE_ESHAPE  # f32 activations
         assert hstep(1, 9, 1, vp) == moe._lib.MOE_ESHAPE  # k > E
         assert hstep(1, 2, 1, vp) == moe._lib.MOE_EINVAL  # a layer without its input

@@ -193,3 +193,27 @@ def test_fill_split_defers_the_listed_copies(moe):
             assert keys == [e for e in miss if e not in later] + later
             c.policy_mark_read(l)
     assert np.array_equal(c.trace(), np.array(sim.log, dtype=np.uint8))
+
+
+def test_failed_copy_releases_its_pin(moe):
+    """A copy that fails frees its slot; when another layer takes that slot, marking the first layer
+    read must not unpin it (the other layer's kernels may still read it)."""
+    c = moe.SlotCache(3, 4, 2)
+    try:
+        c.lookup(0, [0])                  # (0,0) -> slot 0, pinned by layer 0
+        c.inject_copy_failures(1)
+        with pytest.raises(moe.MoeError):
+            c.policy_fill()               # the copy fails: (0,0) is dropped, slot 0 is free again
+        assert c.slot_of(0, 0) == -1
+        slots, _ = c.lookup(1, [2])       # (1,2) takes slot 0, pinned by layer 1
+        assert list(slots) == [0]
+        c.policy_fill()
+        c.policy_mark_read(0)             # layer 0 no longer holds slot 0
+        with pytest.raises(moe.MoeError) as err:
+            c.lookup(2, [0, 1])           # needs both slots: slot 0 is still pinned by layer 1
+        assert err.value.status == moe._lib.MOE_ESTATE
+        c.policy_mark_read(1)
+        slots, nm = c.lookup(2, [0, 1])
+        assert nm == 2 and sorted(slots) == [0, 1]
+    finally:
+        c.close()

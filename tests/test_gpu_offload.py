@@ -245,10 +245,13 @@ def test_hybrid_miss_split(copy_too):
     and the cache sees every request in full; without it the cache sees only the GPU share (as the
     simulator fed the same split).  Outputs match the oracle."""
     need_gpu()
-    from expert_offload_cache_amd.offload import OffloadStack, hybrid_split
+    from expert_offload_cache_amd.offload import OffloadStack
+    from oracle.hybrid import host_misses, hybrid_split
 
     wl, trace = _wl(), _trace()
-    rates = (1.0, 1.0, copy_too)  # equal host and PCIe rates: the host takes half of each layer's misses
+    # equal host and PCIe rates with a fixed host cost of 0.3 expert-times: a layer with one miss
+    # keeps it on the GPU, two misses put one on the host
+    rates = (1.0, 1.0, copy_too, 0.3)
     stack = OffloadStack(wl, L, 16, seed=0, n_images=IMAGES, prefill_tokens=T_PRE)
     try:
         stack.prefill()
@@ -263,8 +266,7 @@ def test_hybrid_miss_split(copy_too):
             for l in range(L):
                 ids = np.unique(trace[s, l]).tolist()
                 miss = [e for e in ids if (l, e) not in sim.od]
-                n_cpu = hybrid_split(len(miss), rates[0], rates[1])
-                on_cpu = miss[len(miss) - n_cpu:] if n_cpu else []
+                on_cpu = host_misses(miss, hybrid_split(len(miss), rates[0], rates[1], rates[3]))
                 n_cpu_total += len(on_cpu)
                 flags += sim.request(l, [e for e in ids if copy_too or e not in on_cpu])[1]
         assert np.array_equal(stack.cache.trace(), np.array(flags, dtype=np.uint8))
@@ -292,7 +294,7 @@ def test_native_hybrid_matches_the_call_by_call_loop(copy_too):
     from expert_offload_cache_amd.offload import OffloadStack
 
     wl, trace = _wl(), _trace()
-    rates = (1.0, 1.0, copy_too)
+    rates = (1.0, 1.0, copy_too, 0.3)
     got = []
     for native in (True, False):
         stack = OffloadStack(wl, L, 16, seed=0, n_images=IMAGES, prefill_tokens=T_PRE)
@@ -311,9 +313,45 @@ def test_native_hybrid_matches_the_call_by_call_loop(copy_too):
         assert (s0, l0) == (s1, l1) and np.array_equal(y0, y1)
 
 
-def test_hybrid_split_rule():
-    from expert_offload_cache_amd.offload import hybrid_split
+def test_resize_right_after_mark_read_without_a_sync():
+    """A shrink enqueued straight after the last layer's mark_read (no host synchronisation, the
+    layer's kernels possibly still queued) must not let those kernels read evicted table entries:
+    outputs stay bitwise those of a fixed-capacity run and no absent slot is flagged."""
+    need_gpu()
+    import torch
+    from expert_offload_cache_amd.offload import OffloadStack
 
-    assert hybrid_split(0, 1.0, 1.0) == 0 and hybrid_split(1, 1.0, 1.0) == 0 and hybrid_split(2, 1.0, 1.0) == 1
-    assert hybrid_split(3, 1.0, 2.0) == 1 and hybrid_split(6, 1.0, 2.0) == 2 and hybrid_split(4, 0.0, 1.0) == 0
-    assert hybrid_split(5, 10.0, 1.0) == 5
+    wl, trace = _wl(), _trace()
+    stack = OffloadStack(wl, L, 32, seed=0, n_images=IMAGES, prefill_tokens=T_PRE)
+    try:
+        stack.prefill()
+        _, o = stack.decode(trace[:6], keep_outputs=True)
+        outs = [(s, l, y_to_f64(y)) for s, l, y in o]
+        # step 6 by hand, so that the shrink follows the last mark_read with work still queued
+        s = 6
+        forced = stack._forced(trace[s:s + 1])
+        ys = []
+        with torch.cuda.stream(stack.compute):
+            for l in range(L):
+                xl = stack.x_dec[l][s % 8:s % 8 + 1]
+                idx, w, perm = stack._layer(l, xl, forced[0, l:l + 1])
+                # the ids are forced from the trace, so the host needs no read-back before the lookup
+                stack.cache.lookup(l, np.unique(trace[s, l]))
+                stack.cache.fill(stack.copy, stack.compute)
+                ys.append(stack._experts(l, xl, w, perm).clone())
+                stack.cache.mark_read(l, stack.compute)
+            stack.resize(12)  # evicts entries the last layer's kernels may not have read yet
+        torch.cuda.synchronize()
+        outs += [(s, l, y_to_f64(y)) for l, y in enumerate(ys)]
+        status = int(stack._workspace(1)[:4].view(torch.int32).item())
+        _, o = stack.decode(trace[7:], keep_outputs=True, first_step=7)
+        outs += [(st, l, y_to_f64(y)) for st, l, y in o]
+    finally:
+        stack.close()
+    assert status == 0
+    ref = _run(32)[1]
+    ref_dec = {(st, l): y for st, l, y in ref["dec"]}
+    assert len(outs) == STEPS * L
+    for st, l, y in outs:
+        assert np.array_equal(y, ref_dec[(st, l)]), (st, l)
+    ref["stack"].close()
