@@ -13,8 +13,8 @@ import numpy as np
 
 from ._lib import (MOE_BF16, MOE_F32, MOE_INT4_G128, MoeError, check, lib)
 
-__all__ = ["route", "permute", "route_permute", "expert_ffn_grouped", "combine", "slot_bytes", "pack_expert",
-           "workspace_bytes", "hybrid_split", "SlotCache", "pinned_alloc", "pinned_free", "profile_enable",
+__all__ = ["route", "permute", "route_permute", "expert_ffn_grouped", "expert_ffn_grouped_noalloc", "combine",
+           "slot_bytes", "pack_expert", "workspace_bytes", "hybrid_split", "SlotCache", "pinned_alloc", "pinned_free", "profile_enable",
            "profile_collect", "profile_results", "profile_reset", "MoeError", "WDT", "lib"]
 
 WDT = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4_G128}
@@ -125,6 +125,20 @@ def expert_ffn_grouped(x, perm, offsets, counts, slot_of_expert, slot_pool, n_sl
                                        _p(slot_of_expert), n_slots, _p(slot_pool), slot_stride, WDT[wdt],
                                        _p(shared_w), _p(y_perm), _p(ws), ws.numel(), _s(stream)))
     return y_perm, ws
+
+
+def expert_ffn_grouped_noalloc(x, perm, offsets, counts, slot_of_expert, slot_pool, n_slots: int,
+                               slot_stride: int, wdt: str, f: int, k: int, y_perm, shared_w=None, status=None,
+                               stream=None):
+    """expert_ffn_grouped through moe_expert_ffn_grouped_noalloc: no workspace, the library's
+    per-GPU scratch instead; y_perm must be given.  status: device int32 tensor or None."""
+    _contig(x, perm, offsets, counts, slot_of_expert, y_perm)
+    T, d = x.shape
+    E = counts.shape[0]
+    check(lib().moe_expert_ffn_grouped_noalloc(_p(x), _act(x), T, d, f, E, k, _p(perm), _p(offsets), _p(counts),
+                                               _p(slot_of_expert), n_slots, _p(slot_pool), slot_stride, WDT[wdt],
+                                               _p(shared_w), _p(y_perm), _p(status), _s(stream)))
+    return y_perm
 
 
 def combine(y_perm, topk_w, inv_perm, k: int, has_shared: bool, out_dtype, y=None, stream=None):

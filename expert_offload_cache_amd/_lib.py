@@ -26,6 +26,8 @@ SIGNATURES = {
     "moe_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_expert_ffn_grouped": (_st, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _sz,
                                      _i32, _vp, _vp, _vp, _sz, _vp]),
+    "moe_expert_ffn_grouped_noalloc": (_st, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32,
+                                             _vp, _sz, _i32, _vp, _vp, _vp, _vp]),
     "moe_combine": (_st, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
     "moe_decode_step": (_st, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _sz, _vp, _vp, _vp,
                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),

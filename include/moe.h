@@ -167,6 +167,24 @@ MOE_API moe_status moe_expert_ffn_grouped(const void* x, moe_dtype act, int T, i
                                           moe_dtype w, const void* shared_w, float* y_perm,
                                           void* ws, size_t ws_bytes, moe_stream s);
 
+/* moe_expert_ffn_grouped for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels, with the
+ * workspace replaced by a scratch array the library holds per GPU (MOE_NOALLOC_SCRATCH_BYTES, on
+ * each GPU it runs on, until the process ends).  The call allocates nothing.
+ *   status: device int32, the sticky status word of the workspace (the caller zero-fills it before
+ *   its first use), or NULL: an absent slot then still gives zero rows but is not reported.
+ *   A call whose moe_workspace_bytes(...) exceeds MOE_NOALLOC_SCRATCH_BYTES returns MOE_ENOMEM with
+ *   nothing enqueued.  Every call on one GPU uses that GPU's one array: calls that may run at the
+ *   same time on one GPU (streams not ordered with each other) race and give undefined outputs.
+ * Other arguments, outputs and errors as moe_expert_ffn_grouped. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+MOE_API moe_status moe_expert_ffn_grouped_noalloc(const void* x, moe_dtype act, int T, int d, int f, int E,
+                                                  int k, const int32_t* perm, const int32_t* offsets,
+                                                  const int32_t* counts, const int32_t* slot_of_expert,
+                                                  int n_slots, const void* slot_pool, size_t slot_stride,
+                                                  moe_dtype w, const void* shared_w, float* y_perm,
+                                                  int32_t* status, moe_stream s);
+
 /* ------------------------------------------------------------------------------------------
  * moe_combine -- gate-weighted sum (pages silent on the form; plain reading):
  *   y[t,:] = sum_{j=0..k-1} topk_w[t,j] * y_perm[inv_perm[t*k+j], :]  (+ y_perm[T*k+t, :] if
