@@ -42,7 +42,11 @@ def parse():
     ap.add_argument("--tokens", type=int, default=64)
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--sweep", default="1,4,16,64", help="extra token counts timed for the sweep field")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the headline oracle CPU sample")
+    ap.add_argument("--cpu-row-seconds", type=float, default=1.0,
+                    help="budget of each other oracle row (every workload at all threads and at one)")
+    ap.add_argument("--int4-tokens", default="1,2,8", help="token counts of the int4 decode figures")
+    ap.add_argument("--no-int4-prefill", action="store_true", help="skip the int4 layer at prefill sizes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-int4", action="store_true")
@@ -53,8 +57,8 @@ def parse():
                     help="stacked layers in the pinned pool (24 need ~80 GB of pinned host memory)")
     ap.add_argument("--offload-steps", type=int, default=2048)
     ap.add_argument("--cpu-extended", action="store_true",
-                    help="also time the oracle on every workload at all and at one BLAS thread, and the LRU "
-                         "simulator on one core (adds about two minutes of host work)")
+                    help="also time the oracle's prefill layer on one BLAS thread, and the LRU simulator on one "
+                         "core")
     return ap.parse_args()
 
 
@@ -74,63 +78,123 @@ def algorithmic_bytes(counts: np.ndarray, T: int, d: int, f: int, k: int, E: int
     return dict(U=U, gateup=gateup, down=down, layer=layer)
 
 
-def cpu_baseline(wl, li, T, budget_s):
-    """The oracle as it stands, on the host cores, on a bounded number of layer calls."""
-    import synth
-    from oracle.layer import moe_layer
+class _F64Expert:
+    """An expert decoded once by the oracle's own routine (oracle.numerics.expert_to_f64) before
+    the timed region; the oracle passes float64 weights through unchanged."""
 
+    def __init__(self, ew):
+        from oracle.numerics import expert_to_f64
+
+        self.wdt = "f64"
+        self.wg, self.wu, self.wd = expert_to_f64(ew)
+
+
+def _decoded_experts(li, batches, k):
+    """li.experts with every expert the sample batches route to decoded in advance (the others are
+    never read by the timed calls), plus li.shared decoded."""
+    from oracle.router import route
+
+    used = set()
+    for x in batches:
+        _, idx, _ = route(x, li.w_router, li.bias, li.wl.act, k)
+        used.update(int(e) for e in np.unique(idx))
+    experts = list(li.experts)
+    for e in used:
+        experts[e] = _F64Expert(experts[e])
+    shared = None if li.shared is None else _F64Expert(li.shared)
+    return experts, shared
+
+
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
 
-        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        blas = 1
-    cores = max(blas, int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
-    calls, t0 = 0, time.perf_counter()
-    while True:
-        xb = synth.layer_inputs(wl, T, seed=0, batch=calls, with_experts=False).x
-        moe_layer(xb, li.w_router, li.bias, wl.act, wl.k, wl.E, li.experts)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or calls >= 1000:
-            break
-    return {"value": calls * T / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{calls} layer calls of {T} tokens of the headline layer (float64 numpy/BLAS oracle, {el:.1f} s)"}
+        return 1
 
 
-def cpu_extended(budget_s: float = 3.0):
-    """The oracle as it stands on each workload's layer, with the BLAS pool at all host threads and
-    at one thread (bounded samples of layer calls), plus the LRU simulator's decode steps/s on one
-    core over the 24-layer routing trace at 40 % and 58 % capacity."""
-    import synth
+def _time_oracle(wl, li, experts, shared, batches, budget_s, threads=None):
+    """Layer calls of the oracle over `batches` (cycled) until `budget_s` has passed (at least one
+    call); BLAS limited to `threads` when given.  -> (tokens/s, calls, seconds, threads used)."""
     from oracle.layer import moe_layer
-    from oracle.lru import LRUSim
-    from threadpoolctl import threadpool_info, threadpool_limits
+    from threadpoolctl import threadpool_limits
 
-    nthreads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    cases = [("tiny_fp32", (16,)), ("qwen_a3b_decode_bf16", (1, 4, 16, 64)), ("dsv4_decode_int4", (1, 2, 8)),
-             ("dsv4_prefill_bf16", (512,))]
-    out = {"blas_threads": nthreads, "layers": {}}
+    with threadpool_limits(limits=threads):
+        used = _blas_threads()
+        calls, toks, t0 = 0, 0, time.perf_counter()
+        while True:
+            x = batches[calls % len(batches)]
+            moe_layer(x, li.w_router, li.bias, wl.act, wl.k, wl.E, experts, shared)
+            calls += 1
+            toks += x.shape[0]
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    return toks / el, calls, el, used
+
+
+def cpu_baseline(budget_s: float, row_s: float, prefill_li=None, extended=False):
+    """The oracle as it stands (float64 numpy/BLAS) on the host cores: every workload's layer, with
+    the BLAS pool at all host threads and at one thread, weights decoded before the timed region
+    (only the experts the timed batches route to).  The headline entry is the Qwen-A3B shaped decode
+    layer at T=64 on all threads with a `budget_s` sample; each other row gets `row_s`.  The
+    prefill layer (T=512, one call) runs on all threads, and on one thread with `extended`."""
+    import synth
+
+    nthreads = _blas_threads()
+    rows = {}
+    head = None
+    cases = [("tiny_fp32", (16,)), ("qwen_a3b_decode_bf16", (1, 4, 16, 64)), ("dsv4_decode_int4", (1, 2, 8))]
     for name, Ts in cases:
         wl = synth.WORKLOADS[name]
         li = synth.layer_inputs(wl, max(Ts), seed=0)
+        bx = {T: [synth.layer_inputs(wl, T, seed=0, batch=b, with_experts=False).x for b in range(2)] for T in Ts}
+        t0 = time.perf_counter()
+        experts, shared = _decoded_experts(li, [x for v in bx.values() for x in v], wl.k)
+        log(f"oracle {name}: {sum(isinstance(e, _F64Expert) for e in experts)} experts decoded in "
+            f"{time.perf_counter() - t0:.1f} s (outside the timed region)")
         for T in Ts:
-            x = synth.layer_inputs(wl, T, seed=0, with_experts=False).x
             row = {}
-            for label, limit in (("all_threads", None), ("one_thread", 1)):
-                if T >= 512 and limit == 1:
-                    continue  # one call takes minutes on one thread
-                with threadpool_limits(limits=limit):
-                    calls, t0 = 0, time.perf_counter()
-                    while True:
-                        moe_layer(x, li.w_router, li.bias, wl.act, wl.k, wl.E, li.experts, li.shared)
-                        calls += 1
-                        el = time.perf_counter() - t0
-                        if el >= budget_s:
-                            break
-                row[label] = {"tokens_per_s": calls * T / el, "calls": calls, "seconds": el}
-            out["layers"][f"{name} T={T}"] = row
-            log(f"oracle {name} T={T}: {row}")
+            for label, lim in (("all_threads", None), ("one_thread", 1)):
+                budget = budget_s if (name == "qwen_a3b_decode_bf16" and T == 64 and lim is None) else row_s
+                v, calls, el, used = _time_oracle(wl, li, experts, shared, bx[T], budget, lim)
+                row[label] = {"tokens_per_s": v, "calls": calls, "seconds": el, "threads": used}
+                if budget == budget_s:
+                    head = (v, calls, el, used)
+            rows[f"{name} T={T}"] = row
+            log(f"oracle {name} T={T}: {row['all_threads']['tokens_per_s']:.4g} / "
+                f"{row['one_thread']['tokens_per_s']:.4g} tokens/s (all threads / one)")
+        del li, experts, shared
+    if prefill_li is not None:
+        wl = prefill_li.wl
+        x = synth.layer_inputs(wl, 512, seed=0, with_experts=False).x
+        t0 = time.perf_counter()
+        experts, shared = _decoded_experts(prefill_li, [x], wl.k)
+        log(f"oracle {wl.name}: experts decoded in {time.perf_counter() - t0:.1f} s (outside the timed region)")
+        row = {}
+        for label, lim in (("all_threads", None), ("one_thread", 1)):
+            if lim == 1 and not extended:
+                continue
+            v, calls, el, used = _time_oracle(wl, prefill_li, experts, shared, [x], 0.0, lim)
+            row[label] = {"tokens_per_s": v, "calls": calls, "seconds": el, "threads": used}
+        rows[f"{wl.name} T=512"] = row
+        log(f"oracle {wl.name} T=512: {row}")
+        del experts, shared
+    v, calls, el, used = head
+    return {"value": v, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{calls} layer calls of 64 tokens of the headline layer (float64 numpy/BLAS oracle, "
+                      f"{el:.1f} s; the experts the calls route to decoded to float64 before timing)",
+            "blas_threads_available": nthreads, "per_config": rows}
+
+
+def cpu_extended(budget_s: float = 3.0):
+    """The LRU simulator's decode steps/s on one core over the 24-layer routing trace at 40 % and
+    58 % capacity."""
+    import synth
+    from oracle.lru import LRUSim
+
+    out = {}
     wl = synth.WORKLOADS["dsv4_offload_int4"]
     L, E, steps = 24, wl.E, 2048
     trace = synth.routing_trace(0, steps, L, E, wl.k)
@@ -369,7 +433,7 @@ def prefill_split(moe, wl, layer, T, stream, heavy_min=256, reps=10):
     return out
 
 
-def bench_prefill(moe, stream):
+def bench_prefill(moe, stream, keep=None):
     import torch
     import synth
     from expert_offload_cache_amd.layer import DeviceLayer
@@ -382,10 +446,12 @@ def bench_prefill(moe, stream):
     out["heavy_tail_split"] = {str(T): prefill_split(moe, wl, layer, T, stream) for T in wl.T_list}
     del layer
     torch.cuda.empty_cache()
+    if keep is not None:
+        keep["li"] = li  # the host weights, for the oracle's prefill row
     return out
 
 
-def bench_int4(moe, stream, replicas=4, graph=False):
+def bench_int4(moe, stream, replicas=4, graph=False, tokens=None, prefill=True):
     import torch
     import synth
     from expert_offload_cache_amd.layer import DeviceLayer
@@ -396,7 +462,7 @@ def bench_int4(moe, stream, replicas=4, graph=False):
     layers = replicate(DeviceLayer.from_inputs(li), replicas)
     out = {}
     wb = 0.5 + 2.0 / 128  # int4 weight bytes per element, with its bf16 group scale
-    for T in wl.T_list:
+    for T in (tokens or wl.T_list):
         steps = 100
         el, kern, counts, el_graph = time_layer(moe, wl, layers, T, steps, 10, stream, graph=graph)
         b = [algorithmic_bytes(c, T, wl.d, wl.f, wl.k, wl.E, w_bytes=wb, shared=True) for c in counts]
@@ -409,7 +475,8 @@ def bench_int4(moe, stream, replicas=4, graph=False):
                        "ffn_GBps": (gu_b + dn_b) / (gu + dn) / 1e3, "kernels_us": kern}
         log(f"int4 decode T={T}: {out[str(T)]['tokens_per_s']:.0f} tok/s, FFN {out[str(T)]['ffn_GBps']:.0f} GB/s")
     # the same int4 layer at prefill sizes: the int4 MFMA grouped GEMM (weights dequantised in registers)
-    out["prefill"] = prefill_figures(moe, wl, layers[0], (512, 2048, 8192), stream, w_bytes=wb)
+    if prefill:
+        out["prefill"] = prefill_figures(moe, wl, layers[0], (512, 2048, 8192), stream, w_bytes=wb)
     del layers
     torch.cuda.empty_cache()
     return out
@@ -507,8 +574,12 @@ def main():
     torch.cuda.empty_cache()
 
     extra = {"hbm_copy_GBps": hbm_copy_GBps()}
-    for name, enabled, fn in (("prefill_bf16", not args.no_prefill, lambda: bench_prefill(moe, stream)),
-                              ("decode_int4", not args.no_int4, lambda: bench_int4(moe, stream, graph=args.graph))):
+    kept = {}
+    int4_T = [int(t) for t in args.int4_tokens.split(",") if t]
+    for name, enabled, fn in (("prefill_bf16", not args.no_prefill, lambda: bench_prefill(moe, stream, kept)),
+                              ("decode_int4", not args.no_int4,
+                               lambda: bench_int4(moe, stream, graph=args.graph, tokens=int4_T,
+                                                  prefill=not args.no_int4_prefill))):
         if enabled:
             try:
                 extra[name] = fn()
@@ -533,9 +604,12 @@ def main():
             extra["offload_int4"] = {"error": f"{type(err).__name__}: {err}"}
 
     cpu = None
+    del li
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores")
-        cpu = cpu_baseline(wl, li, Tmain, args.cpu_seconds)
+        cpu = cpu_baseline(args.cpu_seconds, args.cpu_row_seconds, prefill_li=kept.get("li"),
+                           extended=args.cpu_extended)
+    kept.clear()
     if args.cpu_extended:
         extra["cpu_extended"] = cpu_extended()
     line = {

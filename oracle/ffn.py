@@ -7,10 +7,15 @@ no biases, W_g, W_u: [f, d], W_d: [d, f] (rows = outputs).
 """
 import numpy as np
 
+from .numerics import round_to_bf16
 
-def swiglu_expert(a: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
-    """a: [n, d] float64 -> [n, d] float64."""
+
+def swiglu_expert(a: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, h_bf16: bool = False) -> np.ndarray:
+    """a: [n, d] float64 -> [n, d] float64.  h_bf16: h rounded to bfloat16 before the down
+    projection, as the bf16 layers may store it (otherwise h stays float64)."""
     g = a @ wg.T
     u = a @ wu.T
     h = (g / (1.0 + np.exp(-g))) * u
+    if h_bf16:
+        h = round_to_bf16(h)
     return h @ wd.T

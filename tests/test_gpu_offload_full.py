@@ -1,0 +1,171 @@
+"""The offloaded stack at the DeepSeek-V4-Flash shaped int4 layer's own size: E=256 routed experts
+a layer, top-6 plus a shared expert, d_model 4096, d_ff 2048, one 12,976,128-byte slot per expert,
+three stacked layers in the pinned host pool (about 10 GB), a 2048-token prefill, then 32 batch-1
+decode steps of the seeded routing trace (FreeToken linux guide, "MoE memory handling" mechanism
+table: one shared LRU over the GPU expert slots, full-layer double buffering during prefill).
+
+Two capacities: C = 2E = 512 slots (the prefill double-buffers the next layer while a layer runs)
+and C = 320 (less than two layers: the prefill fetches each layer before it runs, and decode
+evicts).  At both, the cache's hit/miss sequence and copy plan equal the oracle's simulator; the
+outputs are bitwise equal across the capacities; decode outputs and sampled prefill tokens match
+the float64 oracle within 2e-2.
+
+Pool contents: 12 distinct seeded expert images, key (layer, expert) holding image
+(layer * 256 + expert) mod 12; every key still has its own pinned bytes, slot, copy and LRU entry.
+"""
+import gc
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import need_gpu, rel_err_per_token, y_to_f64
+from oracle.layer import moe_layer, moe_layer_tokens
+from oracle.lru import LRUSim
+from oracle.numerics import expert_to_f64
+
+pytestmark = pytest.mark.gpu
+
+L, T_PRE, STEPS, IMAGES = 3, 2048, 32, 12
+
+
+def _wl():
+    return synth.WORKLOADS["dsv4_offload_int4"]
+
+
+def _trace(wl):
+    return synth.routing_trace(seed=0, steps=STEPS, L=L, E=wl.E, k=wl.k)
+
+
+def _expected(wl, trace, C):
+    sim = LRUSim(C)
+    flags, copies = [], []
+    reqs = [(l, list(range(wl.E)), "prefill") for l in range(L)]
+    reqs += [(l, np.unique(trace[s, l]).tolist(), "decode") for s in range(STEPS) for l in range(L)]
+    for l, ids, phase in reqs:
+        slots, fl, _ = sim.request(l, ids, phase=phase)
+        flags += fl
+        copies += [(sl, l * wl.E + e) for e, sl, h in zip(sorted(ids), slots, fl) if not h]
+    return np.array(flags, dtype=np.uint8), copies
+
+
+@pytest.fixture(scope="module")
+def runs():
+    need_gpu()
+    import torch
+    from expert_offload_cache_amd.offload import OffloadStack
+
+    wl = _wl()
+    trace = _trace(wl)
+    out = {}
+    for C in (512, 320):
+        print(f"full-size int4 offload stack: L={L} E={wl.E} C={C} slot={12976128} B", flush=True)
+        stack = OffloadStack(wl, L, C, seed=0, n_images=IMAGES, prefill_tokens=T_PRE)
+        try:
+            assert stack.stride == 12976128
+            _, pre = stack.prefill(keep_outputs=True)
+            _, dec = stack.decode(trace, keep_outputs=True)
+            out[C] = dict(pre=[(i.cpu().numpy(), y_to_f64(y)) for i, y in pre],
+                          dec=[(s, l, y_to_f64(y)) for s, l, y in dec], trace=stack.cache.trace(),
+                          log=stack.cache.copy_log(), stats=stack.cache.stats(),
+                          status=int(stack._workspace(1)[:4].view(torch.int32).item()),
+                          images=[[stack.image_of(l, e) for e in range(wl.E)] for l in range(L)],
+                          shared_layer=[stack.shared_layer_of(l) for l in range(L)])
+        finally:
+            stack.close()
+            del stack
+            gc.collect()
+            torch.cuda.empty_cache()
+    return wl, trace, out
+
+
+@pytest.mark.parametrize("C", [512, 320])
+def test_full_size_cache_decisions_match_simulator(runs, C):
+    wl, trace, out = runs
+    r = out[C]
+    want, copies = _expected(wl, trace, C)
+    assert np.array_equal(r["trace"], want)
+    assert [(int(a), int(b)) for a, b in r["log"][:, :2]] == copies
+    st = r["stats"]
+    assert st["pre_acc"] == L * wl.E and st["dec_acc"] == int(sum(len(np.unique(trace[s, l]))
+                                                                   for s in range(STEPS) for l in range(L)))
+    assert st["bytes_h2d"] == int((want == 0).sum()) * 12976128
+    assert r["status"] == 0
+
+
+def test_full_size_outputs_do_not_depend_on_capacity(runs):
+    _, _, out = runs
+    a, b = out[512], out[320]
+    assert len(a["dec"]) == len(b["dec"]) == STEPS * L
+    for (s0, l0, y0), (s1, l1, y1) in zip(a["dec"], b["dec"]):
+        assert (s0, l0) == (s1, l1) and np.array_equal(y0, y1)
+    for (i0, y0), (i1, y1) in zip(a["pre"], b["pre"]):
+        assert np.array_equal(i0, i1) and np.array_equal(y0, y1)
+
+
+class _Decoded:
+    """An expert already decoded by the oracle (oracle.numerics.expert_to_f64 passes float64 through)."""
+
+    def __init__(self, ew):
+        self.wdt = "f64"
+        self.wg, self.wu, self.wd = expert_to_f64(ew)
+
+
+_decoded = {}
+
+
+def _image(wl, i):
+    if i not in _decoded:
+        _decoded[i] = _Decoded(synth.expert_weights(wl, 0, i // wl.E, i % wl.E))
+    return _decoded[i]
+
+
+def _shared(wl, layer):
+    key = ("shared", layer)
+    if key not in _decoded:
+        _decoded[key] = _Decoded(synth.expert_weights(wl, 0, layer, 0, shared=True))
+    return _decoded[key]
+
+
+class _Experts:
+    """Layer l's expert list for the oracle: image i of key (l, e), decoded once per image."""
+
+    def __init__(self, wl, images):
+        self.wl, self.images = wl, images
+
+    def __len__(self):
+        return len(self.images)
+
+    def __getitem__(self, e):
+        return _image(self.wl, self.images[e])
+
+
+def test_full_size_decode_matches_oracle(runs):
+    wl, trace, out = runs
+    r = out[512]
+    worst = 0.0
+    for s, l, y in r["dec"]:
+        li = synth.layer_inputs(wl, 8, 0, layer=l, batch=1, with_experts=False)
+        experts = _Experts(wl, r["images"][l])
+        shared = _shared(wl, r["shared_layer"][l])
+        ref = moe_layer(li.x[s % 8:s % 8 + 1], li.w_router, li.bias, "bf16", wl.k, wl.E, experts, shared,
+                        forced_idx=trace[s, l:l + 1])
+        worst = max(worst, float(rel_err_per_token(y, ref["y"]).max()))
+    print(f"full-size decode: max per-token rel err {worst:.3g} over {len(r['dec'])} layer steps")
+    assert worst <= 2e-2
+
+
+def test_full_size_prefill_matches_oracle(runs):
+    wl, _, out = runs
+    r = out[512]
+    toks = [0, 1, 511, 1024, 1500, T_PRE - 1]
+    for l, (idx, y) in enumerate(r["pre"]):
+        li = synth.layer_inputs(wl, T_PRE, 0, layer=l, batch=0, with_experts=False)
+        experts = _Experts(wl, r["images"][l])
+        shared = _shared(wl, r["shared_layer"][l])
+        ref = moe_layer_tokens(toks, li.x, li.w_router, li.bias, "bf16", wl.k, wl.E, experts, shared)
+        assert np.array_equal(idx[toks], ref["topk_idx"])
+        err = rel_err_per_token(y[toks], ref["y"])
+        print(f"full-size prefill layer {l}: max rel err {err.max():.3g}")
+        assert err.max() <= 2e-2, (l, err)
+    _decoded.clear()
