@@ -43,6 +43,9 @@ moe_status ffn_gemv(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st
 moe_status ffn_gemv_mfma(const FfnArgs& a, int mode, hipStream_t st);
 // bf16 or int4 weights x bf16 activations, K streamed through each wave (ffn_gemv_ks.hip)
 moe_status ffn_gemv_ks(const FfnArgs& a, int mode, moe_dtype w, hipStream_t st);
+// bf16 or int4 weights x bf16 activations, a few tokens, every weight load of a wave issued at once
+// (ffn_gemv_deep.hip)
+moe_status ffn_gemv_deep(const FfnArgs& a, int mode, moe_dtype w, hipStream_t st);
 // prefill path: MFMA grouped GEMM (ffn_mfma.hip); returns MOE_EDTYPE when it does not apply
 moe_status ffn_mfma(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st);
 

@@ -293,18 +293,22 @@ moe_status ffn_gemv(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st
     if (w == MOE_BF16 && act == MOE_BF16) {
         // each projection: the K-streaming kernel where it applies, else the split-input
         // matrix-core kernel, else the vector-ALU kernel
-        r = ffn_gemv_ks(a, kGateUp, MOE_BF16, st);
+        r = ffn_gemv_deep(a, kGateUp, MOE_BF16, st);
+        if (r == MOE_EDTYPE) r = ffn_gemv_ks(a, kGateUp, MOE_BF16, st);
         if (r == MOE_EDTYPE) r = ffn_gemv_mfma(a, kGateUp, st);
         if (r == MOE_EDTYPE) r = launch<kGateUp, MOE_BF16, true>(a, st, "ffn_gemv_gateup_bf16");
         if (r != MOE_OK) return r;
-        r = ffn_gemv_ks(a, kDown, MOE_BF16, st);
+        r = ffn_gemv_deep(a, kDown, MOE_BF16, st);
+        if (r == MOE_EDTYPE) r = ffn_gemv_ks(a, kDown, MOE_BF16, st);
         if (r == MOE_EDTYPE) r = ffn_gemv_mfma(a, kDown, st);
         if (r == MOE_EDTYPE) r = launch<kDown, MOE_BF16, true>(a, st, "ffn_gemv_down_bf16");
     } else if (w == MOE_INT4_G128 && act == MOE_BF16) {
-        r = ffn_gemv_ks(a, kGateUp, MOE_INT4_G128, st);
+        r = ffn_gemv_deep(a, kGateUp, MOE_INT4_G128, st);
+        if (r == MOE_EDTYPE) r = ffn_gemv_ks(a, kGateUp, MOE_INT4_G128, st);
         if (r == MOE_EDTYPE) r = launch<kGateUp, MOE_INT4_G128, true>(a, st, "ffn_gemv_gateup_int4");
         if (r != MOE_OK) return r;
-        r = ffn_gemv_ks(a, kDown, MOE_INT4_G128, st);
+        r = ffn_gemv_deep(a, kDown, MOE_INT4_G128, st);
+        if (r == MOE_EDTYPE) r = ffn_gemv_ks(a, kDown, MOE_INT4_G128, st);
         if (r == MOE_EDTYPE) r = launch<kDown, MOE_INT4_G128, true>(a, st, "ffn_gemv_down_int4");
     } else if (w == MOE_F32 && act == MOE_F32) {
         r = launch<kGateUp, MOE_F32, false>(a, st, "ffn_gemv_gateup_f32");

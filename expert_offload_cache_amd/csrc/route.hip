@@ -339,40 +339,47 @@ __global__ __launch_bounds__(1024) void route_topk(const float* __restrict__ log
                     topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
 }
 
-// For one token (batch-1 decode) one block selects and gates (select_and_gate, as route_topk;
-// with more tokens it takes them in turn) and then sorts the T*k pairs with moe_permute's
-// counting sort from the ids it kept in LDS: one launch instead of two.  (A sort by the last of route_topk's blocks would need a
-// device-scope release and acquire, which write back and invalidate an XCD's L2.)
-// Dynamic LDS: WAVES * E ints for the sort, then T * k ids.
-// tokens for which one block selects and sorts: each further token adds its selection's latency
-// (about 3 us on MI355X), and at 2 tokens the two kernels were already faster
-constexpr int kOneBlockMaxT = 1;
-
-template <int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void route_topk_permute(const float* __restrict__ logits, int T, int E,
-                                                                 int k, const int32_t* __restrict__ forced,
-                                                                 int nbits, int32_t* __restrict__ topk_idx,
-                                                                 float* __restrict__ topk_w,
-                                                                 int32_t* __restrict__ counts,
-                                                                 int32_t* __restrict__ offsets,
-                                                                 int32_t* __restrict__ perm,
-                                                                 int32_t* __restrict__ inv_perm) {
+// For one token (batch-1 decode) one block selects and gates (select_and_gate, as route_topk) and
+// then places the token's k pairs by expert straight from the selected ids: expert e's count is the
+// number of pairs with id e, its offset the number of pairs with a smaller id, and pair j's sorted
+// position the number of pairs before it in (id, j) order -- the stable counting sort's result for
+// one token, without its passes.  One launch instead of two.  (A sort by the last of route_topk's
+// blocks would need a device-scope release and acquire, which write back and invalidate an XCD's
+// L2.)  Ids are clamped into [0, E) for the placement, as in moe_permute.
+__global__ __launch_bounds__(1024) void route_topk_permute1(const float* __restrict__ logits, int E, int k,
+                                                           const int32_t* __restrict__ forced,
+                                                           int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
     __shared__ __align__(16) float s_logit[1024];
     __shared__ int s_sel[1024];
     __shared__ float s_val[1024];
-    __shared__ int32_t s_wave[WAVES];
-    extern __shared__ int32_t dyn[];
-    int32_t* run = dyn;
-    int32_t* s_ids = dyn + WAVES * E;
-    for (int t = 0; t < T; ++t) {
-        for (int e = threadIdx.x; e < E; e += blockDim.x) s_logit[e] = logits[(size_t)t * E + e];
-        __syncthreads();
-        select_and_gate(s_logit, E, k, forced ? forced + (size_t)t * k : nullptr, s_sel, s_val,
-                        topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
-        for (int j = threadIdx.x; j < k; j += blockDim.x) s_ids[t * k + j] = s_sel[j];
-        __syncthreads();  // the next token overwrites s_logit, s_sel and the gate terms
+    const int tid = threadIdx.x, nth = blockDim.x;
+    for (int e = tid; e < E; e += nth) s_logit[e] = logits[e];
+    __syncthreads();
+    // s_sel is complete after the barrier inside (nothing writes it afterwards)
+    select_and_gate(s_logit, E, k, forced, s_sel, s_val, topk_idx, topk_w);
+    for (int e = tid; e < E; e += nth) {
+        int c = 0, o = 0;
+        for (int j = 0; j < k; ++j) {
+            const int id = min(max(s_sel[j], 0), E - 1);
+            c += id == e;
+            o += id < e;
+        }
+        counts[e] = c;
+        offsets[e] = o;
     }
-    permute_block<WAVES>(s_ids, T * k, E, nbits, counts, offsets, perm, inv_perm, run, s_wave);
+    if (tid == 0) offsets[E] = k;
+    for (int j = tid; j < k; j += nth) {
+        const int idj = min(max(s_sel[j], 0), E - 1);
+        int pos = 0;
+        for (int i = 0; i < k; ++i) {
+            const int idi = min(max(s_sel[i], 0), E - 1);
+            pos += idi < idj || (idi == idj && i < j);
+        }
+        perm[pos] = j;
+        inv_perm[j] = pos;
+    }
 }
 
 // decode: one wave per (token, expert); lane j owns segment j of the row, issues all of its
@@ -574,28 +581,16 @@ extern "C" moe_status moe_route_permute(const void* x, moe_dtype act, int T, int
     hipStream_t st = (hipStream_t)s;
     r = launch_route_logits(x, act == MOE_BF16, T, d, w_router, bias, E, logits, st);
     if (r != MOE_OK) return r;
-    // the top-k block's waves: a power of two with 4 threads an expert (as route_topk)
-    int waves = 1;
-    while (waves < 16 && waves * 64 < 4 * E) waves *= 2;
-    const size_t dyn_bytes = sizeof(int32_t) * ((size_t)waves * E + (size_t)T * k);
-    if (T > kOneBlockMaxT || dyn_bytes > 40960) {
+    if (T > 1) {
         r = launch_route_topk(logits, T, E, k, forced_idx, topk_idx, topk_w, st);
         if (r != MOE_OK) return r;
         return moe_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, nullptr, 0, s);
     }
-    int nbits = 0;
-    while ((1 << nbits) < E) ++nbits;
+    // one token: the top-k block's threads, a power of two with 4 threads an expert (as route_topk)
+    int nth = 64;
+    while (nth < 1024 && nth < 4 * E) nth *= 2;
     ProfScope p("route_topk_permute", st);
-#define RTP(W)                                                                                              \
-    route_topk_permute<W><<<1, 64 * W, dyn_bytes, st>>>(logits, T, E, k, forced_idx, nbits, topk_idx, topk_w, \
-                                                         counts, offsets, perm, inv_perm)
-    switch (waves) {
-        case 1: RTP(1); break;
-        case 2: RTP(2); break;
-        case 4: RTP(4); break;
-        case 8: RTP(8); break;
-        default: RTP(16); break;
-    }
-#undef RTP
+    route_topk_permute1<<<1, nth, 0, st>>>(logits, E, k, forced_idx, topk_idx, topk_w, counts, offsets, perm,
+                                           inv_perm);
     return check_launch("route_topk_permute");
 }

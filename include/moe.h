@@ -132,8 +132,8 @@ MOE_API moe_status moe_permute(const int32_t* topk_idx, int T, int k, int E, int
  * (FreeToken linux guide, "MoE memory handling": per layer the router picks the experts and
  * the runtime gathers each expert's tokens).  Every output is bitwise what the two calls give
  * for the same arguments: logits, topk_idx, topk_w as moe_route; counts, offsets, perm,
- * inv_perm as moe_permute.  For T = 1 (and E <= 512) one block selects, gates and sorts, one
- * launch fewer than the two calls; other shapes run the two calls' kernels.  Arguments, shapes,
+ * inv_perm as moe_permute.  For T = 1 one block selects, gates and places the k pairs by expert,
+ * one launch fewer than the two calls; other shapes run the two calls' kernels.  Arguments, shapes,
  * ownership and errors are those of the two calls; a non-OK status means nothing was enqueued.
  * With T = 0 only counts and offsets are written (zeros). */
 MOE_API moe_status moe_route_permute(const void* x, moe_dtype act, int T, int d, const void* w_router,

@@ -103,6 +103,11 @@ SMALL = [
     # int4, f = 128: the down projection's input split does not apply, the VALU kernel runs it
     ("bf16", "int4", 256, 128, 8, 2, 5, True),
     ("bf16", "int4", 512, 256, 16, 4, 67, False),
+    # int4 at the DeepSeek-shaped d and d_ff with few tokens: the deep-issue decode kernel (every
+    # weight load of a wave in flight at once), both of its gate/up plans and its down plan
+    ("bf16", "int4", 4096, 2048, 8, 2, 1, True),
+    ("bf16", "int4", 4096, 2048, 8, 3, 2, False),
+    ("bf16", "int4", 4096, 2048, 16, 4, 7, True),
     # int4 with many tokens per expert: the int4 MFMA grouped GEMM (down: an odd number of groups)
     ("bf16", "int4", 512, 256, 6, 2, 300, True),
     ("bf16", "int4", 1024, 384, 16, 4, 257, False),
@@ -225,6 +230,34 @@ def test_absent_slot_is_flagged_not_read(qwen_layer, T):
     keep = np.ones(len(yp), bool)
     keep[off[e_bad]:off[e_bad + 1]] = False
     assert np.array_equal(yp[keep], ref[keep])
+
+
+@pytest.mark.parametrize("T", [1, 2, 8])
+def test_int4_absent_slot_is_flagged_not_read(dsv4_int4_layer, T):
+    """The few-token int4 kernels: an absent slot sets the status word and gives that expert zero
+    rows; every other row is bitwise the full call's."""
+    import torch
+    import expert_offload_cache_amd as moe
+
+    wl, _, layer = dsv4_int4_layer
+    lt = synth.layer_inputs(wl, T, seed=0, with_experts=False)
+    x = layer.x_to_device(lt.x)
+    out = layer.forward(x)
+    counts = out["counts"].cpu().numpy()
+    e_bad = int(np.argmax(counts))
+    soe = layer.slot_of_expert.clone()
+    soe[e_bad] = -1
+    ws = layer.workspace(T)
+    y_perm, ws = moe.expert_ffn_grouped(x, out["perm"], out["offsets"], out["counts"], soe, layer.pool,
+                                        layer.n_slots, layer.stride, "int4", wl.f, wl.k, shared_w=layer.shared, ws=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 1
+    off = out["offsets"].cpu().numpy()
+    yp = y_perm.cpu().numpy()
+    assert np.all(yp[off[e_bad]:off[e_bad + 1]] == 0)
+    keep = np.ones(len(yp), bool)
+    keep[off[e_bad]:off[e_bad + 1]] = False
+    assert np.array_equal(yp[keep], out["y_perm"].cpu().numpy()[keep])
 
 
 @pytest.fixture(scope="module")

@@ -71,6 +71,13 @@ def runs():
                           status=int(stack._workspace(1)[:4].view(torch.int32).item()),
                           images=[[stack.image_of(l, e) for e in range(wl.E)] for l in range(L)],
                           shared_layer=[stack.shared_layer_of(l) for l in range(L)])
+            if C == 320:
+                # the same trace with split launches (resident experts before the copies' wait,
+                # the missed ones after them: MOE_SLOT_ELSEWHERE rows in each launch)
+                stack.new_cache(C)
+                stack.prefill()
+                _, dec = stack.decode(trace, keep_outputs=True, split_launch=True)
+                out["split"] = dict(dec=[(s, l, y_to_f64(y)) for s, l, y in dec], trace=stack.cache.trace())
         finally:
             stack.close()
             del stack
@@ -101,6 +108,15 @@ def test_full_size_outputs_do_not_depend_on_capacity(runs):
         assert (s0, l0) == (s1, l1) and np.array_equal(y0, y1)
     for (i0, y0), (i1, y1) in zip(a["pre"], b["pre"]):
         assert np.array_equal(i0, i1) and np.array_equal(y0, y1)
+
+
+def test_full_size_split_launch_matches_plain_decode(runs):
+    _, _, out = runs
+    a, b = out[320], out["split"]
+    assert np.array_equal(a["trace"], b["trace"])  # a fresh cache at the same capacity decides the same
+    assert len(a["dec"]) == len(b["dec"])
+    for (s0, l0, y0), (s1, l1, y1) in zip(a["dec"], b["dec"]):
+        assert (s0, l0) == (s1, l1) and np.array_equal(y0, y1)
 
 
 class _Decoded:
