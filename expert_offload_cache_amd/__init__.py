@@ -13,7 +13,7 @@ import numpy as np
 
 from ._lib import (MOE_BF16, MOE_F32, MOE_INT4_G128, MoeError, check, lib)
 
-__all__ = ["route", "permute", "route_permute", "expert_ffn_grouped", "expert_ffn_grouped_noalloc", "combine",
+__all__ = ["route", "permute", "permute_workspace", "permute_workspace_bytes", "route_permute", "expert_ffn_grouped", "expert_ffn_grouped_noalloc", "combine",
            "slot_bytes", "pack_expert", "workspace_bytes", "hybrid_split", "SlotCache", "pinned_alloc", "pinned_free", "profile_enable",
            "profile_collect", "profile_results", "profile_reset", "MoeError", "WDT", "lib"]
 
@@ -71,8 +71,18 @@ def route(x, w_router, bias, k: int, forced_idx=None, out=None, stream=None):
     return idx, w, logits
 
 
-def permute(topk_idx, E: int, out=None, stream=None):
-    """-> (counts [E], offsets [E+1], perm [T*k], inv_perm [T*k]) int32."""
+def permute_workspace_bytes(T: int, k: int, E: int) -> int:
+    return int(lib().moe_permute_workspace_bytes(T, k, E))
+
+
+def permute_workspace(T: int, k: int, E: int, device):
+    """Device scratch for a split sort of T*k pairs (None when one workgroup sorts)."""
+    n = permute_workspace_bytes(T, k, E)
+    return _torch().empty(n, dtype=_torch().uint8, device=device) if n else None
+
+
+def permute(topk_idx, E: int, out=None, stream=None, ws=None):
+    """-> (counts [E], offsets [E+1], perm [T*k], inv_perm [T*k]) int32.  ws: permute_workspace or None."""
     torch = _torch()
     _contig(topk_idx)
     T, k = topk_idx.shape
@@ -81,12 +91,14 @@ def permute(topk_idx, E: int, out=None, stream=None):
         out = (torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
                torch.empty(T * k, dtype=torch.int32, device=dev), torch.empty(T * k, dtype=torch.int32, device=dev))
     c, o, p, ip = out
-    check(lib().moe_permute(_p(topk_idx), T, k, E, _p(c), _p(o), _p(p), _p(ip), None, 0, _s(stream)))
+    check(lib().moe_permute(_p(topk_idx), T, k, E, _p(c), _p(o), _p(p), _p(ip), _p(ws),
+                            0 if ws is None else ws.numel(), _s(stream)))
     return c, o, p, ip
 
 
-def route_permute(x, w_router, bias, k: int, forced_idx=None, out=None, stream=None):
-    """route then permute as one call -> (topk_idx, topk_w, logits, counts, offsets, perm, inv_perm)."""
+def route_permute(x, w_router, bias, k: int, forced_idx=None, out=None, stream=None, ws=None):
+    """route then permute as one call -> (topk_idx, topk_w, logits, counts, offsets, perm, inv_perm).
+    ws: permute_workspace(T, k, E) or None (then a large batch sorts in one workgroup)."""
     torch = _torch()
     _contig(x, w_router, bias, forced_idx)
     T, d = x.shape
@@ -99,7 +111,8 @@ def route_permute(x, w_router, bias, k: int, forced_idx=None, out=None, stream=N
                torch.empty(T * k, dtype=torch.int32, device=dev))
     idx, w, logits, c, o, p, ip = out
     check(lib().moe_route_permute(_p(x), _act(x), T, d, _p(w_router), _p(bias), E, k, _p(forced_idx), _p(idx),
-                                  _p(w), _p(logits), _p(c), _p(o), _p(p), _p(ip), _s(stream)))
+                                  _p(w), _p(logits), _p(c), _p(o), _p(p), _p(ip), _p(ws),
+                                  0 if ws is None else ws.numel(), _s(stream)))
     return out
 
 

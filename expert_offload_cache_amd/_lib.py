@@ -22,12 +22,14 @@ SIGNATURES = {
     "moe_pack_expert": (_st, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_route": (_st, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "moe_permute": (_st, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "moe_route_permute": (_st, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _i32] + [_vp] * 9),
+    "moe_route_permute": (_st, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _i32] + [_vp] * 8 + [_vp, _sz, _vp]),
+    "moe_permute_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_expert_ffn_grouped": (_st, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _sz,
                                      _i32, _vp, _vp, _vp, _sz, _vp]),
     "moe_expert_ffn_grouped_noalloc": (_st, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32,
                                              _vp, _sz, _i32, _vp, _vp, _vp, _vp]),
+    "moe_prefill_gemv_tokens": (_i32, [_i32]),
     "moe_combine": (_st, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
     "moe_decode_step": (_st, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _sz, _vp, _vp, _vp,
                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),

@@ -50,7 +50,7 @@ extern "C" moe_status moe_decode_step(moe_cache* cache, int n_layers, const moe_
     for (int i = 0; i < n_layers; ++i) {
         const moe_decode_layer& ly = layers[i];
         moe_status r = moe_route_permute(ly.x, act, T, d, ly.w_router, ly.bias, E, k, ly.forced_idx, topk_idx,
-                                         topk_w, logits, counts, offsets, perm, inv_perm, compute);
+                                         topk_w, logits, counts, offsets, perm, inv_perm, nullptr, 0, compute);
         if (r != MOE_OK) return r;
         MOE_HIP(hipMemcpyAsync(host_idx, topk_idx, sizeof(int32_t) * (size_t)T * k, hipMemcpyDeviceToHost, cs));
         MOE_HIP(hipEventRecord(ev.e, cs));
@@ -136,7 +136,7 @@ extern "C" moe_status moe_decode_step_hybrid(
     for (int i = 0; i < n_layers; ++i) {
         const moe_decode_layer& ly = layers[i];
         moe_status r = moe_route_permute(ly.x, act, T, d, ly.w_router, ly.bias, E, k, ly.forced_idx, topk_idx,
-                                         topk_w, logits, counts, offsets, perm, inv_perm, compute);
+                                         topk_w, logits, counts, offsets, perm, inv_perm, nullptr, 0, compute);
         if (r != MOE_OK) return r;
         MOE_HIP(hipMemcpyAsync(host_idx, topk_idx, sizeof(int32_t) * k, hipMemcpyDeviceToHost, cs));
         MOE_HIP(hipEventRecord(ev.e, cs));
@@ -237,7 +237,7 @@ extern "C" moe_status moe_decode_step_split(moe_cache* cache, int n_layers, cons
     for (int i = 0; i < n_layers; ++i) {
         const moe_decode_layer& ly = layers[i];
         moe_status r = moe_route_permute(ly.x, act, T, d, ly.w_router, ly.bias, E, k, ly.forced_idx, topk_idx,
-                                         topk_w, logits, counts, offsets, perm, inv_perm, compute);
+                                         topk_w, logits, counts, offsets, perm, inv_perm, nullptr, 0, compute);
         if (r != MOE_OK) return r;
         MOE_HIP(hipMemcpyAsync(host_idx, topk_idx, sizeof(int32_t) * (size_t)T * k, hipMemcpyDeviceToHost, cs));
         MOE_HIP(hipEventRecord(ev.e, cs));

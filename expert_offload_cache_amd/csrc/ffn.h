@@ -20,7 +20,10 @@ struct FfnArgs {
     float* y_perm;               // [rows, d]
     int32_t* status;             // sticky error word
     void* plan;                  // scratch for the prefill tile schedule
+    int n_lo = 1, n_hi = 1 << 30;  // a launch covers the experts with n_lo <= n_e <= n_hi tokens
 };
+
+enum { kGateUp = 0, kDown = 1 };  // the two projections of a grouped call
 
 constexpr size_t kWsHeader = 256;
 constexpr size_t kPlanBytes = 1 << 16;
@@ -35,8 +38,10 @@ moe_status ffn_prepare(FfnArgs& a, const char* fn, const void* x, moe_dtype act,
 // Launch the grouped experts: the prefill MFMA GEMM where it applies, else the decode GEMVs.
 moe_status ffn_run(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st);
 
-// decode path: grouped GEMV kernels (ffn_gemv.hip)
+// decode path: grouped GEMV kernels (ffn_gemv.hip), both projections or one (mode kGateUp = 0,
+// kDown = 1)
 moe_status ffn_gemv(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st);
+moe_status ffn_gemv_proj(const FfnArgs& a, moe_dtype act, moe_dtype w, int mode, hipStream_t st);
 // The decode kernels below launch one projection (mode kGateUp = 0 or kDown = 1) and return
 // MOE_EDTYPE, with nothing launched, for shapes they do not cover.
 // bf16 x bf16, weights held in registers, inputs split over the waves (ffn_gemv_mfma.hip)
@@ -46,7 +51,9 @@ moe_status ffn_gemv_ks(const FfnArgs& a, int mode, moe_dtype w, hipStream_t st);
 // bf16 or int4 weights x bf16 activations, a few tokens, every weight load of a wave issued at once
 // (ffn_gemv_deep.hip)
 moe_status ffn_gemv_deep(const FfnArgs& a, int mode, moe_dtype w, hipStream_t st);
-// prefill path: MFMA grouped GEMM (ffn_mfma.hip); returns MOE_EDTYPE when it does not apply
+// prefill path: MFMA grouped GEMM (ffn_mfma.hip), both projections or one; MOE_EDTYPE when it
+// does not apply
 moe_status ffn_mfma(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st);
+moe_status ffn_mfma_proj(const FfnArgs& a, moe_dtype act, moe_dtype w, int mode, hipStream_t st);
 
 }  // namespace moe

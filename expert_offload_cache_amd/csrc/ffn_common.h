@@ -25,15 +25,19 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 
 // Work item a of the launch -> (expert, token chunk).  Expert e contributes ceil(n_e / ntg)
 // chunks, in ascending expert id; the shared expert's ceil(T / ntg) chunks come last (e = -1).
+// Only experts whose token count lies in [n_lo, n_hi] take part (the shared expert counts T
+// tokens): a grouped call can run its heavy and its light experts in different launches.
 // Returns false when a is past the last item.  Every lane of the calling wave agrees.
 __device__ __forceinline__ bool find_work(const int32_t* __restrict__ counts, int E, int T, int ntg, bool has_shared, int a,
-                          int& e_out, int& chunk_out) {
+                          int& e_out, int& chunk_out, int n_lo, int n_hi) {
     const int lane = threadIdx.x & 63;
     const int per = (E + 63) / 64;
+    has_shared = has_shared && T >= n_lo && T <= n_hi;
+    auto chunks = [&](int n) { return (n >= n_lo && n <= n_hi) ? (n + ntg - 1) / ntg : 0; };
     int nz = 0;
     for (int i = 0; i < per; ++i) {
         int e = lane * per + i;
-        if (e < E) nz += (counts[e] + ntg - 1) / ntg;
+        if (e < E) nz += chunks(counts[e]);
     }
     int incl = nz;
 #pragma unroll
@@ -56,7 +60,7 @@ __device__ __forceinline__ bool find_work(const int32_t* __restrict__ counts, in
         for (int i = 0; i < per; ++i) {
             int e = lane * per + i;
             if (e >= E) break;
-            int ce = (counts[e] + ntg - 1) / ntg;
+            int ce = chunks(counts[e]);
             if (r < ce) {
                 found = e;
                 chunk = r;
@@ -98,7 +102,6 @@ __device__ __forceinline__ void int4_word_to_bf16(uint32_t w, uint32_t* out) {
     out[3] = ((w >> 12) & 0x000F000Fu) | kMagic;
 }
 
-enum { kGateUp = 0, kDown = 1 };
 
 // One token group of one item: acc[i][m] = this lane's partial dot products of its weight share
 // (fragments f0 .. f0+nmine-1 of matrix m, already in registers) with token i's staged row.

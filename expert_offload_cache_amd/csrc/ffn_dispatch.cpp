@@ -59,7 +59,34 @@ moe_status ffn_prepare(FfnArgs& a, const char* fn, const void* x, moe_dtype act,
     return MOE_OK;
 }
 
+#ifndef MOE_SPLIT_INT4
+#define MOE_SPLIT_INT4 0
+#endif
+#ifndef MOE_SPLIT_BF16
+#define MOE_SPLIT_BF16 0
+#endif
+
+int prefill_split(moe_dtype w) { return w == MOE_INT4_G128 ? MOE_SPLIT_INT4 : w == MOE_BF16 ? MOE_SPLIT_BF16 : 0; }
+
 moe_status ffn_run(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st) {
+    // Prefill with few tokens on most experts: the experts holding fewer than `split` tokens go to
+    // the decode kernels (their weights are streamed once, no 128-token tiles to fill), the others
+    // and the shared expert to the matrix-core GEMM; both gate/up launches precede both down
+    // launches.  0 = one launch per projection.
+    const int split = prefill_split(w);
+    if (split > 1 && act == MOE_BF16 && a.T > 64) {
+        FfnArgs heavy = a, light = a;
+        heavy.n_lo = split;
+        light.n_hi = split - 1;
+        for (int mode = kGateUp; mode <= kDown; ++mode) {
+            moe_status r = ffn_mfma_proj(heavy, act, w, mode, st);
+            if (r == MOE_EDTYPE) return ffn_gemv(a, act, w, st);  // the GEMM does not take this shape
+            if (r != MOE_OK) return r;
+            r = ffn_gemv_proj(light, act, w, mode, st);
+            if (r != MOE_OK) return r;
+        }
+        return MOE_OK;
+    }
     moe_status r = ffn_mfma(a, act, w, st);
     if (r != MOE_EDTYPE) return r;
     return ffn_gemv(a, act, w, st);
@@ -68,6 +95,11 @@ moe_status ffn_run(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st)
 }  // namespace moe
 
 extern "C" {
+
+int moe_prefill_gemv_tokens(moe_dtype w) {
+    const int s = moe::prefill_split(w);
+    return s > 1 ? s - 1 : 0;
+}
 
 size_t moe_workspace_bytes(int T, int d, int f, int E, int k, int has_shared, moe_dtype act, moe_dtype w) {
     (void)d;

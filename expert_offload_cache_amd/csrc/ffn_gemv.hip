@@ -64,7 +64,7 @@ __global__ __launch_bounds__(max_threads(MODE, W)) void ffn_gemv_kernel(FfnArgs 
     float* s_red = (float*)(smem + (size_t)NTG * K * ESZ);
 
     int e, chunk;
-    if (!find_work(a.counts, a.E, a.T, NTG, a.shared_w != nullptr, blockIdx.y, e, chunk)) return;
+    if (!find_work(a.counts, a.E, a.T, NTG, a.shared_w != nullptr, blockIdx.y, e, chunk, a.n_lo, a.n_hi)) return;
     const bool shared = (e == -1);
     const int n_all = __builtin_amdgcn_readfirstlane(shared ? a.T : a.counts[e]);
     const int i0 = chunk * NTG;                 // this workgroup's tokens: i0 .. i0 + nt - 1
@@ -288,35 +288,38 @@ moe_status launch(const FfnArgs& a, hipStream_t st, const char* name) {
 
 }  // namespace
 
-moe_status ffn_gemv(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st) {
+// One projection (mode kGateUp or kDown) of the decode kernels: the deep-issue kernel where it
+// applies, else the K-streaming kernel, else the split-input matrix-core kernel (bf16), else the
+// vector-ALU kernel.
+moe_status ffn_gemv_proj(const FfnArgs& a, moe_dtype act, moe_dtype w, int mode, hipStream_t st) {
     moe_status r;
     if (w == MOE_BF16 && act == MOE_BF16) {
-        // each projection: the K-streaming kernel where it applies, else the split-input
-        // matrix-core kernel, else the vector-ALU kernel
-        r = ffn_gemv_deep(a, kGateUp, MOE_BF16, st);
-        if (r == MOE_EDTYPE) r = ffn_gemv_ks(a, kGateUp, MOE_BF16, st);
-        if (r == MOE_EDTYPE) r = ffn_gemv_mfma(a, kGateUp, st);
-        if (r == MOE_EDTYPE) r = launch<kGateUp, MOE_BF16, true>(a, st, "ffn_gemv_gateup_bf16");
-        if (r != MOE_OK) return r;
-        r = ffn_gemv_deep(a, kDown, MOE_BF16, st);
-        if (r == MOE_EDTYPE) r = ffn_gemv_ks(a, kDown, MOE_BF16, st);
-        if (r == MOE_EDTYPE) r = ffn_gemv_mfma(a, kDown, st);
-        if (r == MOE_EDTYPE) r = launch<kDown, MOE_BF16, true>(a, st, "ffn_gemv_down_bf16");
-    } else if (w == MOE_INT4_G128 && act == MOE_BF16) {
-        r = ffn_gemv_deep(a, kGateUp, MOE_INT4_G128, st);
-        if (r == MOE_EDTYPE) r = ffn_gemv_ks(a, kGateUp, MOE_INT4_G128, st);
-        if (r == MOE_EDTYPE) r = launch<kGateUp, MOE_INT4_G128, true>(a, st, "ffn_gemv_gateup_int4");
-        if (r != MOE_OK) return r;
-        r = ffn_gemv_deep(a, kDown, MOE_INT4_G128, st);
-        if (r == MOE_EDTYPE) r = ffn_gemv_ks(a, kDown, MOE_INT4_G128, st);
-        if (r == MOE_EDTYPE) r = launch<kDown, MOE_INT4_G128, true>(a, st, "ffn_gemv_down_int4");
-    } else if (w == MOE_F32 && act == MOE_F32) {
-        r = launch<kGateUp, MOE_F32, false>(a, st, "ffn_gemv_gateup_f32");
-        if (r == MOE_OK) r = launch<kDown, MOE_F32, false>(a, st, "ffn_gemv_down_f32");
-    } else {
-        return set_error(MOE_EDTYPE, "moe_expert_ffn_grouped: unsupported act/weight dtypes (%d,%d)", (int)act, (int)w);
+        r = ffn_gemv_deep(a, mode, MOE_BF16, st);
+        if (r == MOE_EDTYPE) r = ffn_gemv_ks(a, mode, MOE_BF16, st);
+        if (r == MOE_EDTYPE) r = ffn_gemv_mfma(a, mode, st);
+        if (r == MOE_EDTYPE)
+            r = mode == kGateUp ? launch<kGateUp, MOE_BF16, true>(a, st, "ffn_gemv_gateup_bf16")
+                                : launch<kDown, MOE_BF16, true>(a, st, "ffn_gemv_down_bf16");
+        return r;
     }
-    return r;
+    if (w == MOE_INT4_G128 && act == MOE_BF16) {
+        r = ffn_gemv_deep(a, mode, MOE_INT4_G128, st);
+        if (r == MOE_EDTYPE) r = ffn_gemv_ks(a, mode, MOE_INT4_G128, st);
+        if (r == MOE_EDTYPE)
+            r = mode == kGateUp ? launch<kGateUp, MOE_INT4_G128, true>(a, st, "ffn_gemv_gateup_int4")
+                                : launch<kDown, MOE_INT4_G128, true>(a, st, "ffn_gemv_down_int4");
+        return r;
+    }
+    if (w == MOE_F32 && act == MOE_F32)
+        return mode == kGateUp ? launch<kGateUp, MOE_F32, false>(a, st, "ffn_gemv_gateup_f32")
+                               : launch<kDown, MOE_F32, false>(a, st, "ffn_gemv_down_f32");
+    return set_error(MOE_EDTYPE, "moe_expert_ffn_grouped: unsupported act/weight dtypes (%d,%d)", (int)act, (int)w);
+}
+
+moe_status ffn_gemv(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st) {
+    moe_status r = ffn_gemv_proj(a, act, w, kGateUp, st);
+    if (r != MOE_OK) return r;
+    return ffn_gemv_proj(a, act, w, kDown, st);
 }
 
 }  // namespace moe

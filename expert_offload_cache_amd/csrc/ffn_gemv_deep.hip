@@ -88,7 +88,7 @@ __global__ __launch_bounds__(64 * S * GR) void ffn_gemv_deep_kernel(FfnArgs a) {
     const int ks_base = si * NS;
 
     int e, chunk;
-    if (!find_work(a.counts, a.E, a.T, 16, a.shared_w != nullptr, blockIdx.y, e, chunk)) return;
+    if (!find_work(a.counts, a.E, a.T, 16, a.shared_w != nullptr, blockIdx.y, e, chunk, a.n_lo, a.n_hi)) return;
     const bool shared = (e == -1);
     const int nt = __builtin_amdgcn_readfirstlane(shared ? a.T : a.counts[e]);  // 1 .. kDeepTok
     const int p0 = __builtin_amdgcn_readfirstlane(shared ? a.T * a.k : a.offsets[e]);

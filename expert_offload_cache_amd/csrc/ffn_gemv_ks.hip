@@ -84,7 +84,7 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
     constexpr int kStep = IL ? S : 1;
 
     int e, chunk;
-    if (!find_work(a.counts, a.E, a.T, NTG, a.shared_w != nullptr, blockIdx.y, e, chunk)) return;
+    if (!find_work(a.counts, a.E, a.T, NTG, a.shared_w != nullptr, blockIdx.y, e, chunk, a.n_lo, a.n_hi)) return;
     const bool shared = (e == -1);
     const int n_all = __builtin_amdgcn_readfirstlane(shared ? a.T : a.counts[e]);
     const int i0 = chunk * NTG;  // this item's tokens: i0 .. i0 + nt - 1

@@ -110,7 +110,7 @@ __global__ __launch_bounds__(512) void ffn_mfma_int4_kernel(FfnArgs a) {
     const int ng = K / 128;    // int4 groups (fragments per row block)
 
     int e, chunk;
-    if (!find_work(a.counts, a.E, a.T, NT, a.shared_w != nullptr, blockIdx.y, e, chunk)) return;
+    if (!find_work(a.counts, a.E, a.T, NT, a.shared_w != nullptr, blockIdx.y, e, chunk, a.n_lo, a.n_hi)) return;
     const bool shared = e == -1;
     const int n_all = __builtin_amdgcn_readfirstlane(shared ? a.T : a.counts[e]);
     const int t0 = chunk * NT;
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(512) void ffn_mfma_areg_kernel(FfnArgs a) {
     const int nks = K / kKT;
 
     int e, chunk;
-    if (!find_work(a.counts, a.E, a.T, NT, a.shared_w != nullptr, blockIdx.y, e, chunk)) return;
+    if (!find_work(a.counts, a.E, a.T, NT, a.shared_w != nullptr, blockIdx.y, e, chunk, a.n_lo, a.n_hi)) return;
     const bool shared = e == -1;
     const int n_all = __builtin_amdgcn_readfirstlane(shared ? a.T : a.counts[e]);
     const int t0 = chunk * NT;
@@ -437,9 +437,9 @@ moe_status launch_int4(const FfnArgs& a, hipStream_t st, const char* name) {
 #define MOE_MFMA4_R 4
 #endif
 
-// Many tokens per expert, bf16 activations, bf16 or int4 weights: the MFMA path.  Other cases
-// report MOE_EDTYPE ("not mine").
-moe_status ffn_mfma(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st) {
+// Many tokens per expert, bf16 activations, bf16 or int4 weights: the MFMA path, one projection
+// (mode kGateUp or kDown).  Other cases report MOE_EDTYPE ("not mine").
+moe_status ffn_mfma_proj(const FfnArgs& a, moe_dtype act, moe_dtype w, int mode, hipStream_t st) {
     constexpr int MT = MOE_MFMA_MT, NT = MOE_MFMA_NT, WM = MOE_MFMA_WM, R = MOE_MFMA_R;
     if (act != MOE_BF16 || a.T <= 64) return MOE_EDTYPE;
     if (w == MOE_INT4_G128) {
@@ -447,15 +447,19 @@ moe_status ffn_mfma(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st
         // the raw fragments of two groups and the dequantised operands within 256 registers
         constexpr int MT4 = MOE_MFMA4_MT, R4 = MOE_MFMA4_R;
         if ((2 * a.f) % MT4 || a.d % MT4) return MOE_EDTYPE;
-        moe_status r = launch_int4<kGateUp, MT4, NT, WM, R4>(a, st, "ffn_mfma_gateup_int4");
-        if (r != MOE_OK) return r;
+        if (mode == kGateUp) return launch_int4<kGateUp, MT4, NT, WM, R4>(a, st, "ffn_mfma_gateup_int4");
         return launch_int4<kDown, MT4, NT, WM, R4>(a, st, "ffn_mfma_down_int4");
     }
     if (w != MOE_BF16) return MOE_EDTYPE;
     if ((2 * a.f) % MT || a.d % MT) return MOE_EDTYPE;
-    moe_status r = launch_areg<kGateUp, MT, NT, WM, R>(a, st, "ffn_mfma_gateup_bf16");
-    if (r != MOE_OK) return r;
+    if (mode == kGateUp) return launch_areg<kGateUp, MT, NT, WM, R>(a, st, "ffn_mfma_gateup_bf16");
     return launch_areg<kDown, MT, NT, WM, R>(a, st, "ffn_mfma_down_bf16");
+}
+
+moe_status ffn_mfma(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st) {
+    moe_status r = ffn_mfma_proj(a, act, w, kGateUp, st);
+    if (r != MOE_OK) return r;
+    return ffn_mfma_proj(a, act, w, kDown, st);
 }
 
 }  // namespace moe

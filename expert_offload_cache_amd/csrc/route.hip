@@ -325,6 +325,9 @@ __device__ void select_and_gate(const float* s_logit, int E, int k, const int32_
 }
 
 // one block per token, logits already in global memory
+// above this many tokens the wave-per-token selection (route_topk_wave) runs instead
+constexpr int kWaveTopkMinT = 64;
+
 __global__ __launch_bounds__(1024) void route_topk(const float* __restrict__ logits, int T, int E, int k,
                                                   const int32_t* __restrict__ forced,
                                                   int32_t* __restrict__ topk_idx,
@@ -337,6 +340,76 @@ __global__ __launch_bounds__(1024) void route_topk(const float* __restrict__ log
     __syncthreads();
     select_and_gate(s_logit, E, k, forced ? forced + (size_t)t * k : nullptr, s_sel, s_val,
                     topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
+}
+
+// Many tokens (prefill): one wave per token, four tokens a workgroup.  The wave holds the token's
+// logits, EPL a lane (lane l: experts l, l + 64, ...), and takes the k best in k rounds: each lane
+// proposes its best expert not yet taken, a butterfly over the 64 lanes keeps the better of each
+// pair (larger logit, equal logits -> lower id: `better`, a strict total order, so every lane ends
+// with the same winner), lane r keeps round r's winner and its owner marks it taken.  Round r's
+// winner is the expert ranked r, so the ids are route_topk's.  Gates as select_and_gate: lane j forms
+// exp(v_j - max) in binary64, every lane sums the k terms in ascending j, one rounding.  Needs
+// k <= 64.  A block per token keeps its barriers and a thousand threads busy for one selection;
+// here one wave does it without LDS or barriers, which is what a batch of thousands of tokens needs.
+template <int EPL>
+__global__ __launch_bounds__(256) void route_topk_wave(const float* __restrict__ logits, int T, int E, int k,
+                                                       const int32_t* __restrict__ forced,
+                                                       int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;  // the whole wave
+    const float* row = logits + (size_t)t * E;
+    int sel_id = 0;
+    float sel_v = 0.f;
+    if (forced) {
+        if (lane < k) {
+            sel_id = forced[(size_t)t * k + lane];
+            sel_v = row[min(max(sel_id, 0), E - 1)];
+        }
+    } else {
+        float v[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane + 64 * i;
+            v[i] = e < E ? row[e] : 0.f;
+        }
+        uint32_t taken = 0;
+        for (int r = 0; r < k; ++r) {
+            float bv = 0.f;
+            int bi = -1;  // -1: no candidate
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int e = lane + 64 * i;
+                if (e < E && !((taken >> i) & 1u) && (bi < 0 || better(v[i], e, bv, bi))) {
+                    bv = v[i];
+                    bi = e;
+                }
+            }
+#pragma unroll
+            for (int sh = 1; sh < 64; sh <<= 1) {
+                const float ov = __shfl_xor(bv, sh, 64);
+                const int oi = __shfl_xor(bi, sh, 64);
+                if (oi >= 0 && (bi < 0 || better(ov, oi, bv, bi))) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            if (lane == r) {
+                sel_id = bi;
+                sel_v = bv;
+            }
+            if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        }
+    }
+    double m = -INFINITY;
+    for (int i = 0; i < k; ++i) m = fmax(m, (double)__shfl(sel_v, i, 64));
+    const double term = lane < k ? exp((double)sel_v - m) : 0.0;
+    double den = 0.0;
+    for (int i = 0; i < k; ++i) den += __shfl(term, i, 64);
+    if (lane < k) {
+        topk_idx[(size_t)t * k + lane] = sel_id;
+        topk_w[(size_t)t * k + lane] = (float)(term / den);
+    }
 }
 
 // For one token (batch-1 decode) one block selects and gates (select_and_gate, as route_topk) and
@@ -544,6 +617,18 @@ moe_status launch_route_logits(const void* x, bool bf, int T, int d, const void*
 moe_status launch_route_topk(const float* logits, int T, int E, int k, const int32_t* forced_idx,
                              int32_t* topk_idx, float* topk_w, hipStream_t st) {
     ProfScope p("route_topk", st);
+    if (T > kWaveTopkMinT && k <= 64) {
+        // many tokens: a wave per token (E <= 1024 holds 16 logits a lane at most)
+        const unsigned blocks = (unsigned)((T + 3) / 4);
+#define RTW(N) route_topk_wave<N><<<blocks, 256, 0, st>>>(logits, T, E, k, forced_idx, topk_idx, topk_w)
+        if (E <= 64) RTW(1);
+        else if (E <= 128) RTW(2);
+        else if (E <= 256) RTW(4);
+        else if (E <= 512) RTW(8);
+        else RTW(16);
+#undef RTW
+        return check_launch("route_topk");
+    }
     // up to 4 threads per expert share its comparisons
     const int nth = std::min(1024, std::max(64, (E * 4 + 63) / 64 * 64));
     route_topk<<<T, nth, 0, st>>>(logits, T, E, k, forced_idx, topk_idx, topk_w);
@@ -571,7 +656,8 @@ extern "C" moe_status moe_route(const void* x, moe_dtype act, int T, int d, cons
 extern "C" moe_status moe_route_permute(const void* x, moe_dtype act, int T, int d, const void* w_router,
                                         const float* bias, int E, int k, const int32_t* forced_idx,
                                         int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts,
-                                        int32_t* offsets, int32_t* perm, int32_t* inv_perm, moe_stream s) {
+                                        int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws,
+                                        size_t ws_bytes, moe_stream s) {
     MOE_CHECK(T >= 0, MOE_ESHAPE, "moe_route_permute: T=%d < 0", T);
     if (T == 0) return moe_permute(nullptr, 0, k, E, counts, offsets, perm, inv_perm, nullptr, 0, s);
     moe_status r = check_route_args("moe_route_permute", x, act, T, d, w_router, E, k, topk_idx, topk_w, logits);
@@ -584,7 +670,7 @@ extern "C" moe_status moe_route_permute(const void* x, moe_dtype act, int T, int
     if (T > 1) {
         r = launch_route_topk(logits, T, E, k, forced_idx, topk_idx, topk_w, st);
         if (r != MOE_OK) return r;
-        return moe_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, nullptr, 0, s);
+        return moe_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, ws, ws_bytes, s);
     }
     // one token: the top-k block's threads, a power of two with 4 threads an expert (as route_topk)
     int nth = 64;

@@ -25,6 +25,44 @@ __device__ __forceinline__ uint64_t match_mask(int e, int nbits, uint64_t active
     return m;
 }
 
+// One wave counts the pairs [lo, hi) per expert into its own LDS row my_run (within a wave, equal ids
+// are found with ballots over the id bits; one lane per distinct id writes).
+__device__ __forceinline__ void count_stretch(const int32_t* ids, int lo, int hi, int E, int nbits, int32_t* my_run) {
+    const int lane = threadIdx.x & 63;
+    for (int b = lo; b < hi; b += 64) {
+        const int i = b + lane;
+        const bool act = i < hi;
+        const uint64_t active = __ballot(act);
+        const int e = act ? min(max(ids[i], 0), E - 1) : 0;
+        const uint64_t m = match_mask(e, nbits, active);
+        if (act && (m >> lane) == 1ull) my_run[e] += __popcll(m);  // highest lane of its group
+    }
+}
+
+// One wave places the pairs [lo, hi) in order: pair i goes to my_run[e] + (equal ids on lower lanes of
+// the same batch), and the run starts advance.
+__device__ __forceinline__ void place_stretch(const int32_t* ids, int lo, int hi, int E, int nbits, int32_t* my_run,
+                                              int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int b = lo; b < hi; b += 64) {
+        const int i = b + lane;
+        const bool act = i < hi;
+        const uint64_t active = __ballot(act);
+        const int e = act ? min(max(ids[i], 0), E - 1) : 0;
+        const uint64_t m = match_mask(e, nbits, active);
+        if (act) {
+            const int pos = my_run[e] + __popcll(m & lt);
+            perm[pos] = i;
+            inv_perm[i] = pos;
+        }
+        // every lane has read its run start before the group's last lane advances it
+        __builtin_amdgcn_wave_barrier();
+        if (act && (m >> lane) == 1ull) my_run[e] += __popcll(m);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 // Stable counting sort of the N flat pair ids t*k + j by expert id ids[i], run by one workgroup
 // of WAVES waves, without atomics on positions (so the result is deterministic):
 //   1. wave w owns a contiguous stretch of pairs and counts it per expert into its own LDS row
@@ -48,18 +86,10 @@ __device__ void permute_block(const int32_t* ids, int N, int E, int nbits, int32
 
     const int per = ((N + WAVES - 1) / WAVES + 63) / 64 * 64;  // stretch length, whole batches
     const int lo = min(N, w * per), hi = min(N, lo + per);
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int32_t* my_run = run + w * E;
 
     // 1. per-wave counts
-    for (int b = lo; b < hi; b += 64) {
-        const int i = b + lane;
-        const bool act = i < hi;
-        const uint64_t active = __ballot(act);
-        const int e = act ? min(max(ids[i], 0), E - 1) : 0;
-        const uint64_t m = match_mask(e, nbits, active);
-        if (act && (m >> lane) == 1ull) my_run[e] += __popcll(m);  // highest lane of its group
-    }
+    count_stretch(ids, lo, hi, E, nbits, my_run);
     __syncthreads();
 
     // 2. counts and offsets: thread tid owns experts [tid*EPT, tid*EPT + EPT)
@@ -103,22 +133,7 @@ __device__ void permute_block(const int32_t* ids, int N, int E, int nbits, int32
     __syncthreads();
 
     // 3. stable scatter
-    for (int b = lo; b < hi; b += 64) {
-        const int i = b + lane;
-        const bool act = i < hi;
-        const uint64_t active = __ballot(act);
-        const int e = act ? min(max(ids[i], 0), E - 1) : 0;
-        const uint64_t m = match_mask(e, nbits, active);
-        if (act) {
-            const int pos = my_run[e] + __popcll(m & lt);
-            perm[pos] = i;
-            inv_perm[i] = pos;
-        }
-        // every lane has read its run start before the group's last lane advances it
-        __builtin_amdgcn_wave_barrier();
-        if (act && (m >> lane) == 1ull) my_run[e] += __popcll(m);
-        __builtin_amdgcn_wave_barrier();
-    }
+    place_stretch(ids, lo, hi, E, nbits, my_run, perm, inv_perm);
 }
 
 }  // namespace moe

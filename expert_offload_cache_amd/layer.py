@@ -8,7 +8,8 @@ from typing import Optional
 
 import numpy as np
 
-from . import combine, expert_ffn_grouped, pack_expert, route_permute, slot_bytes, workspace_bytes, WDT
+from . import (combine, expert_ffn_grouped, pack_expert, permute_workspace, route_permute, slot_bytes, workspace_bytes,
+               WDT)
 from ._lib import MOE_BF16, MOE_F32
 
 
@@ -91,16 +92,17 @@ class DeviceLayer:
                    torch.empty(E + 1, **i32), torch.empty(T * k, **i32), torch.empty(T * k, **i32)),
             y_perm=torch.empty((rows, d), dtype=torch.float32, device=dev),
             y=torch.empty((T, d), dtype=torch.bfloat16 if self.act == "bf16" else torch.float32, device=dev),
-            ws=self.workspace(T))
+            ws=self.workspace(T), pws=permute_workspace(T, k, E, dev))
 
     def forward(self, x, forced_idx=None, ws=None, stream=None, slot_of_expert=None, bufs=None):
         """x: device tensor [T, d].  Returns a dict of every intermediate and y [T, d].  With
         `bufs` (from buffers(T)) the outputs are written there instead of new tensors."""
         T = x.shape[0]
         b = bufs or {}
+        pws = b["pws"] if "pws" in b else permute_workspace(T, self.k, self.E, x.device)
         idx, w, logits, counts, offsets, perm, inv = route_permute(x, self.w_router, self.bias, self.k,
                                                                   forced_idx=forced_idx, out=b.get("route"),
-                                                                  stream=stream)
+                                                                  stream=stream, ws=pws)
         if ws is None:
             ws = b["ws"] if "ws" in b else self.workspace(T)
         soe = self.slot_of_expert if slot_of_expert is None else slot_of_expert

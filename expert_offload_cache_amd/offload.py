@@ -19,8 +19,8 @@ from typing import Optional
 
 import numpy as np
 
-from . import (MoeError, SlotCache, combine, expert_ffn_grouped, hybrid_split, pack_expert, pinned_alloc,
-               pinned_free, route_permute, slot_bytes, workspace_bytes, WDT)
+from . import (MoeError, SlotCache, combine, expert_ffn_grouped, hybrid_split, pack_expert, permute_workspace,
+               pinned_alloc, pinned_free, route_permute, slot_bytes, workspace_bytes, WDT)
 from ._lib import MOE_BF16, MOE_F32
 from .layer import _expert_arrays, _to_device
 
@@ -173,7 +173,8 @@ class OffloadStack:
                       torch.empty(T * k, dtype=torch.int32, device=dev),
                       torch.empty(T * k, dtype=torch.int32, device=dev)),
                 y_perm=torch.empty((rows, d), dtype=torch.float32, device=dev),
-                y=torch.empty((T, d), dtype=torch.bfloat16 if self.wl.act == "bf16" else torch.float32, device=dev))
+                y=torch.empty((T, d), dtype=torch.bfloat16 if self.wl.act == "bf16" else torch.float32, device=dev),
+                pws=permute_workspace(T, k, E, dev))
         return self._bufs[T]
 
     def _layer(self, l: int, x, forced=None):
@@ -181,7 +182,7 @@ class OffloadStack:
         T = x.shape[0]
         b = self._buffers(T)
         idx, w, _, *perm = route_permute(x, self.w_router[l], self.bias[l], self.k, forced_idx=forced,
-                                         out=b["route"] + b["perm"], stream=self.compute)
+                                         out=b["route"] + b["perm"], stream=self.compute, ws=b["pws"])
         return idx, w, tuple(perm)
 
     def _experts(self, l: int, x, w, perm, table=None, do_combine: bool = True, with_shared: bool = True):

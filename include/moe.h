@@ -122,10 +122,16 @@ MOE_API moe_status moe_route(const void* x, moe_dtype act, int T, int d, const v
  *   counts[e] pairs routed to e; offsets[0..E] exclusive prefix sum (offsets[E] = T*k);
  *   perm[p] flat pair index at sorted position p (stable: ascending flat index within an
  *   expert); inv_perm[i] sorted position of flat pair i.  All int32, device.
- * topk_idx must hold ids in [0, E).  T*k <= 2^24.  ws/ws_bytes unused (may be NULL/0). */
+ * topk_idx must hold ids in [0, E).  T*k <= 2^24.  ws: device scratch of moe_permute_workspace_bytes
+ * bytes (4-byte aligned) or NULL/0, see below. */
 MOE_API moe_status moe_permute(const int32_t* topk_idx, int T, int k, int E, int32_t* counts,
                                int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws,
                                size_t ws_bytes, moe_stream s);
+/* Device scratch moe_permute (and moe_route_permute) can use for T*k pairs over E experts: the
+ * per-workgroup counts of a sort split over several workgroups, used when T*k is large (more than
+ * 8192 pairs).  0 when one workgroup sorts.  With a smaller or NULL ws the call still works (one
+ * workgroup sorts); the results are the same bits either way. */
+MOE_API size_t moe_permute_workspace_bytes(int T, int k, int E);
 
 /* ------------------------------------------------------------------------------------------
  * moe_route_permute -- moe_route followed by moe_permute on its topk_idx, as one call
@@ -133,13 +139,15 @@ MOE_API moe_status moe_permute(const int32_t* topk_idx, int T, int k, int E, int
  * the runtime gathers each expert's tokens).  Every output is bitwise what the two calls give
  * for the same arguments: logits, topk_idx, topk_w as moe_route; counts, offsets, perm,
  * inv_perm as moe_permute.  For T = 1 one block selects, gates and places the k pairs by expert,
- * one launch fewer than the two calls; other shapes run the two calls' kernels.  Arguments, shapes,
- * ownership and errors are those of the two calls; a non-OK status means nothing was enqueued.
+ * one launch fewer than the two calls; other shapes run the two calls' kernels (ws and ws_bytes
+ * go to moe_permute).  Arguments, shapes, ownership and errors are those of the two calls; a
+ * non-OK status means nothing was enqueued.
  * With T = 0 only counts and offsets are written (zeros). */
 MOE_API moe_status moe_route_permute(const void* x, moe_dtype act, int T, int d, const void* w_router,
                                      const float* bias, int E, int k, const int32_t* forced_idx,
                                      int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts,
-                                     int32_t* offsets, int32_t* perm, int32_t* inv_perm, moe_stream s);
+                                     int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws,
+                                     size_t ws_bytes, moe_stream s);
 
 /* ------------------------------------------------------------------------------------------
  * moe_expert_ffn_grouped -- every expert with n_e > 0 runs once on its n_e rows (SwiGLU, the
@@ -158,6 +166,12 @@ MOE_API moe_status moe_route_permute(const void* x, moe_dtype act, int T, int d,
  *   first use.  Its first 4 bytes are a sticky int32 status word (0 = no error).
  * Intermediate h is rounded to bf16 when act is BF16 (binary32 when act is F32). */
 #define MOE_SLOT_ELSEWHERE (-2)
+/* Above 64 tokens (prefill) the experts run on the matrix-core grouped GEMM, which feeds int4
+ * weights to the matrix cores as bf16(q * s).  Experts holding at most moe_prefill_gemv_tokens(w)
+ * tokens instead run on the decode kernels (their weights are streamed once and no 128-token tile
+ * is left mostly empty); those take exact q * s products.  The shared expert always holds T tokens.
+ * 0 = every expert on the GEMM. */
+MOE_API int moe_prefill_gemv_tokens(moe_dtype w);
 MOE_API size_t moe_workspace_bytes(int T, int d, int f, int E, int k, int has_shared,
                                    moe_dtype act, moe_dtype w);
 MOE_API moe_status moe_expert_ffn_grouped(const void* x, moe_dtype act, int T, int d, int f, int E,

@@ -61,17 +61,23 @@ def test_host_validation_needs_no_gpu(moe):
     assert L.moe_route(None, 1, 4, 128, vp, None, 8, 2, None, vp, vp, vp, None) == moe._lib.MOE_EINVAL
     assert b"NULL" in L.moe_last_error()
     assert L.moe_permute(vp, 4, 2, 2000, vp, vp, vp, vp, None, 0, None) == moe._lib.MOE_ESHAPE
+    # prefill experts with few tokens run on the decode kernels: a threshold per weight type
+    assert 0 <= L.moe_prefill_gemv_tokens(2) < 1000 and L.moe_prefill_gemv_tokens(0) == 0
+    # the split sort's scratch: none for few pairs, one int32 per (workgroup, expert) for many
+    assert L.moe_permute_workspace_bytes(64, 8, 128) == 0
+    assert L.moe_permute_workspace_bytes(8192, 6, 256) == 24 * 256 * 4
+    assert L.moe_permute_workspace_bytes(8192, 6, 2000) == 0
     # route + permute in one call: the route checks, then the permute buffers
     rp = L.moe_route_permute
-    assert rp(vp, 1, -1, 128, vp, None, 8, 2, None, vp, vp, vp, vp, vp, vp, vp, None) == moe._lib.MOE_ESHAPE
-    assert rp(vp, 1, 4, 100, vp, None, 8, 2, None, vp, vp, vp, vp, vp, vp, vp, None) == moe._lib.MOE_ESHAPE
-    assert rp(vp, 1, 4, 128, vp, None, 8, 9, None, vp, vp, vp, vp, vp, vp, vp, None) == moe._lib.MOE_ESHAPE
-    assert rp(vp, 7, 4, 128, vp, None, 8, 2, None, vp, vp, vp, vp, vp, vp, vp, None) == moe._lib.MOE_EDTYPE
-    assert rp(vp, 1, 4, 128, None, None, 8, 2, None, vp, vp, vp, vp, vp, vp, vp, None) == moe._lib.MOE_EINVAL
-    assert rp(vp, 1, 4, 128, vp, None, 8, 2, None, vp, vp, vp, vp, vp, None, vp, None) == moe._lib.MOE_EINVAL
+    assert rp(vp, 1, -1, 128, vp, None, 8, 2, None, vp, vp, vp, vp, vp, vp, vp, None, 0, None) == moe._lib.MOE_ESHAPE
+    assert rp(vp, 1, 4, 100, vp, None, 8, 2, None, vp, vp, vp, vp, vp, vp, vp, None, 0, None) == moe._lib.MOE_ESHAPE
+    assert rp(vp, 1, 4, 128, vp, None, 8, 9, None, vp, vp, vp, vp, vp, vp, vp, None, 0, None) == moe._lib.MOE_ESHAPE
+    assert rp(vp, 7, 4, 128, vp, None, 8, 2, None, vp, vp, vp, vp, vp, vp, vp, None, 0, None) == moe._lib.MOE_EDTYPE
+    assert rp(vp, 1, 4, 128, None, None, 8, 2, None, vp, vp, vp, vp, vp, vp, vp, None, 0, None) == moe._lib.MOE_EINVAL
+    assert rp(vp, 1, 4, 128, vp, None, 8, 2, None, vp, vp, vp, vp, vp, None, vp, None, 0, None) == moe._lib.MOE_EINVAL
     assert b"moe_route_permute" in L.moe_last_error()
-    assert rp(vp, 1, 4, 128, vp, None, 8, 2, None, vp, vp, vp, vp, vp, vp, None, None) == moe._lib.MOE_EINVAL
-    assert rp(vp, 1, 0, 128, vp, None, 2000, 2, None, vp, vp, vp, vp, vp, vp, vp, None) == moe._lib.MOE_ESHAPE
+    assert rp(vp, 1, 4, 128, vp, None, 8, 2, None, vp, vp, vp, vp, vp, vp, None, None, 0, None) == moe._lib.MOE_EINVAL
+    assert rp(vp, 1, 0, 128, vp, None, 2000, 2, None, vp, vp, vp, vp, vp, vp, vp, None, 0, None) == moe._lib.MOE_ESHAPE
     assert L.moe_combine(vp, vp, vp, 4, 2, 6, 0, vp, 1, None) == moe._lib.MOE_ESHAPE
     a = ctypes.c_void_p(256)
     # int4 weights need bf16 activations; dense weights must match the activation dtype

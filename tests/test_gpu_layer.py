@@ -52,6 +52,10 @@ def _check_experts_whole(out, x, wl, experts, shared, T, tight=None, int4_bf16=F
     groups = [(int(e), perm[off[e]:off[e + 1]] // wl.k, yp_all[off[e]:off[e + 1]], experts[int(e)]) for e in pick]
     if shared is not None:
         groups.append((-1, np.arange(T), yp_all[T * wl.k:T * wl.k + T], shared))
+    # experts the library runs on the decode kernels (few tokens) take exact q*s products
+    from expert_offload_cache_amd._lib import lib, MOE_INT4_G128
+
+    gemv_max = lib().moe_prefill_gemv_tokens(MOE_INT4_G128) if int4_bf16 else 0
     worst, worst_t, errs, errs_t = 0.0, 0.0, [], []
     for e, toks, yp, ew in groups:
         y = yp.cpu().numpy().astype(np.float64)
@@ -60,7 +64,8 @@ def _check_experts_whole(out, x, wl, experts, shared, T, tight=None, int4_bf16=F
         errs.append(err)
         assert err.max() <= 2e-2, (e, len(toks), err.max())
         if tight is not None:
-            ref = swiglu_expert(xf[toks], *expert_to_f64(ew, int4_bf16=int4_bf16), h_bf16=True)
+            on_gemm = int4_bf16 and (e == -1 or len(toks) > gemv_max)
+            ref = swiglu_expert(xf[toks], *expert_to_f64(ew, int4_bf16=on_gemm), h_bf16=True)
             et = rel_err_per_token(y, ref)
             worst_t = max(worst_t, float(et.max()))
             errs_t.append(et)

@@ -87,6 +87,10 @@ PERM_CASES = [
     (1, 8, 2, "rand"), (16, 8, 2, "rand"), (64, 128, 8, "rand"), (1, 256, 6, "rand"), (333, 256, 6, "rand"),
     (8192, 256, 6, "rand"), (1000, 1024, 8, "rand"), (4096, 64, 1, "one"), (700, 5, 5, "all"),
     (8192, 256, 6, "zipf"),
+    # beyond 8192 pairs with a workspace: the sort split over workgroups (ragged last workgroup,
+    # one expert holding every pair, every expert in every token, a thousand experts)
+    (2048, 256, 6, "zipf"), (3001, 7, 3, "rand"), (12000, 64, 1, "one"), (700, 16, 16, "all"),
+    (1500, 1024, 8, "rand"), (40000, 256, 6, "zipf"),
 ]
 
 
@@ -96,6 +100,7 @@ def test_permute_bit_exact(T, E, k, kind):
     import expert_offload_cache_amd as moe
 
     print(f"permute T={T} E={E} k={k} {kind}", flush=True)
+    ws = moe.permute_workspace(T, k, E, "cuda")
     if kind == "rand":
         idx = synth.forced_topk(T, T, E, k)
     elif kind == "one":
@@ -106,11 +111,13 @@ def test_permute_bit_exact(T, E, k, kind):
         tr = synth.routing_trace(0, T, 1, E, k, p_reuse=0.0)  # independent Zipf draws per token
         idx = np.ascontiguousarray(tr[:, 0, :])
     c, o, p, ip = o_permute(idx, E)
-    gc, go, gp, gip = moe.permute(to_dev(idx, "i32"), E)
-    assert np.array_equal(gc.cpu().numpy(), c)
-    assert np.array_equal(go.cpu().numpy(), o)
-    assert np.array_equal(gp.cpu().numpy(), p)
-    assert np.array_equal(gip.cpu().numpy(), ip)
+    for w in ([None] if ws is None else [None, ws]):  # one workgroup, and the split sort
+        gc, go, gp, gip = moe.permute(to_dev(idx, "i32"), E, ws=w)
+        assert np.array_equal(gc.cpu().numpy(), c)
+        assert np.array_equal(go.cpu().numpy(), o)
+        assert np.array_equal(gp.cpu().numpy(), p)
+        assert np.array_equal(gip.cpu().numpy(), ip)
+    assert (ws is not None) == (T * k > 8192)
 
 
 RP_CASES = [
@@ -154,6 +161,16 @@ RP_CASES = [
     ("bf16", 1024, 512, 16, 1, 1.1, "rand"),
     ("bf16", 2048, 100, 4, 1, None, "rand"),
     ("bf16", 1024, 256, 8, 64, 1.1, "rand"),
+    # more than 64 tokens: a wave per token selects (ties, equal logits, replayed ids, k = 64 of
+    # 1024, ragged E), and beyond 8192 pairs the sort is split over workgroups
+    ("bf16", 256, 64, 8, 100, None, "ties"),
+    ("bf16", 256, 64, 8, 100, None, "flat"),
+    ("bf16", 4096, 256, 6, 300, 1.1, "forced"),
+    ("bf16", 512, 1024, 64, 70, 1.1, "rand"),
+    ("bf16", 512, 1000, 16, 80, None, "rand"),
+    ("bf16", 512, 40, 40, 66, 1.1, "rand"),
+    ("bf16", 4096, 256, 6, 2048, 1.1, "rand"),
+    ("f32", 128, 8, 2, 4500, None, "rand"),
 ]
 
 
@@ -181,8 +198,9 @@ def test_route_permute_matches_the_two_calls_and_the_oracle(act, d, E, k, T, bia
     xd, wd = to_dev(x, act), to_dev(w, act)
     bd = None if b is None else to_dev(b, "f32")
     fd = None if forced is None else to_dev(forced, "i32")
-    out = moe.route_permute(xd, wd, bd, k, forced_idx=fd)
-    moe.route_permute(xd, wd, bd, k, forced_idx=fd, out=out)  # again into the same buffers
+    pws = moe.permute_workspace(T, k, E, "cuda")
+    out = moe.route_permute(xd, wd, bd, k, forced_idx=fd, ws=pws)
+    moe.route_permute(xd, wd, bd, k, forced_idx=fd, out=out, ws=pws)  # again into the same buffers
     got = [a.cpu().numpy() for a in out]
     gi, gw, gl = moe.route(xd, wd, bd, k, forced_idx=fd)
     two = [gi, gw, gl] + list(moe.permute(gi, E))
