@@ -1,6 +1,8 @@
 // Internal interface between the moe_expert_ffn_grouped dispatcher and its kernels.
 #pragma once
 
+#include <algorithm>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -27,6 +29,17 @@ enum { kGateUp = 0, kDown = 1 };  // the two projections of a grouped call
 
 constexpr size_t kWsHeader = 256;
 constexpr size_t kPlanBytes = 1 << 16;
+
+// Upper bound on the work items (expert, chunk of ntg tokens) of a launch over the experts in
+// [n_lo, n_hi] (grid rows; the items past the real count exit at once).
+inline int64_t work_items(const FfnArgs& a, int ntg) {
+    const int64_t tk = (int64_t)a.T * a.k;
+    const int64_t nexp = std::min<int64_t>(std::min<int64_t>(a.E, tk), tk / std::max(a.n_lo, 1));
+    int64_t routed = (tk + ntg - 1) / ntg + nexp;
+    if (a.n_hi < (1 << 30)) routed = std::min<int64_t>(routed, nexp * ((a.n_hi + ntg - 1) / ntg));
+    const bool sh = a.shared_w && a.T >= a.n_lo && a.T <= a.n_hi;
+    return routed + (sh ? (a.T + ntg - 1) / ntg : 0);
+}
 
 // Argument checks of moe_expert_ffn_grouped except the workspace; fills every field of `a` but
 // status, plan and h (left NULL).  T == 0 returns MOE_OK with nothing to run.  `fn` names the

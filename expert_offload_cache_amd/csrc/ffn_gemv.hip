@@ -274,9 +274,7 @@ moe_status launch(const FfnArgs& a, hipStream_t st, const char* name) {
     const Plan p = plan_for(MODE, W, M, K, Frag<W>::kIn, kBf16Act ? 2 : 4, a.T);
     if (!p.fpw || p.lds > 65536) return set_error(MOE_ESHAPE, "%s: K=%d too large for this kernel", name, K);
     // work items: sum over experts of ceil(n_e / ntg) <= T*k/ntg + min(E, T*k), plus the shared chunks
-    const int64_t tk = (int64_t)a.T * a.k;
-    const int64_t items = (tk + p.ntg - 1) / p.ntg + std::min<int64_t>(a.E, tk) +
-                          (a.shared_w ? (a.T + p.ntg - 1) / p.ntg : 0);
+    const int64_t items = work_items(a, p.ntg);
     if (items > 65535) return set_error(MOE_ESHAPE, "%s: %lld work items exceed one launch", name, (long long)items);
     dim3 grid((unsigned)(M / 16 / p.rb), (unsigned)items);
     if constexpr (MODE == kDown) {

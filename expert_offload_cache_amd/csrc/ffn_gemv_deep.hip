@@ -283,8 +283,7 @@ moe_status launch_deep(const FfnArgs& a, hipStream_t st, const char* name) {
     const int K = (MODE == kGateUp) ? a.d : a.f;
     const int per_wave = (MODE == kGateUp) ? RA / 2 : RA;
     if (a.T > kDeepTok || K % KIN != 0 || K / KIN != S * NS || (M / 16) % (per_wave * GR) != 0) return MOE_EDTYPE;
-    const int64_t tk = (int64_t)a.T * a.k;
-    const int64_t items = std::min<int64_t>(a.E, tk) + (a.shared_w ? 1 : 0);
+    const int64_t items = work_items(a, 16);
     const size_t xbytes = (size_t)S * (((size_t)std::min(a.T, kDeepTok) * NS * KIN * 2 + 1023) / 1024 * 1024);
     const size_t jbytes = S > 1 ? (size_t)S * GR * RA * 1024 : 0;
     const size_t lds = std::max(xbytes, jbytes);

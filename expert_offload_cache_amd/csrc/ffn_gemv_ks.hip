@@ -323,8 +323,7 @@ static moe_status launch_ks(const FfnArgs& a, hipStream_t st, const char* name) 
     if ((M / 16) % (per_wave * groups) != 0 || (K / KsFrag<W>::kIn) % S != 0) return MOE_EDTYPE;
     if (XL && (a.T > kXlTok || (size_t)kXlTok * K * 2 > 65536)) return MOE_EDTYPE;
     const int ntg = 16 * G;
-    const int64_t tk = (int64_t)a.T * a.k;
-    const int64_t items = (tk + ntg - 1) / ntg + std::min<int64_t>(a.E, tk) + (a.shared_w ? (a.T + ntg - 1) / ntg : 0);
+    const int64_t items = work_items(a, ntg);
     if (items > 65535) return set_error(MOE_ESHAPE, "%s: %lld work items exceed one launch", name, (long long)items);
     dim3 grid((unsigned)(M / 16 / (per_wave * groups)), (unsigned)items), block(64 * kKsWaves);
     // staged rows: as many as an item can hold (min(T, kXlTok)); then the S-way join buffer

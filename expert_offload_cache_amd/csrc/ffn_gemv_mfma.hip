@@ -237,8 +237,7 @@ moe_status launch(const FfnArgs& a, hipStream_t st, const char* name) {
     if (!p.fpw) return set_error(MOE_ESHAPE, "%s: K=%d too large for this kernel", name, K);
     // work items: sum over experts of ceil(n_e / ntg) <= T*k/ntg + min(E, T*k), plus the shared chunks
     const int ntg = 16 * p.g;
-    const int64_t tk = (int64_t)a.T * a.k;
-    const int64_t items = (tk + ntg - 1) / ntg + std::min<int64_t>(a.E, tk) + (a.shared_w ? (a.T + ntg - 1) / ntg : 0);
+    const int64_t items = work_items(a, ntg);
     if (items > 65535) return set_error(MOE_ESHAPE, "%s: %lld work items exceed one launch", name, (long long)items);
     dim3 grid((unsigned)(M / 16 / p.rb), (unsigned)items);
     if constexpr (MODE == kDown) {

@@ -390,8 +390,7 @@ template <int MODE, int MT, int NT, int WM, int R>
 moe_status launch_areg(const FfnArgs& a, hipStream_t st, const char* name) {
     using TL = Tile4<MT, NT, WM, R>;
     const int M = (MODE == kGateUp) ? 2 * a.f : a.d;
-    const int64_t tk = (int64_t)a.T * a.k;
-    const int64_t items = (tk + NT - 1) / NT + std::min<int64_t>(a.E, tk) + (a.shared_w ? (a.T + NT - 1) / NT : 0);
+    const int64_t items = work_items(a, NT);
     if (items > 65535) return set_error(MOE_ESHAPE, "%s: %lld token tiles exceed one launch", name, (long long)items);
     auto kern = ffn_mfma_areg_kernel<MODE, MT, NT, WM, R>;
     MOE_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, TL::kLds));
@@ -405,8 +404,7 @@ template <int MODE, int MT, int NT, int WM, int R>
 moe_status launch_int4(const FfnArgs& a, hipStream_t st, const char* name) {
     using TL = Tile4<MT, NT, WM, R>;
     const int M = (MODE == kGateUp) ? 2 * a.f : a.d;
-    const int64_t tk = (int64_t)a.T * a.k;
-    const int64_t items = (tk + NT - 1) / NT + std::min<int64_t>(a.E, tk) + (a.shared_w ? (a.T + NT - 1) / NT : 0);
+    const int64_t items = work_items(a, NT);
     if (items > 65535) return set_error(MOE_ESHAPE, "%s: %lld token tiles exceed one launch", name, (long long)items);
     auto kern = ffn_mfma_int4_kernel<MODE, MT, NT, WM, R>;
     MOE_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, TL::kLds));
