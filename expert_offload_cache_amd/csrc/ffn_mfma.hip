@@ -12,12 +12,14 @@
 // one expert; each wave owns 64 rows x 128 tokens.  In the gate/up launch a wave's 64 rows are 32
 // gate rows and the same 32 up rows, so SwiGLU is applied in registers before one bf16 store of h.
 // Inputs advance 32 at a time.  Each wave loads its own weight fragments (4 x 1 KB a stage, one
-// 16-byte load per lane each, already in A-operand order) straight into registers, R-1 stages
+// 16-byte load per lane each, already in A-operand order) straight into registers, R stages
 // ahead; the token rows are gathered through the permutation straight into B fragments in a ring
 // of R LDS stages filled by direct-to-LDS loads (global_load_lds_dwordx4), shared by the 8 waves.
 // So the LDS carries only the token fragments (written once, read by every wave as conflict-free
 // 16-byte lane reads) -- measured against staging the weights in LDS too, this lifts the dense
-// contraction from 0.43 to 0.46 of the MFMA peak and moves the same bits.
+// contraction from 0.43 to 0.46 of the MFMA peak and moves the same bits.  Measured and dropped:
+// 3 to 6 stages of lead (no gain beyond 3), two 4-wave workgroups per CU with 256-row tiles (0.47
+// -> 0.32 dense), 256 x 256 tiles (0.39).
 // int4 weights use a 256-row variant that dequantises in registers (below).
 // Workgroup (m, n) follows (m, n-1) M/MT blocks later in dispatch order; blocks go round-robin
 // over the 8 XCDs, so where M/MT is a multiple of 8 (the large shapes) an expert's weight tile
@@ -29,6 +31,7 @@
 #include "ffn.h"
 #include "ffn_common.h"
 #include "slot_layout.h"
+
 
 namespace moe {
 namespace {
@@ -69,16 +72,17 @@ __device__ __forceinline__ void load_to_lds(const uint8_t* src, uint8_t* lds_wav
 // one 128-input group ahead) and dequantises one word per step into bf16(q s) -- the weight of the
 // int4 format, rounded once to bf16 -- with the row's group scale; the token rows go through the
 // same direct-to-LDS ring as in the bf16 kernel, 32 inputs a stage.
-template <int MT, int NT, int WM, int R>
+template <int MT, int NT, int WM, int R, int NW>
 struct Tile4 {
-    static constexpr int kWN = 8 / WM;
+    static constexpr int kWN = NW / WM;
     static constexpr int kRA = MT / 16 / WM;   // row blocks per wave
     static constexpr int kRB = NT / 16 / kWN;  // token blocks per wave
-    static constexpr int kLB = NT / 128;       // token fragments each wave loads per stage
+    static constexpr int kLB = NT / 16 / NW;   // token fragments each wave loads per stage
     static constexpr int kStage = NT * kKT * 2;
     static constexpr int kLds = R * kStage;
     static constexpr int kLoads = kLB;
-    static_assert(kRA % 2 == 0 && kRA * WM * 16 == MT && kRB * kWN * 16 == NT && R >= 3, "tile shape");
+    static_assert(kRA % 2 == 0 && kRA * WM * 16 == MT && kRB * kWN * 16 == NT && kLB * NW * 16 == NT && R >= 3,
+                  "tile shape");
 };
 
 // word w of an int4 fragment (input pairs at bits 4p and 16+4p, nibble u -> q = u - 8) times the
@@ -97,9 +101,9 @@ __device__ __forceinline__ u32x4_t dequant_word(uint32_t w, float s) {
     return u32x4_t{r[0], r[1], r[2], r[3]};
 }
 
-template <int MODE, int MT, int NT, int WM, int R>
-__global__ __launch_bounds__(512) void ffn_mfma_int4_kernel(FfnArgs a) {
-    using TL = Tile4<MT, NT, WM, R>;
+template <int MODE, int MT, int NT, int WM, int R, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void ffn_mfma_int4_kernel(FfnArgs a) {
+    using TL = Tile4<MT, NT, WM, R, NW>;
     constexpr int RA = TL::kRA, RB = TL::kRB, LB = TL::kLB;
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -252,12 +256,16 @@ __global__ __launch_bounds__(512) void ffn_mfma_int4_kernel(FfnArgs a) {
 }
 
 // bf16 weights with the A operands in registers: each wave loads its own weight fragments
-// (RA row blocks x 1 KB a stage) straight into one of R register sets, the same R-1 stages ahead as
-// the token ring; only the token rows go through LDS, so the LDS carries B reads and DMA writes
-// only.
-template <int MODE, int MT, int NT, int WM, int R>
-__global__ __launch_bounds__(512) void ffn_mfma_areg_kernel(FfnArgs a) {
-    using TL = Tile4<MT, NT, WM, R>;
+// (RA row blocks x 1 KB a stage) straight into one of R register sets, R stages ahead like the
+// token ring; only the token rows go through LDS, so the LDS carries B reads and DMA writes only.
+// The weight loads are ordinary (cached) loads: the 32 workgroups of an XCD that share a weight
+// tile find it in their L2 (non-temporal loads were 8 % slower on the routed 8192-token layer).
+// Step ks multiplies its first half of token blocks, meets the other waves (stage ks+1 landed),
+// refills stage ks's LDS buffer, reads stage ks+1's token fragments around its second half of
+// MFMAs and then refills its weight registers, so a step begins with its operands in registers.
+template <int MODE, int MT, int NT, int WM, int R, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void ffn_mfma_areg_kernel(FfnArgs a) {
+    using TL = Tile4<MT, NT, WM, R, NW>;
     constexpr int RA = TL::kRA, RB = TL::kRB, LB = TL::kLB;
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -316,48 +324,65 @@ __global__ __launch_bounds__(512) void ffn_mfma_areg_kernel(FfnArgs a) {
         }
     }
     u32x4_t areg[R][RA];
-    // stage ks: the token fragments to LDS buffer ks % R, then this wave's weight fragments to
-    // register set `set` (== ks % R); past the end both repeat the last stage (never used)
-    auto issue = [&](int ks, u32x4_t (&set)[RA]) __attribute__((always_inline)) {
-        ks = min(ks, nks - 1);
-        uint8_t* buf = smem + (ks % R) * TL::kStage;
-#pragma unroll
-        for (int u = 0; u < LB; ++u) load_to_lds(b_src[u] + (size_t)ks * (kKT * 2), buf + (LB * wv + u) * 1024);
-#pragma unroll
-        for (int u = 0; u < RA; ++u) set[u] = __builtin_nontemporal_load((const u32x4_t*)(a_blk[u] + (size_t)ks * 1024));
-    };
-
     f32x4_t acc[RA][RB];
 #pragma unroll
     for (int i = 0; i < RA; ++i)
 #pragma unroll
         for (int j = 0; j < RB; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-    auto step = [&](int ks, const u32x4_t (&cur)[RA], u32x4_t (&ahead)[RA]) __attribute__((always_inline)) {
-        // stage ks landed (its token rows for every wave, its weights for this wave); the younger
-        // loads are the R-2 later stages' LB + RA loads
-        stage_barrier<(R - 2) * (LB + RA)>();
-        issue(ks + R - 1, ahead);
+    // stage ks: the token fragments to LDS buffer ks % R, this wave's weight fragments to register
+    // set ks % R; past the end both repeat the last stage (never used)
+    auto issue_lds = [&](int ks) __attribute__((always_inline)) {
+        ks = min(ks, nks - 1);
+        uint8_t* buf = smem + (ks % R) * TL::kStage;
+#pragma unroll
+        for (int u = 0; u < LB; ++u) load_to_lds(b_src[u] + (size_t)ks * (kKT * 2), buf + (LB * wv + u) * 1024);
+    };
+    auto issue_a = [&](int ks, u32x4_t (&set)[RA]) __attribute__((always_inline)) {
+        ks = min(ks, nks - 1);
+#pragma unroll
+        for (int u = 0; u < RA; ++u) set[u] = *(const u32x4_t*)(a_blk[u] + (size_t)ks * 1024);
+    };
+    constexpr int H = RB / 2;
+    u32x4_t bv[RB];
+    auto read_b = [&](int ks, int j0) __attribute__((always_inline)) {
         const uint8_t* sb = smem + (ks % R) * TL::kStage;
-        u32x4_t bv[RB];
 #pragma unroll
-        for (int j = 0; j < RB; ++j) bv[j] = *(const u32x4_t*)(sb + (wn * RB + j) * 1024 + lane * 16);
+        for (int j = j0; j < j0 + H; ++j) bv[j] = *(const u32x4_t*)(sb + (wn * RB + j) * 1024 + lane * 16);
+    };
+    auto step = [&](int ks, u32x4_t (&cur)[RA]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < RB; ++j)
+        for (int j = 0; j < H; ++j)
 #pragma unroll
             for (int i = 0; i < RA; ++i) acc[i][j] = mfma(cur[i], bv[j], acc[i][j]);
+        // stage ks+1 landed (younger: stages ks+2 .. ks+R-1); every wave's reads of stage ks are done
+        stage_barrier<(R - 2) * (LB + RA)>();
+        issue_lds(ks + R);  // into stage ks's buffer
+        const bool more = ks + 1 < nks;
+        if (more) read_b(ks + 1, 0);
+#pragma unroll
+        for (int j = H; j < RB; ++j)
+#pragma unroll
+            for (int i = 0; i < RA; ++i) acc[i][j] = mfma(cur[i], bv[j], acc[i][j]);
+        if (more) read_b(ks + 1, H);
+        issue_a(ks + R, cur);  // set ks % R: its last use was just above
     };
-    static_assert(R == 3, "register sets rotate by three");
-    issue(0, areg[0]);
-    issue(1, areg[1]);
-    int ks = 0;
-    for (; ks + 3 <= nks; ks += 3) {
-        step(ks, areg[0], areg[2]);
-        step(ks + 1, areg[1], areg[0]);
-        step(ks + 2, areg[2], areg[1]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        issue_lds(r);
+        issue_a(r, areg[r]);
     }
-    if (ks < nks) step(ks, areg[0], areg[2]);
-    if (ks + 1 < nks) step(ks + 1, areg[1], areg[0]);
+    stage_barrier<(R - 1) * (LB + RA)>();
+    read_b(0, 0);
+    read_b(0, H);
+    int ks = 0;
+    for (; ks + R <= nks; ks += R) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) step(ks + r, areg[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < R - 1; ++r)
+        if (ks + r < nks) step(ks + r, areg[r]);
     __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
 
     const int quad = lane >> 4;
@@ -386,31 +411,31 @@ __global__ __launch_bounds__(512) void ffn_mfma_areg_kernel(FfnArgs a) {
     }
 }
 
-template <int MODE, int MT, int NT, int WM, int R>
+template <int MODE, int MT, int NT, int WM, int R, int NW>
 moe_status launch_areg(const FfnArgs& a, hipStream_t st, const char* name) {
-    using TL = Tile4<MT, NT, WM, R>;
+    using TL = Tile4<MT, NT, WM, R, NW>;
     const int M = (MODE == kGateUp) ? 2 * a.f : a.d;
     const int64_t items = work_items(a, NT);
     if (items > 65535) return set_error(MOE_ESHAPE, "%s: %lld token tiles exceed one launch", name, (long long)items);
-    auto kern = ffn_mfma_areg_kernel<MODE, MT, NT, WM, R>;
+    auto kern = ffn_mfma_areg_kernel<MODE, MT, NT, WM, R, NW>;
     MOE_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, TL::kLds));
     dim3 grid((unsigned)(M / MT), (unsigned)items);
     ProfScope p(name, st);
-    kern<<<grid, 512, TL::kLds, st>>>(a);
+    kern<<<grid, NW * 64, TL::kLds, st>>>(a);
     return check_launch(name);
 }
 
-template <int MODE, int MT, int NT, int WM, int R>
+template <int MODE, int MT, int NT, int WM, int R, int NW>
 moe_status launch_int4(const FfnArgs& a, hipStream_t st, const char* name) {
-    using TL = Tile4<MT, NT, WM, R>;
+    using TL = Tile4<MT, NT, WM, R, NW>;
     const int M = (MODE == kGateUp) ? 2 * a.f : a.d;
     const int64_t items = work_items(a, NT);
     if (items > 65535) return set_error(MOE_ESHAPE, "%s: %lld token tiles exceed one launch", name, (long long)items);
-    auto kern = ffn_mfma_int4_kernel<MODE, MT, NT, WM, R>;
+    auto kern = ffn_mfma_int4_kernel<MODE, MT, NT, WM, R, NW>;
     MOE_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, TL::kLds));
     dim3 grid((unsigned)(M / MT), (unsigned)items);
     ProfScope p(name, st);
-    kern<<<grid, 512, TL::kLds, st>>>(a);
+    kern<<<grid, NW * 64, TL::kLds, st>>>(a);
     return check_launch(name);
 }
 
@@ -428,30 +453,39 @@ moe_status launch_int4(const FfnArgs& a, hipStream_t st, const char* name) {
 #ifndef MOE_MFMA_R
 #define MOE_MFMA_R 3
 #endif
+#ifndef MOE_MFMA_NW
+#define MOE_MFMA_NW 8
+#endif
 #ifndef MOE_MFMA4_MT
 #define MOE_MFMA4_MT 256
 #endif
 #ifndef MOE_MFMA4_R
 #define MOE_MFMA4_R 4
 #endif
+#ifndef MOE_MFMA4_NW
+#define MOE_MFMA4_NW 8
+#endif
+#ifndef MOE_MFMA4_WM
+#define MOE_MFMA4_WM 8
+#endif
 
 // Many tokens per expert, bf16 activations, bf16 or int4 weights: the MFMA path, one projection
 // (mode kGateUp or kDown).  Other cases report MOE_EDTYPE ("not mine").
 moe_status ffn_mfma_proj(const FfnArgs& a, moe_dtype act, moe_dtype w, int mode, hipStream_t st) {
-    constexpr int MT = MOE_MFMA_MT, NT = MOE_MFMA_NT, WM = MOE_MFMA_WM, R = MOE_MFMA_R;
+    constexpr int MT = MOE_MFMA_MT, NT = MOE_MFMA_NT, WM = MOE_MFMA_WM, R = MOE_MFMA_R, NW = MOE_MFMA_NW;
     if (act != MOE_BF16 || a.T <= 64) return MOE_EDTYPE;
     if (w == MOE_INT4_G128) {
         // 256 weight rows a workgroup: 2 row blocks x 8 token blocks a wave keep the accumulators,
         // the raw fragments of two groups and the dequantised operands within 256 registers
-        constexpr int MT4 = MOE_MFMA4_MT, R4 = MOE_MFMA4_R;
+        constexpr int MT4 = MOE_MFMA4_MT, R4 = MOE_MFMA4_R, NW4 = MOE_MFMA4_NW, WM4 = MOE_MFMA4_WM;
         if ((2 * a.f) % MT4 || a.d % MT4) return MOE_EDTYPE;
-        if (mode == kGateUp) return launch_int4<kGateUp, MT4, NT, WM, R4>(a, st, "ffn_mfma_gateup_int4");
-        return launch_int4<kDown, MT4, NT, WM, R4>(a, st, "ffn_mfma_down_int4");
+        if (mode == kGateUp) return launch_int4<kGateUp, MT4, NT, WM4, R4, NW4>(a, st, "ffn_mfma_gateup_int4");
+        return launch_int4<kDown, MT4, NT, WM4, R4, NW4>(a, st, "ffn_mfma_down_int4");
     }
     if (w != MOE_BF16) return MOE_EDTYPE;
     if ((2 * a.f) % MT || a.d % MT) return MOE_EDTYPE;
-    if (mode == kGateUp) return launch_areg<kGateUp, MT, NT, WM, R>(a, st, "ffn_mfma_gateup_bf16");
-    return launch_areg<kDown, MT, NT, WM, R>(a, st, "ffn_mfma_down_bf16");
+    if (mode == kGateUp) return launch_areg<kGateUp, MT, NT, WM, R, NW>(a, st, "ffn_mfma_gateup_bf16");
+    return launch_areg<kDown, MT, NT, WM, R, NW>(a, st, "ffn_mfma_down_bf16");
 }
 
 moe_status ffn_mfma(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st) {
