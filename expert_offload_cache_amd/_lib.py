@@ -5,7 +5,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe.so")
+# MOE_LIB_PATH selects another build of the same library (the host-sanitizer build of the tests)
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EDTYPE, MOE_ENOMEM, MOE_EHIP, MOE_ECAPACITY, MOE_ESTATE = 0, -1, -2, -3, -4, -5, -6, -7
 MOE_F32, MOE_BF16, MOE_INT4_G128 = 0, 1, 2

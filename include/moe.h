@@ -57,7 +57,10 @@ enum {
     MOE_ESTATE = -7     /* call out of order, or an eviction would hit an unread slot */
 };
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_INT4_G128 = 2 } moe_dtype;
+/* element type codes (an integer, so that any value a caller passes is well defined; values other
+ * than these are rejected with MOE_EDTYPE) */
+typedef int32_t moe_dtype;
+enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_INT4_G128 = 2 };
 typedef void* moe_stream;
 
 MOE_API const char* moe_last_error(void);
