@@ -3,19 +3,31 @@
 // picks the experts, the GPU-resident ones are used from their slots and a miss is copied from
 // the pinned host pool first; FreeToken GGUF page, offload backend).
 //
-// Per layer, on the compute stream: route + permute (one call) -> ids copied to pinned host
-// memory; the host waits for the copy (the cache decides on the host, with no lookahead) ->
-// distinct ids, lookup, fill (copies on the copy stream, compute waits) -> grouped experts
-// through the layer's slot-table row -> combine -> mark_read.  The same calls as a caller would
-// make one by one; only the host-side marshalling between them is gone.
+// Per layer, on the compute stream (moe_decode_step): route + permute (one call) -> grouped experts
+// through the layer's slot-table row as it stands and the combine, enqueued at once -> the host
+// reads the ids (at one token the route kernel stores them straight into coherent host memory; the
+// cache decides on the host, with no lookahead) -> distinct ids, lookup, fill (copies on the copy
+// stream, compute waits) -> for a layer with misses, the missed experts again after their copies,
+// and the combine again -> mark_read.  The cache's decisions and the outputs are those of the calls
+// made one by one; the GPU runs the resident experts while the host decides.  The hybrid and
+// split-launch steps decide before launching any expert.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
+#include <climits>
 #include <vector>
 
 #include "moe_common.h"
 
 using namespace moe;
+
+namespace moe {
+moe_status route_permute_publish(const void* x, moe_dtype act, int T, int d, const void* w_router, const float* bias,
+                                 int E, int k, const int32_t* forced_idx, int32_t* topk_idx, float* topk_w,
+                                 float* logits, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                 void* ws, size_t ws_bytes, int32_t* publish, moe_stream s);  // route.hip
+}
 
 namespace {
 // Event marking the ids' arrival in host memory (created per call, released on every return).
@@ -27,7 +39,109 @@ struct IdsEvent {
         if (e) (void)hipEventDestroy(e);
     }
 };
+
+// Per host thread (a thread runs one decode step at a time) and device, allocated on first use and
+// held until the process ends: coherent host memory that the one-token route kernel stores the
+// ids into, and a slot-table row (pinned host, device) for a layer's second launch.  NULL when any
+// of them cannot be allocated (the steps then take the copy-and-wait path).
+constexpr int kMaxE = 1024;  // k <= E <= 1024
+constexpr int kScratchDevices = 64;
+struct StepScratch {
+    int32_t* mirror = nullptr;    // [kMaxE] coherent host
+    int32_t* host_row = nullptr;  // [kMaxE] pinned host
+    int32_t* dev_row = nullptr;   // [kMaxE] device
+    bool failed = false;
+};
+StepScratch* step_scratch() {
+    thread_local StepScratch scratch[kScratchDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+    StepScratch& sc = scratch[dev];
+    if (sc.failed) return nullptr;
+    if (!sc.dev_row) {
+        void *m = nullptr, *h = nullptr, *dv = nullptr;
+        const size_t bytes = sizeof(int32_t) * kMaxE;
+        if (hipHostMalloc(&m, bytes, hipHostMallocCoherent) != hipSuccess || hipHostMalloc(&h, bytes) != hipSuccess ||
+            hipMalloc(&dv, bytes) != hipSuccess) {
+            if (m) (void)hipHostFree(m);
+            if (h) (void)hipHostFree(h);
+            sc.failed = true;
+            return nullptr;
+        }
+        sc.mirror = (int32_t*)m;
+        sc.host_row = (int32_t*)h;
+        sc.dev_row = (int32_t*)dv;
+    }
+    return &sc;
+}
+
+// Enqueues route + permute of one layer on `compute` and starts the ids' way to the host: with a
+// `mirror` (one token only) the route kernel also stores the k ids into it, with system scope,
+// after the host has set it to INT_MIN; without one, topk_idx is copied to host_idx and an event
+// recorded after the copy.
+moe_status route_start(const moe_decode_layer& ly, moe_dtype act, int T, int d, int E, int k, int32_t* topk_idx,
+                       float* topk_w, float* logits, int32_t* counts, int32_t* offsets, int32_t* perm,
+                       int32_t* inv_perm, int32_t* mirror, int32_t* host_idx, IdsEvent& ev, moe_stream compute) {
+    hipStream_t cs = (hipStream_t)compute;
+    if (mirror)
+        for (int j = 0; j < k; ++j) __atomic_store_n(mirror + j, INT_MIN, __ATOMIC_RELAXED);
+    moe_status r = route_permute_publish(ly.x, act, T, d, ly.w_router, ly.bias, E, k, ly.forced_idx, topk_idx, topk_w,
+                                         logits, counts, offsets, perm, inv_perm, nullptr, 0, mirror, compute);
+    if (r != MOE_OK || mirror) return r;
+    MOE_HIP(hipMemcpyAsync(host_idx, topk_idx, sizeof(int32_t) * (size_t)T * k, hipMemcpyDeviceToHost, cs));
+    MOE_HIP(hipEventRecord(ev.e, cs));
+    return MOE_OK;
+}
+
+// Waits until the layer's T*k ids are in host memory and leaves them in host_idx.  When it returns
+// OK, everything enqueued on `compute` before the route launch has completed.  With a mirror the
+// host polls it; a poll that sees the stream finished, or a stream error, without every id
+// arriving returns MOE_EHIP (the kernel's stores are posted before its completion).
+moe_status ids_wait(int T, int k, int32_t* mirror, int32_t* host_idx, IdsEvent& ev, moe_stream compute) {
+    if (!mirror) {
+        MOE_HIP(hipEventSynchronize(ev.e));
+        return MOE_OK;
+    }
+    hipStream_t cs = (hipStream_t)compute;
+    auto arrived = [&] {
+        int j = 0;
+        while (j < k && __atomic_load_n(mirror + j, __ATOMIC_ACQUIRE) != INT_MIN) ++j;
+        return j == k;
+    };
+    const auto t0 = std::chrono::steady_clock::now();
+    for (unsigned spin = 0; !arrived(); ++spin) {
+        if ((spin & 1023u) == 1023u) {
+            const hipError_t q = hipStreamQuery(cs);
+            if (q == hipSuccess) {
+                if (arrived()) break;
+                return set_error(MOE_EHIP, "decode step: the route kernel finished without publishing its ids");
+            }
+            if (q != hipErrorNotReady) return hip_error(q, "decode step: route kernel");
+            if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(30))
+                return set_error(MOE_EHIP, "decode step: the layer's ids did not arrive within 30 s");
+        }
+        __builtin_ia32_pause();
+    }
+    for (int j = 0; j < T * k; ++j) host_idx[j] = mirror[j];
+    return MOE_OK;
+}
+
+// route_start + ids_wait (the steps that decide before launching any expert)
+moe_status route_ids_to_host(const moe_decode_layer& ly, moe_dtype act, int T, int d, int E, int k, int32_t* topk_idx,
+                             float* topk_w, float* logits, int32_t* counts, int32_t* offsets, int32_t* perm,
+                             int32_t* inv_perm, int32_t* host_idx, IdsEvent& ev, moe_stream compute) {
+    StepScratch* sc = T == 1 ? step_scratch() : nullptr;
+    int32_t* mirror = sc ? sc->mirror : nullptr;
+    moe_status r = route_start(ly, act, T, d, E, k, topk_idx, topk_w, logits, counts, offsets, perm, inv_perm, mirror,
+                               host_idx, ev, compute);
+    if (r != MOE_OK) return r;
+    return ids_wait(T, k, mirror, host_idx, ev, compute);
+}
 }  // namespace
+
+namespace moe {
+moe_status cache_wait_background(moe_cache* c, hipStream_t compute);  // cache.cpp
+}
 
 extern "C" moe_status moe_decode_step(moe_cache* cache, int n_layers, const moe_decode_layer* layers, int T, int d,
                                       int f, int E, int k, moe_dtype act, moe_dtype w, const void* slot_pool,
@@ -44,30 +158,70 @@ extern "C" moe_status moe_decode_step(moe_cache* cache, int n_layers, const moe_
                   "moe_decode_step: layer %d: NULL pointer", i);
     if (n_layers == 0) return MOE_OK;
     hipStream_t cs = (hipStream_t)compute;
-    std::vector<int32_t> ids((size_t)T * k), slots((size_t)T * k);
+    std::vector<int32_t> ids((size_t)T * k), slots((size_t)T * k), missed;
     IdsEvent ev;
     MOE_HIP(ev.status);
+    StepScratch* sc = E <= kMaxE ? step_scratch() : nullptr;
     for (int i = 0; i < n_layers; ++i) {
         const moe_decode_layer& ly = layers[i];
-        moe_status r = moe_route_permute(ly.x, act, T, d, ly.w_router, ly.bias, E, k, ly.forced_idx, topk_idx,
-                                         topk_w, logits, counts, offsets, perm, inv_perm, nullptr, 0, compute);
+        const int32_t* row = slot_table + (size_t)ly.layer * E;
+        int32_t* mirror = (sc && T == 1) ? sc->mirror : nullptr;
+        moe_status r = route_start(ly, act, T, d, E, k, topk_idx, topk_w, logits, counts, offsets, perm, inv_perm,
+                                   mirror, host_idx, ev, compute);
         if (r != MOE_OK) return r;
-        MOE_HIP(hipMemcpyAsync(host_idx, topk_idx, sizeof(int32_t) * (size_t)T * k, hipMemcpyDeviceToHost, cs));
-        MOE_HIP(hipEventRecord(ev.e, cs));
-        MOE_HIP(hipEventSynchronize(ev.e));
+        if (sc) {
+            // the experts and the combine go ahead through the slot table as it stands while the host
+            // reads the ids and decides: a resident expert's rows are final; a missed expert's rows
+            // (its slot absent, or being refilled) are recomputed below once its copy has landed
+            r = cache_wait_background(cache, cs);
+            if (r != MOE_OK) return r;
+            r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, row, n_slots, slot_pool,
+                                       slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, compute);
+            if (r != MOE_OK) return r;
+            r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
+            if (r != MOE_OK) return r;
+        }
+        r = ids_wait(T, k, mirror, host_idx, ev, compute);
+        if (r != MOE_OK) return r;
         std::copy(host_idx, host_idx + (size_t)T * k, ids.begin());
         std::sort(ids.begin(), ids.end());
         const int n = (int)(std::unique(ids.begin(), ids.end()) - ids.begin());
+        missed.clear();
+        if (sc)
+            for (int j = 0; j < n; ++j) {
+                int32_t sl = -1;
+                r = moe_cache_slot_of(cache, ly.layer, ids[j], &sl);
+                if (r != MOE_OK) return r;
+                if (sl < 0) missed.push_back(j);
+            }
         int32_t n_miss = 0;
         r = moe_cache_lookup(cache, ly.layer, ids.data(), n, slots.data(), &n_miss);
         if (r != MOE_OK) return r;
         r = moe_cache_fill(cache, copy, compute);
         if (r != MOE_OK) return r;
-        r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, slot_table + (size_t)ly.layer * E,
-                                   n_slots, slot_pool, slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, compute);
-        if (r != MOE_OK) return r;
-        r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
-        if (r != MOE_OK) return r;
+        if (!sc) {
+            r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, row, n_slots, slot_pool,
+                                       slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, compute);
+            if (r != MOE_OK) return r;
+            r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
+            if (r != MOE_OK) return r;
+        } else if (!missed.empty()) {
+            // the missed experts again, after their copies (the fill made `compute` wait for them):
+            // a row with only them in their new slots, every other expert produced elsewhere (and
+            // the shared expert's rows kept); then the combine again.  The next layer's ids arriving
+            // retires this row's copy before the host writes the row again.
+            for (int e = 0; e < E; ++e) sc->host_row[e] = MOE_SLOT_ELSEWHERE;
+            for (int j : missed) sc->host_row[ids[j]] = slots[j];
+            MOE_HIP(hipMemcpyAsync(sc->dev_row, sc->host_row, sizeof(int32_t) * E, hipMemcpyHostToDevice, cs));
+            // the first launch flagged the missed experts' absent slots in the workspace status
+            // word; the flag is the second launch's to set
+            MOE_HIP(hipMemsetAsync(ws, 0, sizeof(int32_t), cs));
+            r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, sc->dev_row, n_slots,
+                                       slot_pool, slot_stride, w, nullptr, y_perm, ws, ws_bytes, compute);
+            if (r != MOE_OK) return r;
+            r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
+            if (r != MOE_OK) return r;
+        }
         r = moe_cache_mark_read(cache, ly.layer, compute);
         if (r != MOE_OK) return r;
     }
@@ -76,7 +230,6 @@ extern "C" moe_status moe_decode_step(moe_cache* cache, int n_layers, const moe_
 
 namespace moe {
 const void* cache_host_image(const moe_cache* c, int layer, int expert);  // cache.cpp
-moe_status cache_wait_background(moe_cache* c, hipStream_t compute);     // cache.cpp
 }
 
 namespace {
@@ -135,13 +288,11 @@ extern "C" moe_status moe_decode_step_hybrid(
     MOE_HIP(ev.status);
     for (int i = 0; i < n_layers; ++i) {
         const moe_decode_layer& ly = layers[i];
-        moe_status r = moe_route_permute(ly.x, act, T, d, ly.w_router, ly.bias, E, k, ly.forced_idx, topk_idx,
-                                         topk_w, logits, counts, offsets, perm, inv_perm, nullptr, 0, compute);
+        // the ids' arrival also retires the previous layer's table and row copies (earlier on the
+        // stream than the route kernel)
+        moe_status r = route_ids_to_host(ly, act, T, d, E, k, topk_idx, topk_w, logits, counts, offsets, perm,
+                                         inv_perm, host_idx, ev, compute);
         if (r != MOE_OK) return r;
-        MOE_HIP(hipMemcpyAsync(host_idx, topk_idx, sizeof(int32_t) * k, hipMemcpyDeviceToHost, cs));
-        MOE_HIP(hipEventRecord(ev.e, cs));
-        // the event also retires the previous layer's table and row copies (earlier on the stream)
-        MOE_HIP(hipEventSynchronize(ev.e));
         std::copy(host_idx, host_idx + k, ids.begin());
         std::sort(ids.begin(), ids.end());
         const int n = (int)(std::unique(ids.begin(), ids.end()) - ids.begin());
@@ -236,13 +387,11 @@ extern "C" moe_status moe_decode_step_split(moe_cache* cache, int n_layers, cons
     MOE_HIP(ev.status);
     for (int i = 0; i < n_layers; ++i) {
         const moe_decode_layer& ly = layers[i];
-        moe_status r = moe_route_permute(ly.x, act, T, d, ly.w_router, ly.bias, E, k, ly.forced_idx, topk_idx,
-                                         topk_w, logits, counts, offsets, perm, inv_perm, nullptr, 0, compute);
+        // the ids' arrival also retires the previous layer's table copy (earlier on the stream than
+        // the route kernel)
+        moe_status r = route_ids_to_host(ly, act, T, d, E, k, topk_idx, topk_w, logits, counts, offsets, perm,
+                                         inv_perm, host_idx, ev, compute);
         if (r != MOE_OK) return r;
-        MOE_HIP(hipMemcpyAsync(host_idx, topk_idx, sizeof(int32_t) * (size_t)T * k, hipMemcpyDeviceToHost, cs));
-        MOE_HIP(hipEventRecord(ev.e, cs));
-        // also retires the previous layer's table copy (earlier on the stream)
-        MOE_HIP(hipEventSynchronize(ev.e));
         std::copy(host_idx, host_idx + (size_t)T * k, ids.begin());
         std::sort(ids.begin(), ids.end());
         const int n = (int)(std::unique(ids.begin(), ids.end()) - ids.begin());

@@ -419,11 +419,15 @@ __global__ __launch_bounds__(256) void route_topk_wave(const float* __restrict__
 // one token, without its passes.  One launch instead of two.  (A sort by the last of route_topk's
 // blocks would need a device-scope release and acquire, which write back and invalidate an XCD's
 // L2.)  Ids are clamped into [0, E) for the placement, as in moe_permute.
+//
+// `publish` (or NULL): coherent host memory that also receives the k ids, stored with system scope
+// so that a host thread polling it sees them without a copy (the native decode steps' read-back).
 __global__ __launch_bounds__(1024) void route_topk_permute1(const float* __restrict__ logits, int E, int k,
                                                            const int32_t* __restrict__ forced,
                                                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
                                                            int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+                                                           int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+                                                           int32_t* __restrict__ publish) {
     __shared__ __align__(16) float s_logit[1024];
     __shared__ int s_sel[1024];
     __shared__ float s_val[1024];
@@ -432,6 +436,8 @@ __global__ __launch_bounds__(1024) void route_topk_permute1(const float* __restr
     __syncthreads();
     // s_sel is complete after the barrier inside (nothing writes it afterwards)
     select_and_gate(s_logit, E, k, forced, s_sel, s_val, topk_idx, topk_w);
+    if (publish)
+        for (int j = tid; j < k; j += nth) __hip_atomic_store(publish + j, s_sel[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     for (int e = tid; e < E; e += nth) {
         int c = 0, o = 0;
         for (int j = 0; j < k; ++j) {
@@ -653,11 +659,12 @@ extern "C" moe_status moe_route(const void* x, moe_dtype act, int T, int d, cons
     return launch_route_topk(logits, T, E, k, forced_idx, topk_idx, topk_w, st);
 }
 
-extern "C" moe_status moe_route_permute(const void* x, moe_dtype act, int T, int d, const void* w_router,
-                                        const float* bias, int E, int k, const int32_t* forced_idx,
-                                        int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts,
-                                        int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws,
-                                        size_t ws_bytes, moe_stream s) {
+namespace moe {
+// moe_route_permute; at T = 1 the ids also go to `publish` (coherent host memory, or NULL)
+moe_status route_permute_publish(const void* x, moe_dtype act, int T, int d, const void* w_router, const float* bias,
+                                 int E, int k, const int32_t* forced_idx, int32_t* topk_idx, float* topk_w,
+                                 float* logits, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                 void* ws, size_t ws_bytes, int32_t* publish, moe_stream s) {
     MOE_CHECK(T >= 0, MOE_ESHAPE, "moe_route_permute: T=%d < 0", T);
     if (T == 0) return moe_permute(nullptr, 0, k, E, counts, offsets, perm, inv_perm, nullptr, 0, s);
     moe_status r = check_route_args("moe_route_permute", x, act, T, d, w_router, E, k, topk_idx, topk_w, logits);
@@ -677,6 +684,16 @@ extern "C" moe_status moe_route_permute(const void* x, moe_dtype act, int T, int
     while (nth < 1024 && nth < 4 * E) nth *= 2;
     ProfScope p("route_topk_permute", st);
     route_topk_permute1<<<1, nth, 0, st>>>(logits, E, k, forced_idx, topk_idx, topk_w, counts, offsets, perm,
-                                           inv_perm);
+                                           inv_perm, publish);
     return check_launch("route_topk_permute");
+}
+}  // namespace moe
+
+extern "C" moe_status moe_route_permute(const void* x, moe_dtype act, int T, int d, const void* w_router,
+                                        const float* bias, int E, int k, const int32_t* forced_idx,
+                                        int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts,
+                                        int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws,
+                                        size_t ws_bytes, moe_stream s) {
+    return route_permute_publish(x, act, T, d, w_router, bias, E, k, forced_idx, topk_idx, topk_w, logits, counts,
+                                 offsets, perm, inv_perm, ws, ws_bytes, nullptr, s);
 }

@@ -292,14 +292,22 @@ MOE_API void moe_cache_destroy(moe_cache* c);
  * moe_decode_step -- one decode step of an offloaded stack, every layer in one call (FreeToken
  * linux guide, "MoE memory handling"; FreeToken GGUF page, offload backend).  For each layer,
  * in order, on `compute`: moe_route_permute (forced_idx may be NULL) into the given buffers;
- * topk_idx copied to host_idx (pinned, T*k int32); the host waits for that copy; the distinct
- * ids, ascending, to moe_cache_lookup(layer);
- * moe_cache_fill(copy, compute); moe_expert_ffn_grouped through slot_table row `layer` (the
- * cache's slot table, device [L*E]); moe_combine into y (act dtype); moe_cache_mark_read(layer).
- * Outputs, cache decisions and statistics are those of the same calls made one by one.  Buffers
- * as in those calls; y_perm [T*k (+T), d] f32; ws: moe_workspace_bytes(T, ...) bytes.  Every
- * layer's x, w_router and y are checked (MOE_EINVAL) before anything is enqueued; later errors
- * return at once, the layers before them enqueued.  Returns the first error. */
+ * moe_expert_ffn_grouped through slot_table row `layer` (the cache's slot table, device [L*E]) and
+ * moe_combine into y (act dtype), enqueued before the host has the ids; the ids reach host_idx
+ * (pinned, T*k int32) -- at one token the route kernel also stores them into coherent host memory
+ * of the library, which the host polls, otherwise topk_idx is copied and the host waits for the
+ * copy; the distinct ids, ascending, to moe_cache_lookup(layer); moe_cache_fill(copy, compute);
+ * when the layer has misses, the missed experts once more after their copies (a slot-table row of
+ * the library with every other expert marked MOE_SLOT_ELSEWHERE) and moe_combine again;
+ * moe_cache_mark_read(layer).  A resident expert's rows from the first launch are final; a missed
+ * expert's (its slot absent or being refilled) are recomputed.  Outputs, cache decisions and
+ * statistics are those of the same calls made one by one (route, lookup, fill, experts, combine,
+ * mark_read).  The library holds, per host thread and device, a 4 KB coherent host buffer, a 4 KB
+ * pinned host row and a 4 KB device row, allocated on first use until the process ends; when they
+ * cannot be allocated the step runs the calls in that order instead.  Buffers as in those calls;
+ * y_perm [T*k (+T), d] f32; ws: moe_workspace_bytes(T, ...) bytes.  Every layer's x, w_router and
+ * y are checked (MOE_EINVAL) before anything is enqueued; later errors return at once, the layers
+ * before them enqueued.  Returns the first error. */
 typedef struct {
     const void* x;             /* [T, d] act: this layer's input (device) */
     const void* w_router;      /* [E, d] act */
