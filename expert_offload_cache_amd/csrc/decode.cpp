@@ -286,12 +286,29 @@ extern "C" moe_status moe_decode_step_hybrid(
     int64_t n_cpu_total = 0;
     IdsEvent ev;
     MOE_HIP(ev.status);
+    StepScratch* sc = E <= kMaxE ? step_scratch() : nullptr;
     for (int i = 0; i < n_layers; ++i) {
         const moe_decode_layer& ly = layers[i];
+        const int32_t* row = slot_table + (size_t)ly.layer * E;
+        int32_t* mirror = sc ? sc->mirror : nullptr;
+        moe_status r = route_start(ly, act, T, d, E, k, topk_idx, topk_w, logits, counts, offsets, perm, inv_perm,
+                                   mirror, host_idx, ev, compute);
+        if (r != MOE_OK) return r;
+        if (sc) {
+            // as moe_decode_step: the experts and the combine through the slot table as it stands
+            // while the host decides; every miss's rows are produced again below (by the host or
+            // after its copy)
+            r = cache_wait_background(cache, cs);
+            if (r != MOE_OK) return r;
+            r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, row, n_slots, slot_pool,
+                                       slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, compute);
+            if (r != MOE_OK) return r;
+            r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
+            if (r != MOE_OK) return r;
+        }
         // the ids' arrival also retires the previous layer's table and row copies (earlier on the
         // stream than the route kernel)
-        moe_status r = route_ids_to_host(ly, act, T, d, E, k, topk_idx, topk_w, logits, counts, offsets, perm,
-                                         inv_perm, host_idx, ev, compute);
+        r = ids_wait(T, k, mirror, host_idx, ev, compute);
         if (r != MOE_OK) return r;
         std::copy(host_idx, host_idx + k, ids.begin());
         std::sort(ids.begin(), ids.end());
@@ -312,12 +329,24 @@ extern "C" moe_status moe_decode_step_hybrid(
             if (r != MOE_OK) return r;
             r = moe_cache_fill(cache, copy, compute);
             if (r != MOE_OK) return r;
-            r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts,
-                                       slot_table + (size_t)ly.layer * E, n_slots, slot_pool, slot_stride, w,
-                                       ly.shared_w, y_perm, ws, ws_bytes, compute);
-            if (r != MOE_OK) return r;
-            r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
-            if (r != MOE_OK) return r;
+            if (!sc) {
+                r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, row, n_slots, slot_pool,
+                                           slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, compute);
+                if (r != MOE_OK) return r;
+                r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
+                if (r != MOE_OK) return r;
+            } else if (!miss.empty()) {
+                // the missed experts again after their copies, then the combine again
+                for (int e = 0; e < E; ++e) sc->host_row[e] = MOE_SLOT_ELSEWHERE;
+                for (int e : miss) sc->host_row[e] = slots[std::lower_bound(ids.begin(), ids.begin() + n, e) - ids.begin()];
+                MOE_HIP(hipMemcpyAsync(sc->dev_row, sc->host_row, sizeof(int32_t) * E, hipMemcpyHostToDevice, cs));
+                MOE_HIP(hipMemsetAsync(ws, 0, sizeof(int32_t), cs));  // the first launch's absent-slot flag
+                r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, sc->dev_row, n_slots,
+                                           slot_pool, slot_stride, w, nullptr, y_perm, ws, ws_bytes, compute);
+                if (r != MOE_OK) return r;
+                r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
+                if (r != MOE_OK) return r;
+            }
             r = moe_cache_mark_read(cache, ly.layer, compute);
             if (r != MOE_OK) return r;
             continue;
@@ -335,13 +364,35 @@ extern "C" moe_status moe_decode_step_hybrid(
         r = copy_too ? moe_cache_fill_split(cache, on_cpu.data(), (int)on_cpu.size(), copy, compute)
                      : moe_cache_fill(cache, copy, compute);
         if (r != MOE_OK) return r;
-        std::fill(host_table, host_table + E, -1);
-        for (size_t j = 0; j < gpu_ids.size(); ++j) host_table[gpu_ids[j]] = slots[j];
-        for (int e : on_cpu) host_table[e] = MOE_SLOT_ELSEWHERE;
-        MOE_HIP(hipMemcpyAsync(dev_table, host_table, sizeof(int32_t) * E, hipMemcpyHostToDevice, cs));
-        r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, dev_table, n_slots, slot_pool,
-                                   slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, compute);
-        if (r != MOE_OK) return r;
+        if (!sc) {
+            std::fill(host_table, host_table + E, -1);
+            for (size_t j = 0; j < gpu_ids.size(); ++j) host_table[gpu_ids[j]] = slots[j];
+            for (int e : on_cpu) host_table[e] = MOE_SLOT_ELSEWHERE;
+            MOE_HIP(hipMemcpyAsync(dev_table, host_table, sizeof(int32_t) * E, hipMemcpyHostToDevice, cs));
+            r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, dev_table, n_slots,
+                                       slot_pool, slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, compute);
+            if (r != MOE_OK) return r;
+        } else {
+            // the first launch produced the resident experts; the GPU's misses again after their
+            // copies (every other expert produced elsewhere), the host's below
+            std::fill(host_table, host_table + E, MOE_SLOT_ELSEWHERE);
+            int n_gpu_miss = 0;
+            for (size_t j = 0; j < gpu_ids.size(); ++j) {
+                const int e = gpu_ids[j];
+                if (std::find(miss.begin(), miss.end(), e) != miss.end() &&
+                    std::find(on_cpu.begin(), on_cpu.end(), e) == on_cpu.end()) {
+                    host_table[e] = slots[j];
+                    ++n_gpu_miss;
+                }
+            }
+            MOE_HIP(hipMemsetAsync(ws, 0, sizeof(int32_t), cs));  // the first launch's absent-slot flag
+            if (n_gpu_miss > 0) {
+                MOE_HIP(hipMemcpyAsync(dev_table, host_table, sizeof(int32_t) * E, hipMemcpyHostToDevice, cs));
+                r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, dev_table, n_slots,
+                                           slot_pool, slot_stride, w, nullptr, y_perm, ws, ws_bytes, compute);
+                if (r != MOE_OK) return r;
+            }
+        }
         // the host's experts run while the copies and the GPU's experts do
         MOE_HIP(hipEventSynchronize(ev.e));  // host_x has arrived
         for (int e : on_cpu) {

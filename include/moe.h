@@ -353,18 +353,20 @@ MOE_API moe_status moe_decode_step_split(moe_cache* cache, int n_layers, const m
 MOE_API moe_status moe_hybrid_split(int m, double cpu_rate, double pcie_rate, double host_fixed_s, int32_t* n_host);
 
 /* moe_decode_step with hybrid miss handling (FreeToken RTX 5090 page, miss split; stork.ai
- * article, miss policy), one token per step (T = 1, bf16 activations).  Per layer, after the ids
- * reach the host (host_idx: k int32, pinned): the layer's m misses are split by moe_hybrid_split
- * (cpu_rate, pcie_rate, host_fixed_s), the host taking the n highest-numbered ones.  A layer with n = 0 runs as in
- * moe_decode_step (the slot-table row as is).  Otherwise x is copied to host_x (d bf16, pinned)
- * while the cache decides, and the other ids (all of them
- * with copy_too, whose host experts are then also inserted, their copies deferred through
- * moe_cache_fill_split) go to moe_cache_lookup and a fill; the layer's table row is staged in
- * host_table (pinned, E int32) and copied to dev_table (device, E int32) with the host experts
- * marked MOE_SLOT_ELSEWHERE; the GPU experts are enqueued; each host expert runs
+ * article, miss policy), one token per step (T = 1, bf16 activations).  Per layer, as in
+ * moe_decode_step, the experts and the combine are first enqueued through the slot-table row as it
+ * stands; after the ids reach the host (host_idx: k int32, pinned): the layer's m misses are split
+ * by moe_hybrid_split (cpu_rate, pcie_rate, host_fixed_s), the host taking the n highest-numbered
+ * ones.  A layer with n = 0 continues as moe_decode_step (lookup, fill, the missed experts again).
+ * Otherwise x is copied to host_x (d bf16, pinned), and the other ids (all of them with copy_too,
+ * whose host experts are then also inserted, their copies deferred through moe_cache_fill_split)
+ * go to moe_cache_lookup and a fill; a table row with only the GPU's missed experts in their slots
+ * (every other expert MOE_SLOT_ELSEWHERE) is staged in host_table (pinned, E int32) and copied to
+ * dev_table (device, E int32), and those experts are enqueued again; each host expert runs
  * moe_cpu_expert_ffn on its pinned image (cpu_threads, 0 = all) into host_y (pinned, k*d f32) and
- * its row is copied into y_perm; then moe_combine and mark_read.  *n_cpu_out (if not NULL) is
- * increased by the number of host-run experts.  Other arguments as moe_decode_step. */
+ * its row is copied into y_perm; then moe_combine and mark_read.  Outputs and cache decisions are
+ * those of the same calls made one by one.  *n_cpu_out (if not NULL) is increased by the number of
+ * host-run experts.  Other arguments, and the library's per-thread buffers, as moe_decode_step. */
 MOE_API moe_status moe_decode_step_hybrid(moe_cache* cache, int n_layers, const moe_decode_layer* layers, int d,
                                           int f, int E, int k, moe_dtype act, moe_dtype w, const void* slot_pool,
                                           int n_slots, size_t slot_stride, const int32_t* slot_table,
