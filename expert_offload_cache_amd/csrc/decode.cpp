@@ -27,6 +27,11 @@ moe_status route_permute_publish(const void* x, moe_dtype act, int T, int d, con
                                  int E, int k, const int32_t* forced_idx, int32_t* topk_idx, float* topk_w,
                                  float* logits, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                                  void* ws, size_t ws_bytes, int32_t* publish, moe_stream s);  // route.hip
+moe_status ffn_grouped_status(const void* x, moe_dtype act, int T, int d, int f, int E, int k, const int32_t* perm,
+                              const int32_t* offsets, const int32_t* counts, const int32_t* slot_of_expert,
+                              int n_slots, const void* slot_pool, size_t slot_stride, moe_dtype w,
+                              const void* shared_w, float* y_perm, void* ws, size_t ws_bytes, int32_t* status,
+                              moe_stream s);  // ffn_dispatch.cpp
 }
 
 namespace {
@@ -49,7 +54,8 @@ constexpr int kScratchDevices = 64;
 struct StepScratch {
     int32_t* mirror = nullptr;    // [kMaxE] coherent host
     int32_t* host_row = nullptr;  // [kMaxE] pinned host
-    int32_t* dev_row = nullptr;   // [kMaxE] device
+    int32_t* dev_row = nullptr;   // [kMaxE + 64] device: a slot-table row, then the first launch's
+                                  // absent-slot flag (never read)
     bool failed = false;
 };
 StepScratch* step_scratch() {
@@ -62,7 +68,7 @@ StepScratch* step_scratch() {
         void *m = nullptr, *h = nullptr, *dv = nullptr;
         const size_t bytes = sizeof(int32_t) * kMaxE;
         if (hipHostMalloc(&m, bytes, hipHostMallocCoherent) != hipSuccess || hipHostMalloc(&h, bytes) != hipSuccess ||
-            hipMalloc(&dv, bytes) != hipSuccess) {
+            hipMalloc(&dv, bytes + 256) != hipSuccess) {
             if (m) (void)hipHostFree(m);
             if (h) (void)hipHostFree(h);
             sc.failed = true;
@@ -172,11 +178,13 @@ extern "C" moe_status moe_decode_step(moe_cache* cache, int n_layers, const moe_
         if (sc) {
             // the experts and the combine go ahead through the slot table as it stands while the host
             // reads the ids and decides: a resident expert's rows are final; a missed expert's rows
-            // (its slot absent, or being refilled) are recomputed below once its copy has landed
+            // (its slot absent, or being refilled) are recomputed below once its copy has landed.
+            // This launch's absent-slot flag goes to a word of the library: the workspace's status
+            // word is the final launches' to set.
             r = cache_wait_background(cache, cs);
             if (r != MOE_OK) return r;
-            r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, row, n_slots, slot_pool,
-                                       slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, compute);
+            r = ffn_grouped_status(ly.x, act, T, d, f, E, k, perm, offsets, counts, row, n_slots, slot_pool,
+                                   slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, sc->dev_row + kMaxE, compute);
             if (r != MOE_OK) return r;
             r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
             if (r != MOE_OK) return r;
@@ -213,9 +221,6 @@ extern "C" moe_status moe_decode_step(moe_cache* cache, int n_layers, const moe_
             for (int e = 0; e < E; ++e) sc->host_row[e] = MOE_SLOT_ELSEWHERE;
             for (int j : missed) sc->host_row[ids[j]] = slots[j];
             MOE_HIP(hipMemcpyAsync(sc->dev_row, sc->host_row, sizeof(int32_t) * E, hipMemcpyHostToDevice, cs));
-            // the first launch flagged the missed experts' absent slots in the workspace status
-            // word; the flag is the second launch's to set
-            MOE_HIP(hipMemsetAsync(ws, 0, sizeof(int32_t), cs));
             r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, sc->dev_row, n_slots,
                                        slot_pool, slot_stride, w, nullptr, y_perm, ws, ws_bytes, compute);
             if (r != MOE_OK) return r;
@@ -300,8 +305,8 @@ extern "C" moe_status moe_decode_step_hybrid(
             // after its copy)
             r = cache_wait_background(cache, cs);
             if (r != MOE_OK) return r;
-            r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, row, n_slots, slot_pool,
-                                       slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, compute);
+            r = ffn_grouped_status(ly.x, act, T, d, f, E, k, perm, offsets, counts, row, n_slots, slot_pool,
+                                   slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, sc->dev_row + kMaxE, compute);
             if (r != MOE_OK) return r;
             r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
             if (r != MOE_OK) return r;
@@ -340,7 +345,6 @@ extern "C" moe_status moe_decode_step_hybrid(
                 for (int e = 0; e < E; ++e) sc->host_row[e] = MOE_SLOT_ELSEWHERE;
                 for (int e : miss) sc->host_row[e] = slots[std::lower_bound(ids.begin(), ids.begin() + n, e) - ids.begin()];
                 MOE_HIP(hipMemcpyAsync(sc->dev_row, sc->host_row, sizeof(int32_t) * E, hipMemcpyHostToDevice, cs));
-                MOE_HIP(hipMemsetAsync(ws, 0, sizeof(int32_t), cs));  // the first launch's absent-slot flag
                 r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, sc->dev_row, n_slots,
                                            slot_pool, slot_stride, w, nullptr, y_perm, ws, ws_bytes, compute);
                 if (r != MOE_OK) return r;
@@ -385,7 +389,6 @@ extern "C" moe_status moe_decode_step_hybrid(
                     ++n_gpu_miss;
                 }
             }
-            MOE_HIP(hipMemsetAsync(ws, 0, sizeof(int32_t), cs));  // the first launch's absent-slot flag
             if (n_gpu_miss > 0) {
                 MOE_HIP(hipMemcpyAsync(dev_table, host_table, sizeof(int32_t) * E, hipMemcpyHostToDevice, cs));
                 r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, dev_table, n_slots,

@@ -50,6 +50,13 @@ moe_status ffn_prepare(FfnArgs& a, const char* fn, const void* x, moe_dtype act,
                        moe_dtype w, const void* shared_w, float* y_perm);
 // Launch the grouped experts: the prefill MFMA GEMM where it applies, else the decode GEMVs.
 moe_status ffn_run(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st);
+// moe_expert_ffn_grouped with the absent-slot flag going to `status` (device int32) instead of the
+// workspace's status word when `status` is not NULL (ffn_dispatch.cpp)
+moe_status ffn_grouped_status(const void* x, moe_dtype act, int T, int d, int f, int E, int k, const int32_t* perm,
+                              const int32_t* offsets, const int32_t* counts, const int32_t* slot_of_expert,
+                              int n_slots, const void* slot_pool, size_t slot_stride, moe_dtype w,
+                              const void* shared_w, float* y_perm, void* ws, size_t ws_bytes, int32_t* status,
+                              moe_stream s);
 
 // decode path: grouped GEMV kernels (ffn_gemv.hip), both projections or one (mode kGateUp = 0,
 // kDown = 1)

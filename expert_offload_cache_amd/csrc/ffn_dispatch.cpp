@@ -117,6 +117,18 @@ moe_status moe_expert_ffn_grouped(const void* x, moe_dtype act, int T, int d, in
                                   const int32_t* slot_of_expert, int n_slots, const void* slot_pool,
                                   size_t slot_stride, moe_dtype w, const void* shared_w, float* y_perm,
                                   void* ws, size_t ws_bytes, moe_stream s) {
+    return moe::ffn_grouped_status(x, act, T, d, f, E, k, perm, offsets, counts, slot_of_expert, n_slots, slot_pool,
+                                   slot_stride, w, shared_w, y_perm, ws, ws_bytes, nullptr, s);
+}
+
+}  // extern "C"
+
+namespace moe {
+moe_status ffn_grouped_status(const void* x, moe_dtype act, int T, int d, int f, int E, int k, const int32_t* perm,
+                              const int32_t* offsets, const int32_t* counts, const int32_t* slot_of_expert,
+                              int n_slots, const void* slot_pool, size_t slot_stride, moe_dtype w,
+                              const void* shared_w, float* y_perm, void* ws, size_t ws_bytes, int32_t* status,
+                              moe_stream s) {
     FfnArgs a;
     moe_status r = ffn_prepare(a, "moe_expert_ffn_grouped", x, act, T, d, f, E, k, perm, offsets, counts,
                                slot_of_expert, n_slots, slot_pool, slot_stride, w, shared_w, y_perm);
@@ -125,10 +137,9 @@ moe_status moe_expert_ffn_grouped(const void* x, moe_dtype act, int T, int d, in
     MOE_CHECK((uintptr_t)ws % 256 == 0, MOE_EINVAL, "moe_expert_ffn_grouped: workspace must be 256-byte aligned");
     size_t need = moe_workspace_bytes(T, d, f, E, k, shared_w != nullptr, act, w);
     MOE_CHECK(ws_bytes >= need, MOE_ENOMEM, "moe_expert_ffn_grouped: workspace %zu < %zu bytes", ws_bytes, need);
-    a.status = (int32_t*)ws;
+    a.status = status ? status : (int32_t*)ws;
     a.plan = (uint8_t*)ws + kWsHeader;
     a.h = (uint8_t*)ws + kWsHeader + kPlanBytes;
     return ffn_run(a, act, w, (hipStream_t)s);
 }
-
-}  // extern "C"
+}  // namespace moe

@@ -302,9 +302,11 @@ MOE_API void moe_cache_destroy(moe_cache* c);
  * moe_cache_mark_read(layer).  A resident expert's rows from the first launch are final; a missed
  * expert's (its slot absent or being refilled) are recomputed.  Outputs, cache decisions and
  * statistics are those of the same calls made one by one (route, lookup, fill, experts, combine,
- * mark_read).  The library holds, per host thread and device, a 4 KB coherent host buffer, a 4 KB
- * pinned host row and a 4 KB device row, allocated on first use until the process ends; when they
- * cannot be allocated the step runs the calls in that order instead.  Buffers as in those calls;
+ * mark_read).  The first launch flags absent slots in a word of the library, not in the workspace's
+ * status word, which only the final launches set.  The library holds, per host thread and device,
+ * a 4 KB coherent host buffer, a 4 KB pinned host row and a 4.25 KB device buffer, allocated on
+ * first use until the process ends; when they cannot be allocated the step runs the calls in that
+ * order instead.  Buffers as in those calls;
  * y_perm [T*k (+T), d] f32; ws: moe_workspace_bytes(T, ...) bytes.  Every layer's x, w_router and
  * y are checked (MOE_EINVAL) before anything is enqueued; later errors return at once, the layers
  * before them enqueued.  Returns the first error. */
