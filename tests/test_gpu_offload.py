@@ -355,3 +355,69 @@ def test_resize_right_after_mark_read_without_a_sync():
     for st, l, y in outs:
         assert np.array_equal(y, ref_dec[(st, l)]), (st, l)
     ref["stack"].close()
+
+
+def test_native_decode_step_several_tokens():
+    """moe_decode_step at T=4 (ids read back by a copy and an event rather than the published word,
+    experts launched ahead of the cache's decision through the slot table as it stands, misses run
+    again after their copies) against the same calls made one by one: outputs bitwise equal, and
+    the same hit/miss sequence, copy plan and statistics, at a capacity that forces misses."""
+    need_gpu()
+    import torch
+    from expert_offload_cache_amd import DECODE_LAYER, decode_step
+    from expert_offload_cache_amd.offload import OffloadStack
+
+    T, C, steps = 4, 16, 12
+    rng = np.random.default_rng(11)
+    # skewed expert popularity, so that the 16 slots see both hits and misses
+    pop = 1.0 / np.arange(1, E + 1) ** 1.5
+    ids = np.stack([rng.choice(E, K, replace=False, p=pop / pop.sum()) for _ in range(steps * L * T)])
+    ids = ids.astype(np.int32).reshape(steps, L, T, K)
+    got = []
+    for native in (True, False):
+        stack = OffloadStack(_wl(), L, C, seed=0, n_images=IMAGES, prefill_tokens=T_PRE)
+        try:
+            stack.prefill()
+            dev = stack.device
+            forced = torch.from_numpy(ids).to(dev)
+            b, ws = stack._buffers(T), stack._workspace(T)
+            xs = [stack.x_dec[l][0:T] for l in range(L)]
+            assert all(x.shape[0] == T for x in xs)
+            ys = [torch.empty_like(b["y"]) for _ in range(L)]
+            host_idx = torch.empty((T, K), dtype=torch.int32, pin_memory=True)
+            outs = []
+            if native:
+                arr = np.zeros(L, dtype=DECODE_LAYER)
+                arr["x"] = [x.data_ptr() for x in xs]
+                arr["w_router"] = [w.data_ptr() for w in stack.w_router]
+                arr["bias"] = [0 if bb is None else bb.data_ptr() for bb in stack.bias]
+                arr["shared_w"] = [0 if sw is None else sw.data_ptr() for sw in stack.shared]
+                arr["y"] = [y.data_ptr() for y in ys]
+                arr["layer"] = np.arange(L)
+            with torch.cuda.stream(stack.compute):
+                for s in range(steps):
+                    if native:
+                        arr["forced"] = [forced[s, l].data_ptr() for l in range(L)]
+                        decode_step(stack.cache, arr, T, D, F, E, K, stack.act_code, stack.wl.wdt, stack.slot_pool,
+                                    stack.n_slots, stack.stride, stack.slot_table, b["route"], b["perm"],
+                                    b["y_perm"], ws, host_idx, stack.compute, stack.copy)
+                    else:
+                        for l in range(L):
+                            _, w, perm = stack._layer(l, xs[l], forced[s, l])
+                            stack.cache.lookup(l, np.unique(ids[s, l]))
+                            stack.cache.fill(stack.copy, stack.compute)
+                            ys[l].copy_(stack._experts(l, xs[l], w, perm))
+                            stack.cache.mark_read(l, stack.compute)
+                    outs += [y_to_f64(y.clone()) for y in ys]
+            stack.compute.synchronize()
+            status = int(ws[:4].view(torch.int32).item())
+            got.append((stack.cache.trace(), stack.cache.copy_log(), stack.cache.stats(), outs, status))
+        finally:
+            stack.close()
+    (t0, c0, st0, o0, s0), (t1, c1, st1, o1, s1) = got
+    assert s0 == s1 == 0
+    assert np.array_equal(t0, t1) and np.array_equal(c0, c1) and st0 == st1
+    assert st0["dec_miss"] > 0 and st0["dec_hit"] > 0
+    assert len(o0) == len(o1) == steps * L
+    for i, (y0, y1) in enumerate(zip(o0, o1)):
+        assert np.array_equal(y0, y1), divmod(i, L)
