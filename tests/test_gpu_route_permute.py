@@ -171,6 +171,8 @@ RP_CASES = [
     ("bf16", 512, 40, 40, 66, 1.1, "rand"),
     ("bf16", 4096, 256, 6, 2048, 1.1, "rand"),
     ("f32", 128, 8, 2, 4500, None, "rand"),
+    ("f32", 128, 8, 2, 1, None, "rand"),       # one token, binary32 activations
+    ("f32", 192, 100, 7, 1, 1.1, "forced"),
 ]
 
 
