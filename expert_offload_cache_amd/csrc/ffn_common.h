@@ -76,6 +76,100 @@ __device__ __forceinline__ bool find_work(const int32_t* __restrict__ counts, in
     return true;
 }
 
+// find_work that also returns the item's slot, token count and first sorted row (the shared expert:
+// slot -1, T tokens, row T*k).  The counts and the slot-table row are loaded together, and the
+// expert's first row is the exclusive prefix sum of the counts (what offsets holds), so the item's
+// weights can be addressed after one round of loads instead of two.
+// (MAXPER experts a lane at most: E <= 64 * MAXPER)
+template <int kMaxPer>
+__device__ __forceinline__ bool find_work_slot(const int32_t* __restrict__ counts, const int32_t* __restrict__ slots,
+                                               int E, int T, int k, int ntg, bool has_shared, int a, int& e_out,
+                                               int& chunk_out, int& slot_out, int& n_out, int& p0_out, int n_lo,
+                                               int n_hi) {
+    const int lane = threadIdx.x & 63;
+    const int per = (E + 63) / 64;
+    has_shared = has_shared && T >= n_lo && T <= n_hi;
+    auto chunks = [&](int n) { return (n >= n_lo && n <= n_hi) ? (n + ntg - 1) / ntg : 0; };
+    int cnt[kMaxPer], sl[kMaxPer];
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+        const int e = lane * per + i;
+        const bool in = i < per && e < E;
+        cnt[i] = in ? counts[e] : 0;
+        sl[i] = in ? slots[e] : 0;
+    }
+    int nz = 0, rows = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+        nz += chunks(cnt[i]);
+        rows += cnt[i];
+    }
+    int incl = nz, rincl = rows;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+        const int v = __shfl_up(incl, s, 64), rv = __shfl_up(rincl, s, 64);
+        if (lane >= s) {
+            incl += v;
+            rincl += rv;
+        }
+    }
+    const int total = __shfl(incl, 63, 64);
+    if (a >= total) {
+        const int c = a - total;
+        if (!has_shared || c >= (T + ntg - 1) / ntg) return false;
+        e_out = -1;
+        chunk_out = __builtin_amdgcn_readfirstlane(c);
+        slot_out = -1;
+        n_out = T;
+        p0_out = T * k;
+        return true;
+    }
+    const int excl = incl - nz;
+    int found = -1, chunk = 0, fslot = 0, fn = 0, fp0 = 0;
+    if (a >= excl && a < incl) {
+        int r = a - excl, row = rincl - rows;  // this lane's first expert's first sorted row
+#pragma unroll
+        for (int i = 0; i < kMaxPer; ++i) {
+            const int ce = chunks(cnt[i]);
+            if (found < 0) {
+                if (r < ce) {
+                    found = lane * per + i;
+                    chunk = r;
+                    fslot = sl[i];
+                    fn = cnt[i];
+                    fp0 = row;
+                } else {
+                    r -= ce;
+                    row += cnt[i];
+                }
+            }
+        }
+    }
+    const int src = (int)__builtin_ctzll(__ballot(found >= 0));
+    e_out = __builtin_amdgcn_readfirstlane(__shfl(found, src, 64));
+    chunk_out = __builtin_amdgcn_readfirstlane(__shfl(chunk, src, 64));
+    slot_out = __builtin_amdgcn_readfirstlane(__shfl(fslot, src, 64));
+    n_out = __builtin_amdgcn_readfirstlane(__shfl(fn, src, 64));
+    p0_out = __builtin_amdgcn_readfirstlane(__shfl(fp0, src, 64));
+    return true;
+}
+
+// Work item `a` of a launch -> (expert, chunk, slot, tokens of the expert, its first sorted row):
+// find_work_slot where a lane covers at most 4 experts (E <= 256), else find_work and then the
+// expert's slot, count and offset.
+__device__ __forceinline__ bool find_item(const FfnArgs& f, int ntg, int a, int& e, int& chunk, int& slot, int& n,
+                                          int& p0) {
+    if (f.E <= 256)
+        return find_work_slot<4>(f.counts, f.slot_of_expert, f.E, f.T, f.k, ntg, f.shared_w != nullptr, a, e, chunk,
+                                 slot, n, p0, f.n_lo, f.n_hi);
+    if (!find_work(f.counts, f.E, f.T, ntg, f.shared_w != nullptr, a, e, chunk, f.n_lo, f.n_hi)) return false;
+    const bool shared = e == -1;
+    slot = shared ? -1 : __builtin_amdgcn_readfirstlane(f.slot_of_expert[e]);
+    n = __builtin_amdgcn_readfirstlane(shared ? f.T : f.counts[e]);
+    p0 = __builtin_amdgcn_readfirstlane(shared ? f.T * f.k : f.offsets[e]);
+    return true;
+}
+
 template <int W>
 struct Frag;
 template <>

@@ -87,17 +87,14 @@ __global__ __launch_bounds__(64 * S * GR) void ffn_gemv_deep_kernel(FfnArgs a) {
     const int nst = K / KIN;  // = S * NS (checked on the host)
     const int ks_base = si * NS;
 
-    int e, chunk;
-    if (!find_work(a.counts, a.E, a.T, 16, a.shared_w != nullptr, blockIdx.y, e, chunk, a.n_lo, a.n_hi)) return;
+    int e, chunk, slot, nt, p0;  // nt: 1 .. kDeepTok
+    if (!find_item(a, 16, blockIdx.y, e, chunk, slot, nt, p0)) return;
     const bool shared = (e == -1);
-    const int nt = __builtin_amdgcn_readfirstlane(shared ? a.T : a.counts[e]);  // 1 .. kDeepTok
-    const int p0 = __builtin_amdgcn_readfirstlane(shared ? a.T * a.k : a.offsets[e]);
     const int orow0 = (blockIdx.x * GR + gi) * NOUT;
     const uint8_t* base;
     if (shared) {
         base = a.shared_w;
     } else {
-        const int slot = __builtin_amdgcn_readfirstlane(a.slot_of_expert[e]);
         if (slot == MOE_SLOT_ELSEWHERE) return;  // rows produced elsewhere: leave them (whole workgroup)
         if (slot < 0 || slot >= a.n_slots) {
             // absent or invalid slot: flag it and give the expert's rows zeros; nothing is read

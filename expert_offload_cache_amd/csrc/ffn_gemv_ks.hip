@@ -83,13 +83,11 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
     const int ks_base = IL ? si : si * nsw;
     constexpr int kStep = IL ? S : 1;
 
-    int e, chunk;
-    if (!find_work(a.counts, a.E, a.T, NTG, a.shared_w != nullptr, blockIdx.y, e, chunk, a.n_lo, a.n_hi)) return;
+    int e, chunk, slot, n_all, p0;
+    if (!find_item(a, NTG, blockIdx.y, e, chunk, slot, n_all, p0)) return;
     const bool shared = (e == -1);
-    const int n_all = __builtin_amdgcn_readfirstlane(shared ? a.T : a.counts[e]);
     const int i0 = chunk * NTG;  // this item's tokens: i0 .. i0 + nt - 1
     const int nt = __builtin_amdgcn_readfirstlane(min(NTG, n_all - i0));
-    const int p0 = __builtin_amdgcn_readfirstlane(shared ? a.T * a.k : a.offsets[e]);
     // first output row (16 per row block, or per gate/up pair) of this wave
     const int orow0 = (blockIdx.x * (kKsWaves / S) + wv / S) * (MODE == kGateUp ? RA / 2 : RA) * 16;
     constexpr int NOUT = (MODE == kGateUp ? RA / 2 : RA) * 16;
@@ -97,7 +95,6 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
     if (shared) {
         base = a.shared_w;
     } else {
-        const int slot = __builtin_amdgcn_readfirstlane(a.slot_of_expert[e]);
         if (slot == MOE_SLOT_ELSEWHERE) return;  // rows produced elsewhere: leave them
         if (slot < 0 || slot >= a.n_slots) {
             // absent or invalid slot: flag it and give the expert's rows zeros; nothing is read

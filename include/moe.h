@@ -157,7 +157,9 @@ MOE_API moe_status moe_route_permute(const void* x, moe_dtype act, int T, int d,
  * plain reading of the expert form: h = silu(x W_g^T) * (x W_u^T), y = h W_d^T, no biases).
  * Expert e's weights are read from the slot slot_of_expert[e] of slot_pool (FreeToken GGUF
  * page, offload backend: expert slots on the GPU), i.e. at slot_pool + slot * slot_stride.
- *   x [T,d] act; perm, offsets, counts from moe_permute; slot_of_expert [E] int32 (a device
+ *   x [T,d] act; perm, offsets, counts from moe_permute (offsets must be the exclusive prefix
+ *   sums of counts, as moe_permute writes them: an expert's first row may be taken from either);
+ *   slot_of_expert [E] int32 (a device
  *   row of the slot table; MOE_SLOT_ELSEWHERE (-2) means the expert's rows of y_perm are
  *   produced elsewhere, e.g. on the host (hybrid miss handling), and are left untouched; any
  *   other slot outside [0, n_slots) sets the workspace status word to 1 and that expert's rows
