@@ -9,15 +9,18 @@
 // one expert (or the shared expert) and its weights are read exactly once.  The launch is bound by
 // how many bytes are in flight: a wave that streams its share of an expert a stage at a time waits
 // one memory round trip per stage or two.  Here a wave instead issues all of its loads before it
-// multiplies anything, in the order it will use them:
-//   1. its input share of the item's activation rows, straight into LDS (direct-to-LDS loads; the
-//      S waves that split the inputs take contiguous shares, and the GR row groups of a workgroup
-//      share the rows: wave (si, gi) loads the rows gi, gi + GR, ... of share si);
-//   2. int4: the group scales of its rows for its stages (one 16- or 8-byte load per row block);
-//   3. its weight fragments, stage by stage (NS stages x RA row blocks, one 16-byte non-temporal
-//      load per lane each: 16-32 KB a wave);
+// multiplies anything:
+//   - its input share of the item's activation rows, straight into LDS (direct-to-LDS loads; the
+//     S waves that split the inputs take contiguous shares, and the GR row groups of a workgroup
+//     share the rows: wave (si, gi) loads the rows gi, gi + GR, ... of share si);
+//   - int4: the group scales of its rows for its stages (one 16- or 8-byte load per row block);
+//   - its weight fragments, stage by stage (NS stages x RA row blocks, one 16-byte non-temporal
+//     load per lane each: 16-32 KB a wave);
 // then waits for the activation loads only, meets the workgroup once, and multiplies stage by stage
-// as the weight loads land (vector loads return in issue order).  The S partial sums of a row block
+// as the weight loads land (vector loads return in issue order).  For gate/up with several tokens
+// the activation rows' addresses need the permutation entries: those are loaded first, and the
+// scales and the first half of the weight stages go out before the activation rows, so the
+// weights do not wait for that round trip.  The S partial sums of a row block
 // are joined through LDS in share order; SiLU(g)*u (rounded to bf16) or the down output is written
 // from registers.
 //
@@ -112,7 +115,59 @@ __global__ __launch_bounds__(64 * S * GR) void ffn_gemv_deep_kernel(FfnArgs a) {
         base = a.pool + (size_t)slot * a.stride;
     }
 
-    // ---- 1. activation rows of share si -> LDS [nt][SHARE], contiguous rows --------------------
+    // Issue order.  Gate/up with several tokens: the permutation entries first, then the group
+    // scales and the first half of the weight stages, then the activation rows (their addresses
+    // need the entries), then the second half; the multiply starts once the activations (and so
+    // the first half) have landed.  Otherwise (one token, or down: no entry to wait for): the
+    // activation rows, the scales, then every weight stage.
+    const bool split = MODE == kGateUp && a.T > 1;
+    const int H = split ? NS / 2 : 0;  // weight stages issued before the activation rows
+    int pe = 0;
+    if (MODE == kGateUp && split && !shared) pe = a.perm[p0 + min(lane, nt - 1)];
+    asm volatile("" ::: "memory");
+
+    const uint8_t* wp[RA];
+#pragma unroll
+    for (int u = 0; u < RA; ++u) {
+        if constexpr (MODE == kGateUp)
+            wp[u] = base + gu_block_offset(orow0 / 16 + u / 2, u & 1, a.d, (moe_dtype)W);
+        else
+            wp[u] = base + down_block_offset(orow0 / 16 + u, a.d, a.f, (moe_dtype)W);
+    }
+    u32x4_t sc[RA][kInt4 ? NSC : 1];
+    auto issue_scales = [&]() __attribute__((always_inline)) {
+        if constexpr (kInt4) {
+#pragma unroll
+            for (int u = 0; u < RA; ++u)
+#pragma unroll
+                for (int c = 0; c < NSC; ++c) {
+                    const uint8_t* p = wp[u] + (size_t)nst * 1024 + ((size_t)r16 * nst + ks_base) * 2 + c * SCV;
+                    if constexpr (SCV == 16) {
+                        sc[u][c] = *(const u32x4_t*)p;
+                    } else {
+                        const uint2 v = *(const uint2*)p;
+                        sc[u][c] = u32x4_t{v.x, v.y, 0u, 0u};
+                    }
+                }
+        }
+    };
+    u32x4_t w[NS][RA];
+    auto issue_stages = [&](int s0, int s1) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            if (s >= s0 && s < s1)
+#pragma unroll
+                for (int u = 0; u < RA; ++u)
+                    w[s][u] =
+                        __builtin_nontemporal_load((const u32x4_t*)(wp[u] + (size_t)(ks_base + s) * 1024 + lane * 16));
+        asm volatile("" ::: "memory");
+    };
+    if (split) {
+        issue_scales();
+        issue_stages(0, H);
+    }
+
+    // ---- activation rows of share si -> LDS [nt][SHARE], contiguous rows -------------------------
     const uint8_t* in_base = (MODE == kGateUp) ? (const uint8_t*)a.x : (const uint8_t*)a.h;
     // share si's region: nt rows, rounded up to whole 1 KB load blocks (the last block's overrun)
     uint8_t* xs = smem + (size_t)si * ((nt * SHARE + 1023) / 1024 * 1024);
@@ -120,7 +175,7 @@ __global__ __launch_bounds__(64 * S * GR) void ffn_gemv_deep_kernel(FfnArgs a) {
         // lane i: token row i (clamped) of the item, as a source row index
         const int i = min(lane, nt - 1);
         int src_row;
-        if (MODE == kGateUp) src_row = shared ? i : (a.T == 1 ? 0 : a.perm[p0 + i] / a.k);
+        if (MODE == kGateUp) src_row = shared ? i : (split ? pe / a.k : 0);
         else src_row = p0 + i;
         const int nvec = nt * (SHARE / 16);  // 16-byte vectors of the share
         // wave gi takes the 64-vector blocks gi, gi + GR, ... (each lands contiguously in LDS)
@@ -133,40 +188,12 @@ __global__ __launch_bounds__(64 * S * GR) void ffn_gemv_deep_kernel(FfnArgs a) {
         }
     }
     asm volatile("" ::: "memory");
-
-    // ---- 2, 3. scales and weights, all issued now ----------------------------------------------
-    const uint8_t* wp[RA];
-#pragma unroll
-    for (int u = 0; u < RA; ++u) {
-        if constexpr (MODE == kGateUp)
-            wp[u] = base + gu_block_offset(orow0 / 16 + u / 2, u & 1, a.d, (moe_dtype)W);
-        else
-            wp[u] = base + down_block_offset(orow0 / 16 + u, a.d, a.f, (moe_dtype)W);
-    }
-    u32x4_t sc[RA][kInt4 ? NSC : 1];
-    if constexpr (kInt4) {
-#pragma unroll
-        for (int u = 0; u < RA; ++u)
-#pragma unroll
-            for (int c = 0; c < NSC; ++c) {
-                const uint8_t* p = wp[u] + (size_t)nst * 1024 + ((size_t)r16 * nst + ks_base) * 2 + c * SCV;
-                if constexpr (SCV == 16) {
-                    sc[u][c] = *(const u32x4_t*)p;
-                } else {
-                    const uint2 v = *(const uint2*)p;
-                    sc[u][c] = u32x4_t{v.x, v.y, 0u, 0u};
-                }
-            }
-    }
-    u32x4_t w[NS][RA];
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int u = 0; u < RA; ++u)
-            w[s][u] = __builtin_nontemporal_load((const u32x4_t*)(wp[u] + (size_t)(ks_base + s) * 1024 + lane * 16));
-    asm volatile("" ::: "memory");
-    // the activation loads (issued before the NLATER others) have landed, in every wave
-    wait_vm<NLATER>();
+    if (!split) issue_scales();
+    issue_stages(H, NS);
+    // the activation loads (issued before the scales or the remaining weight stages) have landed,
+    // in every wave
+    if (split) wait_vm<(NS - NS / 2) * RA>();
+    else wait_vm<NLATER>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 

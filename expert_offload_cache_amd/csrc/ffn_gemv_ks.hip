@@ -121,13 +121,27 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
     // token group j: this lane's token 16 j + l%16 (clamped to the chunk; the clamped columns
     // are computed and dropped), input quarter l/16
     const uint8_t* in_base = (MODE == kGateUp) ? (const uint8_t*)a.x : (const uint8_t*)a.h;
-    const uint8_t* xp[G];
+    // gate/up: the token groups' permutation entries, loaded together and used only after the
+    // first stages' weight loads are issued below (the shared expert loads entries it ignores)
+    int pe[G];
+    if constexpr (MODE == kGateUp && !XL) {
+        const int32_t* pb = a.perm + (shared ? 0 : p0 + i0);
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-        const int i = min(16 * j + r16, nt - 1);
-        const int row = (MODE == kGateUp) ? (shared ? (i0 + i) : (a.perm[p0 + i0 + i] / a.k)) : (p0 + i0 + i);
-        xp[j] = in_base + (size_t)row * K * 2 + q * 16;
+        for (int j = 0; j < G; ++j) pe[j] = pb[min(16 * j + r16, nt - 1)];
+        asm volatile("" ::: "memory");  // keep these loads ahead of the weight loads
     }
+    const uint8_t* xp[G];
+    auto set_rows = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int i = min(16 * j + r16, nt - 1);
+            int row;
+            if constexpr (MODE == kGateUp && !XL) row = shared ? (i0 + i) : pe[j] / a.k;
+            else row = (MODE == kGateUp) ? (shared ? (i0 + i) : (a.perm[p0 + i0 + i] / a.k)) : (p0 + i0 + i);
+            xp[j] = in_base + (size_t)row * K * 2 + q * 16;
+        }
+    };
+    if constexpr (XL) set_rows();
 
     // XL: the item's activation rows (at most kXlTok) are staged in LDS once, so only weight
     // loads go through the in-order load queue and the stages read their activations from LDS
@@ -157,14 +171,16 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
     uint32_t sst[R][kInt4 ? RA : 1];
     // local stage ks into register set (w, x, s); past the end of the share its last stage is
     // repeated (never used)
-    auto issue = [&](int ks, u32x4_t (&w)[RA], u32x4_t (&x)[G][XV], uint32_t (&s)[kInt4 ? RA : 1])
-        __attribute__((always_inline)) {
+    auto issue_x = [&](int ks, u32x4_t (&x)[G][XV]) __attribute__((always_inline)) {
         ks = ks_base + kStep * min(ks, nsw - 1);
 #pragma unroll
         for (int j = 0; j < G; ++j)
             if (!XL && (j == 0 || 16 * j < nt))  // token groups the item does not fill are not loaded
 #pragma unroll
                 for (int v = 0; v < XV; ++v) x[j][v] = *(const u32x4_t*)(xp[j] + (size_t)ks * (XV * 64) + v * 64);
+    };
+    auto issue_w = [&](int ks, u32x4_t (&w)[RA], uint32_t (&s)[kInt4 ? RA : 1]) __attribute__((always_inline)) {
+        ks = ks_base + kStep * min(ks, nsw - 1);
         if constexpr (kInt4) {
 #pragma unroll
             for (int u = 0; u < RA; ++u)
@@ -173,6 +189,11 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
 #pragma unroll
         for (int u = 0; u < RA; ++u)
             w[u] = __builtin_nontemporal_load((const u32x4_t*)(wp[u] + (size_t)ks * 1024 + lane * 16));
+    };
+    auto issue = [&](int ks, u32x4_t (&w)[RA], u32x4_t (&x)[G][XV], uint32_t (&s)[kInt4 ? RA : 1])
+        __attribute__((always_inline)) {
+        issue_x(ks, x);
+        issue_w(ks, w, s);
     };
 
     f32x4_t acc[RA][G];
@@ -231,8 +252,12 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
         }
     };
 
+    // the first stages' weights go out before the activation rows' addresses are known
 #pragma unroll
-    for (int s = 0; s < R - 1; ++s) issue(s, wst[s], xst[s], sst[s]);
+    for (int s = 0; s < R - 1; ++s) issue_w(s, wst[s], sst[s]);
+    if constexpr (!XL) set_rows();
+#pragma unroll
+    for (int s = 0; s < R - 1; ++s) issue_x(s, xst[s]);
     for (int ks0 = 0; ks0 < nsw; ks0 += R) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
