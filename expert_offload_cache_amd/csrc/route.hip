@@ -291,13 +291,29 @@ __device__ void select_and_gate(const float* s_logit, int E, int k, const int32_
         // P adjacent lanes share an expert, each counting the experts i = p (mod P) that beat it;
         // the partial counts are summed over the P lanes
         const int P = nth >= 4 * E ? 4 : nth >= 2 * E ? 2 : 1;
+        // with E a multiple of 4P each lane takes a contiguous quarter (or half, or all) of the
+        // experts and reads them four at a time: a quarter of the LDS reads, which bound this loop
+        // (s_logit is 16-byte aligned)
+        const bool vec = E % (4 * P) == 0;
+        const int span = E / P;
         for (int b = tid; b < E * P; b += nth) {
             const int e = b / P, p = b - e * P;
             const float v = s_logit[e];
             int r = 0;
             // unrolled so that the LDS reads issue back to back (an integer count: order-free)
+            if (vec) {
+                const float4* s4 = (const float4*)(s_logit + p * span);
+#pragma unroll 4
+                for (int c = 0; c < span / 4; ++c) {
+                    const float4 q = s4[c];
+                    const int i = p * span + 4 * c;
+                    r += better(q.x, i, v, e) + better(q.y, i + 1, v, e) + better(q.z, i + 2, v, e) +
+                         better(q.w, i + 3, v, e);
+                }
+            } else {
 #pragma unroll 8
-            for (int i = p; i < E; i += P) r += better(s_logit[i], i, v, e);
+                for (int i = p; i < E; i += P) r += better(s_logit[i], i, v, e);
+            }
             if (P >= 2) r += __shfl_xor(r, 1, 64);
             if (P >= 4) r += __shfl_xor(r, 2, 64);
             if (p == 0 && r < k) {
