@@ -60,10 +60,13 @@ moe_status ffn_prepare(FfnArgs& a, const char* fn, const void* x, moe_dtype act,
 }
 
 // experts with fewer tokens than this run on the decode kernels in prefill (int4: measured on the
-// DeepSeek-V4-Flash shaped layer, FFN 1082 -> 685 us at 512 tokens, 1811 -> 1377 us at 2048; bf16
-// weights gain nothing, the light experts' launch is bound by HBM either way)
+// DeepSeek-V4-Flash shaped layer, FFN 1082 -> 685 us at 512 tokens, 1811 -> 1377 us at 2048 with
+// 32; 28 then measured 8 % faster at 512 tokens and 2-5 % at 2048 than 32, 20 and 24 in between,
+// equal at 8192: an expert holding 28-31 tokens fills two 16-token items of the decode kernel and
+// reads its weights twice; bf16 weights gain nothing, the light experts' launch is bound by HBM
+// either way)
 #ifndef MOE_SPLIT_INT4
-#define MOE_SPLIT_INT4 32
+#define MOE_SPLIT_INT4 28
 #endif
 #ifndef MOE_SPLIT_BF16
 #define MOE_SPLIT_BF16 0
