@@ -174,8 +174,8 @@ MOE_API moe_status moe_route_permute(const void* x, moe_dtype act, int T, int d,
 /* Above 64 tokens (prefill) the experts run on the matrix-core grouped GEMM, which feeds int4
  * weights to the matrix cores as bf16(q * s).  Experts holding at most moe_prefill_gemv_tokens(w)
  * tokens instead run on the decode kernels (their weights are streamed once and no 128-token tile
- * is left mostly empty); those take exact q * s products.  The shared expert always holds T tokens.
- * 0 = every expert on the GEMM. */
+ * is left mostly empty); those take exact q * s products.  For bf16 weights this applies only to
+ * calls with T*k <= 64*E.  The shared expert always holds T tokens.  0 = every expert on the GEMM. */
 MOE_API int moe_prefill_gemv_tokens(moe_dtype w);
 MOE_API size_t moe_workspace_bytes(int T, int d, int f, int E, int k, int has_shared,
                                    moe_dtype act, moe_dtype w);
