@@ -10,12 +10,16 @@ import numpy as np
 from .numerics import round_to_bf16
 
 
-def swiglu_expert(a: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, h_bf16: bool = False) -> np.ndarray:
+def swiglu_expert(a: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, h_bf16: bool = False,
+                  y_bf16: bool = False) -> np.ndarray:
     """a: [n, d] float64 -> [n, d] float64.  h_bf16: h rounded to bfloat16 before the down
-    projection, as the bf16 layers may store it (otherwise h stays float64)."""
+    projection, as the bf16 layers may store it (otherwise h stays float64).  y_bf16: the expert's
+    output rows rounded to bfloat16, as a bf16 prefill may store them before the gate-weighted
+    combine (the intermediate rows of a bf16 layer may be bf16, like h)."""
     g = a @ wg.T
     u = a @ wu.T
     h = (g / (1.0 + np.exp(-g))) * u
     if h_bf16:
         h = round_to_bf16(h)
-    return h @ wd.T
+    y = h @ wd.T
+    return round_to_bf16(y) if y_bf16 else y

@@ -1,5 +1,5 @@
 """Pins of the oracle's bfloat16 rounding modes (oracle/numerics.py round_to_bf16, the int4
-weights seen as bf16(q * s), and SwiGLU with h rounded to bf16): hand cases, then the bit-level
+weights seen as bf16(q * s), SwiGLU with h and with the output rows rounded to bf16): hand cases, then the bit-level
 round-to-nearest-even of binary32 patterns as an independent method."""
 import numpy as np
 
@@ -55,3 +55,27 @@ def test_swiglu_with_h_rounded():
     # the two roundings can differ only where h's float64 value lies within a binary32 ulp of a tie
     assert np.max(np.abs(got - want)) <= 1e-6 * np.max(np.abs(want))
     assert not np.array_equal(got, swiglu_expert(a, wg, wu, wd))
+
+
+def test_swiglu_with_y_rounded_hand_cases():
+    # one input, one hidden unit: silu(64) is 64 in binary64 (exp(-64) is far below half an ulp of
+    # 1), u = 1, so y = 64 wd exactly; wd = (1 + 2^-8)/64 and (1 + 3*2^-8)/64 put y on the two ties
+    # of the rounding hand cases above (to 1.0 and up to 1.015625), and (1 + 2^-7)/64 on a bf16 value
+    a = np.array([[1.0]])
+    wg, wu = np.array([[64.0]]), np.array([[1.0]])
+    wd = np.array([[(1 + 2.0 ** -8) / 64], [(1 + 3 * 2.0 ** -8) / 64], [(1 + 2.0 ** -7) / 64], [-(1 + 2.0 ** -8) / 64]])
+    assert swiglu_expert(a, wg, wu, wd).tolist() == [[1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -7, -(1 + 2.0 ** -8)]]
+    assert swiglu_expert(a, wg, wu, wd, y_bf16=True).tolist() == [[1.0, 1.015625, 1.0078125, -1.0]]
+
+
+def test_swiglu_with_y_rounded_is_a_bf16_value_within_half_an_ulp():
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal((7, 96))
+    wg, wu, wd = (rng.standard_normal(s) * 0.1 for s in ((48, 96), (48, 96), (96, 48)))
+    y = swiglu_expert(a, wg, wu, wd, h_bf16=True)
+    yr = swiglu_expert(a, wg, wu, wd, h_bf16=True, y_bf16=True)
+    bits = yr.astype(np.float32).view(np.uint32)
+    assert np.array_equal(yr.astype(np.float32).astype(np.float64), yr)  # binary32-exact
+    assert np.all(bits & 0xFFFF == 0)  # and a bf16 value
+    assert np.all(np.abs(yr - y) <= np.abs(y) * 2.0 ** -8)  # unit roundoff of 8 significant bits
+    assert not np.array_equal(yr, y)
