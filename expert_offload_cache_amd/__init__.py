@@ -35,6 +35,23 @@ def _act(t) -> int:
     raise TypeError(f"activations must be float32 or bfloat16, got {t.dtype}")
 
 
+def _y_code(t) -> int:
+    """Element type code of a y_perm tensor (float32 or bfloat16)."""
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"y_perm must be float32 or bfloat16, got {t.dtype}")
+
+
+def y_perm_dtype(act_dtype, T: int):
+    """The y_perm element type the layer orchestration uses: bfloat16 for bf16 prefill (more than 64
+    tokens, the matrix-core path), where the intermediate rows may be bf16; float32 otherwise."""
+    torch = _torch()
+    return torch.bfloat16 if act_dtype == torch.bfloat16 and T > 64 else torch.float32
+
+
 def _p(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -121,8 +138,10 @@ def workspace_bytes(T, d, f, E, k, has_shared, act: int, wdt: int) -> int:
 
 
 def expert_ffn_grouped(x, perm, offsets, counts, slot_of_expert, slot_pool, n_slots: int, slot_stride: int,
-                       wdt: str, f: int, k: int, shared_w=None, y_perm=None, ws=None, stream=None):
-    """Grouped SwiGLU experts through the slot table. -> (y_perm f32 [T*k (+T), d], ws)."""
+                       wdt: str, f: int, k: int, shared_w=None, y_perm=None, ws=None, stream=None, y_dtype=None):
+    """Grouped SwiGLU experts through the slot table. -> (y_perm [T*k (+T), d], ws).  y_perm's element
+    type is that of the given tensor (float32, or bfloat16 with bf16 activations), else y_dtype
+    (a torch dtype, default float32)."""
     torch = _torch()
     _contig(x, perm, offsets, counts, slot_of_expert)
     T, d = x.shape
@@ -130,13 +149,13 @@ def expert_ffn_grouped(x, perm, offsets, counts, slot_of_expert, slot_pool, n_sl
     act = _act(x)
     rows = T * k + (T if shared_w is not None else 0)
     if y_perm is None:
-        y_perm = torch.empty((rows, d), dtype=torch.float32, device=x.device)
+        y_perm = torch.empty((rows, d), dtype=y_dtype or torch.float32, device=x.device)
     if ws is None:
         need = workspace_bytes(T, d, f, E, k, shared_w is not None, act, WDT[wdt])
         ws = torch.zeros(need, dtype=torch.uint8, device=x.device)
     check(lib().moe_expert_ffn_grouped(_p(x), act, T, d, f, E, k, _p(perm), _p(offsets), _p(counts),
                                        _p(slot_of_expert), n_slots, _p(slot_pool), slot_stride, WDT[wdt],
-                                       _p(shared_w), _p(y_perm), _p(ws), ws.numel(), _s(stream)))
+                                       _p(shared_w), _p(y_perm), _y_code(y_perm), _p(ws), ws.numel(), _s(stream)))
     return y_perm, ws
 
 
@@ -150,7 +169,7 @@ def expert_ffn_grouped_noalloc(x, perm, offsets, counts, slot_of_expert, slot_po
     E = counts.shape[0]
     check(lib().moe_expert_ffn_grouped_noalloc(_p(x), _act(x), T, d, f, E, k, _p(perm), _p(offsets), _p(counts),
                                                _p(slot_of_expert), n_slots, _p(slot_pool), slot_stride, WDT[wdt],
-                                               _p(shared_w), _p(y_perm), _p(status), _s(stream)))
+                                               _p(shared_w), _p(y_perm), _y_code(y_perm), _p(status), _s(stream)))
     return y_perm
 
 
@@ -162,8 +181,8 @@ def combine(y_perm, topk_w, inv_perm, k: int, has_shared: bool, out_dtype, y=Non
     if y is None:
         y = torch.empty((T, d), dtype=out_dtype, device=y_perm.device)
     code = MOE_BF16 if y.dtype == torch.bfloat16 else MOE_F32
-    check(lib().moe_combine(_p(y_perm), _p(topk_w), _p(inv_perm), T, k, d, int(bool(has_shared)), _p(y), code,
-                            _s(stream)))
+    check(lib().moe_combine(_p(y_perm), _y_code(y_perm), _p(topk_w), _p(inv_perm), T, k, d, int(bool(has_shared)),
+                            _p(y), code, _s(stream)))
     return y
 
 

@@ -27,11 +27,11 @@ SIGNATURES = {
     "moe_permute_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_expert_ffn_grouped": (_st, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _sz,
-                                     _i32, _vp, _vp, _vp, _sz, _vp]),
+                                     _i32, _vp, _vp, _i32, _vp, _sz, _vp]),
     "moe_expert_ffn_grouped_noalloc": (_st, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32,
-                                             _vp, _sz, _i32, _vp, _vp, _vp, _vp]),
+                                             _vp, _sz, _i32, _vp, _vp, _i32, _vp, _vp]),
     "moe_prefill_gemv_tokens": (_i32, [_i32]),
-    "moe_combine": (_st, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
+    "moe_combine": (_st, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
     "moe_decode_step": (_st, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _sz, _vp, _vp, _vp,
                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
     "moe_decode_step_split": (_st, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _sz, _vp,

@@ -30,8 +30,8 @@ moe_status route_permute_publish(const void* x, moe_dtype act, int T, int d, con
 moe_status ffn_grouped_status(const void* x, moe_dtype act, int T, int d, int f, int E, int k, const int32_t* perm,
                               const int32_t* offsets, const int32_t* counts, const int32_t* slot_of_expert,
                               int n_slots, const void* slot_pool, size_t slot_stride, moe_dtype w,
-                              const void* shared_w, float* y_perm, void* ws, size_t ws_bytes, int32_t* status,
-                              moe_stream s);  // ffn_dispatch.cpp
+                              const void* shared_w, void* y_perm, moe_dtype y_dtype, void* ws, size_t ws_bytes,
+                              int32_t* status, moe_stream s);  // ffn_dispatch.cpp
 }
 
 namespace {
@@ -184,9 +184,9 @@ extern "C" moe_status moe_decode_step(moe_cache* cache, int n_layers, const moe_
             r = cache_wait_background(cache, cs);
             if (r != MOE_OK) return r;
             r = ffn_grouped_status(ly.x, act, T, d, f, E, k, perm, offsets, counts, row, n_slots, slot_pool,
-                                   slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, sc->dev_row + kMaxE, compute);
+                                   slot_stride, w, ly.shared_w, y_perm, MOE_F32, ws, ws_bytes, sc->dev_row + kMaxE, compute);
             if (r != MOE_OK) return r;
-            r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
+            r = moe_combine(y_perm, MOE_F32, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
             if (r != MOE_OK) return r;
         }
         r = ids_wait(T, k, mirror, host_idx, ev, compute);
@@ -209,9 +209,9 @@ extern "C" moe_status moe_decode_step(moe_cache* cache, int n_layers, const moe_
         if (r != MOE_OK) return r;
         if (!sc) {
             r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, row, n_slots, slot_pool,
-                                       slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, compute);
+                                       slot_stride, w, ly.shared_w, y_perm, MOE_F32, ws, ws_bytes, compute);
             if (r != MOE_OK) return r;
-            r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
+            r = moe_combine(y_perm, MOE_F32, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
             if (r != MOE_OK) return r;
         } else if (!missed.empty()) {
             // the missed experts again, after their copies (the fill made `compute` wait for them):
@@ -222,9 +222,9 @@ extern "C" moe_status moe_decode_step(moe_cache* cache, int n_layers, const moe_
             for (int j : missed) sc->host_row[ids[j]] = slots[j];
             MOE_HIP(hipMemcpyAsync(sc->dev_row, sc->host_row, sizeof(int32_t) * E, hipMemcpyHostToDevice, cs));
             r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, sc->dev_row, n_slots,
-                                       slot_pool, slot_stride, w, nullptr, y_perm, ws, ws_bytes, compute);
+                                       slot_pool, slot_stride, w, nullptr, y_perm, MOE_F32, ws, ws_bytes, compute);
             if (r != MOE_OK) return r;
-            r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
+            r = moe_combine(y_perm, MOE_F32, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
             if (r != MOE_OK) return r;
         }
         r = moe_cache_mark_read(cache, ly.layer, compute);
@@ -306,9 +306,9 @@ extern "C" moe_status moe_decode_step_hybrid(
             r = cache_wait_background(cache, cs);
             if (r != MOE_OK) return r;
             r = ffn_grouped_status(ly.x, act, T, d, f, E, k, perm, offsets, counts, row, n_slots, slot_pool,
-                                   slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, sc->dev_row + kMaxE, compute);
+                                   slot_stride, w, ly.shared_w, y_perm, MOE_F32, ws, ws_bytes, sc->dev_row + kMaxE, compute);
             if (r != MOE_OK) return r;
-            r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
+            r = moe_combine(y_perm, MOE_F32, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
             if (r != MOE_OK) return r;
         }
         // the ids' arrival also retires the previous layer's table and row copies (earlier on the
@@ -336,9 +336,9 @@ extern "C" moe_status moe_decode_step_hybrid(
             if (r != MOE_OK) return r;
             if (!sc) {
                 r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, row, n_slots, slot_pool,
-                                           slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, compute);
+                                           slot_stride, w, ly.shared_w, y_perm, MOE_F32, ws, ws_bytes, compute);
                 if (r != MOE_OK) return r;
-                r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
+                r = moe_combine(y_perm, MOE_F32, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
                 if (r != MOE_OK) return r;
             } else if (!miss.empty()) {
                 // the missed experts again after their copies, then the combine again
@@ -346,9 +346,9 @@ extern "C" moe_status moe_decode_step_hybrid(
                 for (int e : miss) sc->host_row[e] = slots[std::lower_bound(ids.begin(), ids.begin() + n, e) - ids.begin()];
                 MOE_HIP(hipMemcpyAsync(sc->dev_row, sc->host_row, sizeof(int32_t) * E, hipMemcpyHostToDevice, cs));
                 r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, sc->dev_row, n_slots,
-                                           slot_pool, slot_stride, w, nullptr, y_perm, ws, ws_bytes, compute);
+                                           slot_pool, slot_stride, w, nullptr, y_perm, MOE_F32, ws, ws_bytes, compute);
                 if (r != MOE_OK) return r;
-                r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
+                r = moe_combine(y_perm, MOE_F32, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
                 if (r != MOE_OK) return r;
             }
             r = moe_cache_mark_read(cache, ly.layer, compute);
@@ -374,7 +374,7 @@ extern "C" moe_status moe_decode_step_hybrid(
             for (int e : on_cpu) host_table[e] = MOE_SLOT_ELSEWHERE;
             MOE_HIP(hipMemcpyAsync(dev_table, host_table, sizeof(int32_t) * E, hipMemcpyHostToDevice, cs));
             r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, dev_table, n_slots,
-                                       slot_pool, slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, compute);
+                                       slot_pool, slot_stride, w, ly.shared_w, y_perm, MOE_F32, ws, ws_bytes, compute);
             if (r != MOE_OK) return r;
         } else {
             // the first launch produced the resident experts; the GPU's misses again after their
@@ -392,7 +392,7 @@ extern "C" moe_status moe_decode_step_hybrid(
             if (n_gpu_miss > 0) {
                 MOE_HIP(hipMemcpyAsync(dev_table, host_table, sizeof(int32_t) * E, hipMemcpyHostToDevice, cs));
                 r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, dev_table, n_slots,
-                                           slot_pool, slot_stride, w, nullptr, y_perm, ws, ws_bytes, compute);
+                                           slot_pool, slot_stride, w, nullptr, y_perm, MOE_F32, ws, ws_bytes, compute);
                 if (r != MOE_OK) return r;
             }
         }
@@ -408,7 +408,7 @@ extern "C" moe_status moe_decode_step_hybrid(
                                    hipMemcpyHostToDevice, cs));
         }
         n_cpu_total += n_cpu;
-        r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
+        r = moe_combine(y_perm, MOE_F32, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
         if (r != MOE_OK) return r;
         r = moe_cache_mark_read(cache, ly.layer, compute);
         if (r != MOE_OK) return r;
@@ -465,7 +465,7 @@ extern "C" moe_status moe_decode_step_split(moe_cache* cache, int n_layers, cons
             if (r == MOE_OK)
                 r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts,
                                            slot_table + (size_t)ly.layer * E, n_slots, slot_pool, slot_stride, w,
-                                           ly.shared_w, y_perm, ws, ws_bytes, compute);
+                                           ly.shared_w, y_perm, MOE_F32, ws, ws_bytes, compute);
         } else {
             // row 0: the resident experts (missed ones produced elsewhere), row 1: the missed ones
             int32_t* hit_row = host_tables;
@@ -482,14 +482,14 @@ extern "C" moe_status moe_decode_step_split(moe_cache* cache, int n_layers, cons
             r = cache_wait_background(cache, cs);
             if (r == MOE_OK)
                 r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, dev_tables, n_slots,
-                                       slot_pool, slot_stride, w, ly.shared_w, y_perm, ws, ws_bytes, compute);
+                                       slot_pool, slot_stride, w, ly.shared_w, y_perm, MOE_F32, ws, ws_bytes, compute);
             if (r == MOE_OK) r = moe_cache_fill(cache, copy, compute);
             if (r == MOE_OK)
                 r = moe_expert_ffn_grouped(ly.x, act, T, d, f, E, k, perm, offsets, counts, dev_tables + E, n_slots,
-                                           slot_pool, slot_stride, w, nullptr, y_perm, ws, ws_bytes, compute);
+                                           slot_pool, slot_stride, w, nullptr, y_perm, MOE_F32, ws, ws_bytes, compute);
         }
         if (r != MOE_OK) return r;
-        r = moe_combine(y_perm, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
+        r = moe_combine(y_perm, MOE_F32, topk_w, inv_perm, T, k, d, ly.shared_w != nullptr, ly.y, act, compute);
         if (r != MOE_OK) return r;
         r = moe_cache_mark_read(cache, ly.layer, compute);
         if (r != MOE_OK) return r;

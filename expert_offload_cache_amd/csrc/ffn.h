@@ -19,7 +19,8 @@ struct FfnArgs {
     size_t stride;               // bytes per slot
     const uint8_t* shared_w;     // shared expert image or nullptr
     void* h;                     // [rows, f] intermediate (bf16 for bf16 activations, else f32)
-    float* y_perm;               // [rows, d]
+    void* y_perm;                // [rows, d], binary32 or (y_bf16) bf16
+    int y_bf16;                  // y_perm rows are bf16 (each sum rounded once) instead of binary32
     int32_t* status;             // sticky error word
     void* plan;                  // scratch for the prefill tile schedule
     int n_lo = 1, n_hi = 1 << 30;  // a launch covers the experts with n_lo <= n_e <= n_hi tokens
@@ -47,7 +48,7 @@ inline int64_t work_items(const FfnArgs& a, int ntg) {
 moe_status ffn_prepare(FfnArgs& a, const char* fn, const void* x, moe_dtype act, int T, int d, int f, int E, int k,
                        const int32_t* perm, const int32_t* offsets, const int32_t* counts,
                        const int32_t* slot_of_expert, int n_slots, const void* slot_pool, size_t slot_stride,
-                       moe_dtype w, const void* shared_w, float* y_perm);
+                       moe_dtype w, const void* shared_w, void* y_perm, moe_dtype y_dtype);
 // Launch the grouped experts: the prefill MFMA GEMM where it applies, else the decode GEMVs.
 moe_status ffn_run(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st);
 // moe_expert_ffn_grouped with the absent-slot flag going to `status` (device int32) instead of the
@@ -55,7 +56,8 @@ moe_status ffn_run(const FfnArgs& a, moe_dtype act, moe_dtype w, hipStream_t st)
 moe_status ffn_grouped_status(const void* x, moe_dtype act, int T, int d, int f, int E, int k, const int32_t* perm,
                               const int32_t* offsets, const int32_t* counts, const int32_t* slot_of_expert,
                               int n_slots, const void* slot_pool, size_t slot_stride, moe_dtype w,
-                              const void* shared_w, float* y_perm, void* ws, size_t ws_bytes, int32_t* status,
+                              const void* shared_w, void* y_perm, moe_dtype y_dtype, void* ws, size_t ws_bytes,
+                              int32_t* status,
                               moe_stream s);
 
 // decode path: grouped GEMV kernels (ffn_gemv.hip), both projections or one (mode kGateUp = 0,

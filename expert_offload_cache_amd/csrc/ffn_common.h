@@ -23,6 +23,24 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
+// Stores into y_perm row `row`, column `c`: binary32, or bf16 (round to nearest even) when the
+// call asked for bf16 rows (a uniform flag of the launch).
+__device__ __forceinline__ void store_y(const FfnArgs& a, size_t row, int c, float v) {
+    if (a.y_bf16) ((uint16_t*)a.y_perm)[row * a.d + c] = f32_to_bf16(v);
+    else ((float*)a.y_perm)[row * a.d + c] = v;
+}
+// four consecutive columns c .. c+3 (c a multiple of 4)
+__device__ __forceinline__ void store_y4(const FfnArgs& a, size_t row, int c, float v0, float v1, float v2, float v3) {
+    if (a.y_bf16) {
+        uint2 o;
+        o.x = (uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
+        o.y = (uint32_t)f32_to_bf16(v2) | ((uint32_t)f32_to_bf16(v3) << 16);
+        *(uint2*)((uint16_t*)a.y_perm + row * a.d + c) = o;
+    } else {
+        *(float4*)((float*)a.y_perm + row * a.d + c) = make_float4(v0, v1, v2, v3);
+    }
+}
+
 // Work item a of the launch -> (expert, token chunk).  Expert e contributes ceil(n_e / ntg)
 // chunks, in ascending expert id; the shared expert's ceil(T / ntg) chunks come last (e = -1).
 // Only experts whose token count lies in [n_lo, n_hi] take part (the shared expert counts T

@@ -19,12 +19,14 @@ namespace moe {
 moe_status ffn_prepare(FfnArgs& a, const char* fn, const void* x, moe_dtype act, int T, int d, int f, int E, int k,
                        const int32_t* perm, const int32_t* offsets, const int32_t* counts,
                        const int32_t* slot_of_expert, int n_slots, const void* slot_pool, size_t slot_stride,
-                       moe_dtype w, const void* shared_w, float* y_perm) {
+                       moe_dtype w, const void* shared_w, void* y_perm, moe_dtype y_dtype) {
     MOE_CHECK(T >= 0, MOE_ESHAPE, "%s: T=%d < 0", fn, T);
     if (T == 0) return MOE_OK;
     MOE_CHECK(act == MOE_F32 || act == MOE_BF16, MOE_EDTYPE, "%s: bad activation dtype", fn);
     MOE_CHECK(w != MOE_INT4_G128 || act == MOE_BF16, MOE_EDTYPE, "%s: int4 needs bf16 activations", fn);
     MOE_CHECK(w == MOE_INT4_G128 || w == act, MOE_EDTYPE, "%s: dense weights must have the activation dtype", fn);
+    MOE_CHECK(y_dtype == MOE_F32 || (y_dtype == MOE_BF16 && act == MOE_BF16), MOE_EDTYPE,
+              "%s: y_perm must be F32, or BF16 with bf16 activations", fn);
     MOE_CHECK(slot_shape_ok(d, f, w), MOE_ESHAPE, "%s: unsupported d=%d f=%d for dtype %d", fn, d, f, (int)w);
     MOE_CHECK(E >= 1 && E <= 1024 && k >= 1 && k <= E, MOE_ESHAPE, "%s: need 1 <= k <= E <= 1024", fn);
     MOE_CHECK((int64_t)T * k <= (1 << 24), MOE_ESHAPE, "%s: T*k too large", fn);
@@ -53,6 +55,7 @@ moe_status ffn_prepare(FfnArgs& a, const char* fn, const void* x, moe_dtype act,
     a.stride = slot_stride;
     a.shared_w = (const uint8_t*)shared_w;
     a.y_perm = y_perm;
+    a.y_bf16 = y_dtype == MOE_BF16;
     a.status = nullptr;
     a.plan = nullptr;
     a.h = nullptr;
@@ -129,10 +132,10 @@ size_t moe_workspace_bytes(int T, int d, int f, int E, int k, int has_shared, mo
 moe_status moe_expert_ffn_grouped(const void* x, moe_dtype act, int T, int d, int f, int E, int k,
                                   const int32_t* perm, const int32_t* offsets, const int32_t* counts,
                                   const int32_t* slot_of_expert, int n_slots, const void* slot_pool,
-                                  size_t slot_stride, moe_dtype w, const void* shared_w, float* y_perm,
-                                  void* ws, size_t ws_bytes, moe_stream s) {
+                                  size_t slot_stride, moe_dtype w, const void* shared_w, void* y_perm,
+                                  moe_dtype y_dtype, void* ws, size_t ws_bytes, moe_stream s) {
     return moe::ffn_grouped_status(x, act, T, d, f, E, k, perm, offsets, counts, slot_of_expert, n_slots, slot_pool,
-                                   slot_stride, w, shared_w, y_perm, ws, ws_bytes, nullptr, s);
+                                   slot_stride, w, shared_w, y_perm, y_dtype, ws, ws_bytes, nullptr, s);
 }
 
 }  // extern "C"
@@ -141,11 +144,11 @@ namespace moe {
 moe_status ffn_grouped_status(const void* x, moe_dtype act, int T, int d, int f, int E, int k, const int32_t* perm,
                               const int32_t* offsets, const int32_t* counts, const int32_t* slot_of_expert,
                               int n_slots, const void* slot_pool, size_t slot_stride, moe_dtype w,
-                              const void* shared_w, float* y_perm, void* ws, size_t ws_bytes, int32_t* status,
-                              moe_stream s) {
+                              const void* shared_w, void* y_perm, moe_dtype y_dtype, void* ws, size_t ws_bytes,
+                              int32_t* status, moe_stream s) {
     FfnArgs a;
     moe_status r = ffn_prepare(a, "moe_expert_ffn_grouped", x, act, T, d, f, E, k, perm, offsets, counts,
-                               slot_of_expert, n_slots, slot_pool, slot_stride, w, shared_w, y_perm);
+                               slot_of_expert, n_slots, slot_pool, slot_stride, w, shared_w, y_perm, y_dtype);
     if (r != MOE_OK || T == 0) return r;
     MOE_CHECK(ws, MOE_EINVAL, "moe_expert_ffn_grouped: NULL workspace");
     MOE_CHECK((uintptr_t)ws % 256 == 0, MOE_EINVAL, "moe_expert_ffn_grouped: workspace must be 256-byte aligned");

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(max_threads(MODE, W)) void ffn_gemv_kernel(FfnArgs 
                     if (kBf16Act) ((uint16_t*)a.h)[row * a.f + c] = 0;
                     else ((float*)a.h)[row * a.f + c] = 0.f;
                 } else {
-                    a.y_perm[row * a.d + c] = 0.f;
+                    store_y(a, row, c, 0.f);
                 }
             }
             return;
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(max_threads(MODE, W)) void ffn_gemv_kernel(FfnArgs 
                 if (kBf16Act) ((uint16_t*)a.h)[row * a.f + col] = f32_to_bf16(h);
                 else ((float*)a.h)[row * a.f + col] = h;
             } else {
-                a.y_perm[row * a.d + col] = v[0];
+                store_y(a, row, col, v[0]);
             }
         }
     }

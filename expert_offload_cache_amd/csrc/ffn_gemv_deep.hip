@@ -107,7 +107,7 @@ __global__ __launch_bounds__(64 * S * GR) void ffn_gemv_deep_kernel(FfnArgs a) {
                     const size_t row = (size_t)(p0 + i / NOUT);
                     const int c = orow0 + i % NOUT;
                     if (MODE == kGateUp) ((uint16_t*)a.h)[row * a.f + c] = 0;
-                    else a.y_perm[row * a.d + c] = 0.f;
+                    else store_y(a, row, c, 0.f);
                 }
             }
             return;
@@ -274,8 +274,7 @@ __global__ __launch_bounds__(64 * S * GR) void ffn_gemv_deep_kernel(FfnArgs a) {
             } else {
 #pragma unroll
                 for (int u = 0; u < RA; ++u)
-                    *(float4*)(a.y_perm + row * a.d + orow0 + u * 16 + q * 4) =
-                        make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+                    store_y4(a, row, orow0 + u * 16 + q * 4, acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
             }
         }
     } else {
@@ -292,7 +291,7 @@ __global__ __launch_bounds__(64 * S * GR) void ffn_gemv_deep_kernel(FfnArgs a) {
                         f32_to_bf16(silu_mul(acc[2 * p][i], acc[2 * p + 1][i]));
             } else {
 #pragma unroll
-                for (int u = 0; u < RA; ++u) a.y_perm[row * a.d + orow0 + u * 16 + r16] = acc[u][i];
+                for (int u = 0; u < RA; ++u) store_y(a, row, orow0 + u * 16 + r16, acc[u][i]);
             }
         }
     }

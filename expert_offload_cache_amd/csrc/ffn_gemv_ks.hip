@@ -103,7 +103,7 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
                 const size_t row = (size_t)(p0 + i0 + i / NOUT);
                 const int c = orow0 + i % NOUT;
                 if (MODE == kGateUp) ((uint16_t*)a.h)[row * a.f + c] = 0;
-                else a.y_perm[row * a.d + c] = 0.f;
+                else store_y(a, row, c, 0.f);
             }
             return;
         }
@@ -305,8 +305,7 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
             } else {
 #pragma unroll
                 for (int u = 0; u < RA; ++u)
-                    *(float4*)(a.y_perm + row * a.d + orow0 + u * 16 + q * 4) =
-                        make_float4(acc[u][j][0], acc[u][j][1], acc[u][j][2], acc[u][j][3]);
+                    store_y4(a, row, orow0 + u * 16 + q * 4, acc[u][j][0], acc[u][j][1], acc[u][j][2], acc[u][j][3]);
             }
         }
     } else {
@@ -325,7 +324,7 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
                             f32_to_bf16(silu_mul(acc[2 * p][j][i], acc[2 * p + 1][j][i]));
                 } else {
 #pragma unroll
-                    for (int u = 0; u < RA; ++u) a.y_perm[row * a.d + orow0 + u * 16 + r16] = acc[u][j][i];
+                    for (int u = 0; u < RA; ++u) store_y(a, row, orow0 + u * 16 + r16, acc[u][j][i]);
                 }
             }
         }

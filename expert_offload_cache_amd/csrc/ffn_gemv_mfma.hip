@@ -82,7 +82,7 @@ __global__ __launch_bounds__(mfma_max_threads(MODE)) void ffn_gemv_mfma_kernel(F
                 const size_t row = (size_t)(p0 + i0 + i / (16 * RB));
                 const int c = blockIdx.x * RB * 16 + i % (16 * RB);
                 if (MODE == kGateUp) ((uint16_t*)a.h)[row * a.f + c] = 0;
-                else a.y_perm[row * a.d + c] = 0.f;
+                else store_y(a, row, c, 0.f);
             }
             return;
         }
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(mfma_max_threads(MODE)) void ffn_gemv_mfma_kernel(F
             if constexpr (MODE == kGateUp) {
                 ((uint16_t*)a.h)[row * a.f + col] = f32_to_bf16(silu_mul(v[0], v[NM - 1]));
             } else {
-                a.y_perm[row * a.d + col] = v[0];
+                store_y(a, row, col, v[0]);
             }
         }
     };

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(NW * 64, 2) void ffn_mfma_int4_kernel(FfnArgs a) {
                 const size_t row = (size_t)(p0 + t0 + i / nr);
                 const int col = rows0 + i % nr;
                 if (MODE == kGateUp) ((uint16_t*)a.h)[row * a.f + col] = 0;
-                else a.y_perm[row * a.d + col] = 0.f;
+                else store_y(a, row, col, 0.f);
             }
             return;
         }
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(NW * 64, 2) void ffn_mfma_int4_kernel(FfnArgs a) {
 #pragma unroll
             for (int i = 0; i < RA; ++i) {
                 const int col = (blockIdx.x * (MT / 16) + wm * RA + i) * 16 + quad * 4;
-                *(float4*)(a.y_perm + row * a.d + col) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+                store_y4(a, row, col, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
             }
         }
     }
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(NW * 64, 2) void ffn_mfma_areg_kernel(FfnArgs a) {
                 const size_t row = (size_t)(p0 + t0 + i / nr);
                 const int col = rows0 + i % nr;
                 if (MODE == kGateUp) ((uint16_t*)a.h)[row * a.f + col] = 0;
-                else a.y_perm[row * a.d + col] = 0.f;
+                else store_y(a, row, col, 0.f);
             }
             return;
         }
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(NW * 64, 2) void ffn_mfma_areg_kernel(FfnArgs a) {
 #pragma unroll
             for (int i = 0; i < RA; ++i) {
                 const int col = (blockIdx.x * (MT / 16) + wm * RA + i) * 16 + quad * 4;
-                *(float4*)(a.y_perm + row * a.d + col) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+                store_y4(a, row, col, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
             }
         }
     }

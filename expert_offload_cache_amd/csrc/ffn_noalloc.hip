@@ -50,11 +50,11 @@ extern "C" moe_status moe_expert_ffn_grouped_noalloc(const void* x, moe_dtype ac
                                                      const int32_t* perm, const int32_t* offsets,
                                                      const int32_t* counts, const int32_t* slot_of_expert,
                                                      int n_slots, const void* slot_pool, size_t slot_stride,
-                                                     moe_dtype w, const void* shared_w, float* y_perm,
-                                                     int32_t* status, moe_stream s) {
+                                                     moe_dtype w, const void* shared_w, void* y_perm,
+                                                     moe_dtype y_dtype, int32_t* status, moe_stream s) {
     FfnArgs a;
     moe_status r = ffn_prepare(a, "moe_expert_ffn_grouped_noalloc", x, act, T, d, f, E, k, perm, offsets, counts,
-                               slot_of_expert, n_slots, slot_pool, slot_stride, w, shared_w, y_perm);
+                               slot_of_expert, n_slots, slot_pool, slot_stride, w, shared_w, y_perm, y_dtype);
     if (r != MOE_OK || T == 0) return r;
     MOE_CHECK(!status || (uintptr_t)status % 4 == 0, MOE_EINVAL,
               "moe_expert_ffn_grouped_noalloc: status must be 4-byte aligned");

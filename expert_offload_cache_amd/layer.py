@@ -9,7 +9,7 @@ from typing import Optional
 import numpy as np
 
 from . import (combine, expert_ffn_grouped, pack_expert, permute_workspace, route_permute, slot_bytes, workspace_bytes,
-               WDT)
+               y_perm_dtype, WDT)
 from ._lib import MOE_BF16, MOE_F32
 
 
@@ -85,13 +85,14 @@ class DeviceLayer:
 
         dev, k, E, d = self.device, self.k, self.E, self.d
         rows = T * k + (T if self.shared is not None else 0)
+        act = torch.bfloat16 if self.act == "bf16" else torch.float32
         i32 = dict(dtype=torch.int32, device=dev)
         return dict(
             route=(torch.empty((T, k), **i32), torch.empty((T, k), dtype=torch.float32, device=dev),
                    torch.empty((T, E), dtype=torch.float32, device=dev), torch.empty(E, **i32),
                    torch.empty(E + 1, **i32), torch.empty(T * k, **i32), torch.empty(T * k, **i32)),
-            y_perm=torch.empty((rows, d), dtype=torch.float32, device=dev),
-            y=torch.empty((T, d), dtype=torch.bfloat16 if self.act == "bf16" else torch.float32, device=dev),
+            y_perm=torch.empty((rows, d), dtype=y_perm_dtype(act, T), device=dev),
+            y=torch.empty((T, d), dtype=act, device=dev),
             ws=self.workspace(T), pws=permute_workspace(T, k, E, dev))
 
     def forward(self, x, forced_idx=None, ws=None, stream=None, slot_of_expert=None, bufs=None):
@@ -108,6 +109,7 @@ class DeviceLayer:
         soe = self.slot_of_expert if slot_of_expert is None else slot_of_expert
         y_perm, ws = expert_ffn_grouped(x, perm, offsets, counts, soe, self.pool, self.n_slots, self.stride,
                                         self.wdt, self.f, self.k, shared_w=self.shared, y_perm=b.get("y_perm"),
+                                        y_dtype=y_perm_dtype(x.dtype, T),
                                         ws=ws, stream=stream)
         y = combine(y_perm, w, inv, self.k, self.shared is not None, x.dtype, y=b.get("y"), stream=stream)
         return dict(y=y, topk_idx=idx, topk_w=w, logits=logits, counts=counts, offsets=offsets, perm=perm,

@@ -20,7 +20,7 @@ from typing import Optional
 import numpy as np
 
 from . import (MoeError, SlotCache, combine, expert_ffn_grouped, hybrid_split, pack_expert, permute_workspace,
-               pinned_alloc, pinned_free, route_permute, slot_bytes, workspace_bytes, WDT)
+               pinned_alloc, pinned_free, route_permute, slot_bytes, workspace_bytes, y_perm_dtype, WDT)
 from ._lib import MOE_BF16, MOE_F32
 from .layer import _expert_arrays, _to_device
 
@@ -165,6 +165,7 @@ class OffloadStack:
         if T not in self._bufs:
             dev, k, E, d = self.device, self.k, self.E, self.d
             rows = T * k + (T if self.wl.shared else 0)
+            act = torch.bfloat16 if self.wl.act == "bf16" else torch.float32
             self._bufs[T] = dict(
                 route=(torch.empty((T, k), dtype=torch.int32, device=dev),
                        torch.empty((T, k), dtype=torch.float32, device=dev),
@@ -172,8 +173,8 @@ class OffloadStack:
                 perm=(torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
                       torch.empty(T * k, dtype=torch.int32, device=dev),
                       torch.empty(T * k, dtype=torch.int32, device=dev)),
-                y_perm=torch.empty((rows, d), dtype=torch.float32, device=dev),
-                y=torch.empty((T, d), dtype=torch.bfloat16 if self.wl.act == "bf16" else torch.float32, device=dev),
+                y_perm=torch.empty((rows, d), dtype=y_perm_dtype(act, T), device=dev),
+                y=torch.empty((T, d), dtype=act, device=dev),
                 pws=permute_workspace(T, k, E, dev))
         return self._bufs[T]
 

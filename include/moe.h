@@ -165,8 +165,11 @@ MOE_API moe_status moe_route_permute(const void* x, moe_dtype act, int T, int d,
  *   other slot outside [0, n_slots) sets the workspace status word to 1 and that expert's rows
  *   to 0 -- it never reads outside the pool).
  *   shared_w: an always-on shared expert packed like a slot (or NULL); it runs on all T tokens.
- *   y_perm [T*k (+T if shared_w), d] f32: row p = expert output of sorted pair p; rows T*k+t
- *   hold the shared expert's output for token t.
+ *   y_perm [T*k (+T if shared_w), d] of type y_dtype: row p = expert output of sorted pair p; rows
+ *   T*k+t hold the shared expert's output for token t.  y_dtype F32 keeps the binary32 sums;
+ *   BF16 (only with act BF16) rounds each output once to bf16 (nearest even), which halves the
+ *   bytes the grouped call writes and the combine reads: the prefill reading, where the
+ *   intermediate rows may be bf16 like h.  Any other value: MOE_EDTYPE.
  *   ws: device workspace of at least moe_workspace_bytes(...) bytes, zero-filled before its
  *   first use.  Its first 4 bytes are a sticky int32 status word (0 = no error).
  * Intermediate h is rounded to bf16 when act is BF16 (binary32 when act is F32). */
@@ -183,8 +186,8 @@ MOE_API moe_status moe_expert_ffn_grouped(const void* x, moe_dtype act, int T, i
                                           int k, const int32_t* perm, const int32_t* offsets,
                                           const int32_t* counts, const int32_t* slot_of_expert,
                                           int n_slots, const void* slot_pool, size_t slot_stride,
-                                          moe_dtype w, const void* shared_w, float* y_perm,
-                                          void* ws, size_t ws_bytes, moe_stream s);
+                                          moe_dtype w, const void* shared_w, void* y_perm,
+                                          moe_dtype y_dtype, void* ws, size_t ws_bytes, moe_stream s);
 
 /* moe_expert_ffn_grouped for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels, with the
@@ -201,17 +204,18 @@ MOE_API moe_status moe_expert_ffn_grouped_noalloc(const void* x, moe_dtype act, 
                                                   int k, const int32_t* perm, const int32_t* offsets,
                                                   const int32_t* counts, const int32_t* slot_of_expert,
                                                   int n_slots, const void* slot_pool, size_t slot_stride,
-                                                  moe_dtype w, const void* shared_w, float* y_perm,
-                                                  int32_t* status, moe_stream s);
+                                                  moe_dtype w, const void* shared_w, void* y_perm,
+                                                  moe_dtype y_dtype, int32_t* status, moe_stream s);
 
 /* ------------------------------------------------------------------------------------------
  * moe_combine -- gate-weighted sum (pages silent on the form; plain reading):
  *   y[t,:] = sum_{j=0..k-1} topk_w[t,j] * y_perm[inv_perm[t*k+j], :]  (+ y_perm[T*k+t, :] if
  *   has_shared), j ascending, binary32 accumulation, one final rounding to out (F32 or BF16,
- *   round to nearest even). */
-MOE_API moe_status moe_combine(const float* y_perm, const float* topk_w, const int32_t* inv_perm,
-                               int T, int k, int d, int has_shared, void* y, moe_dtype out,
-                               moe_stream s);
+ *   round to nearest even).  y_perm holds y_dtype elements (F32, or BF16 as
+ *   moe_expert_ffn_grouped writes them with y_dtype BF16; widened exactly before the products). */
+MOE_API moe_status moe_combine(const void* y_perm, moe_dtype y_dtype, const float* topk_w,
+                               const int32_t* inv_perm, int T, int k, int d, int has_shared, void* y,
+                               moe_dtype out, moe_stream s);
 
 /* ------------------------------------------------------------------------------------------
  * Expert-slot cache shared by all MoE layers (FreeToken linux guide, "MoE memory handling":

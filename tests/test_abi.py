@@ -78,22 +78,29 @@ def test_host_validation_needs_no_gpu(moe):
     assert b"moe_route_permute" in L.moe_last_error()
     assert rp(vp, 1, 4, 128, vp, None, 8, 2, None, vp, vp, vp, vp, vp, vp, None, None, 0, None) == moe._lib.MOE_EINVAL
     assert rp(vp, 1, 0, 128, vp, None, 2000, 2, None, vp, vp, vp, vp, vp, vp, vp, None, 0, None) == moe._lib.MOE_ESHAPE
-    assert L.moe_combine(vp, vp, vp, 4, 2, 6, 0, vp, 1, None) == moe._lib.MOE_ESHAPE
+    assert L.moe_combine(vp, 0, vp, vp, 4, 2, 6, 0, vp, 1, None) == moe._lib.MOE_ESHAPE
+    # y_perm element type: F32 or BF16 only
+    assert L.moe_combine(vp, 2, vp, vp, 4, 2, 8, 0, vp, 1, None) == moe._lib.MOE_EDTYPE
     a = ctypes.c_void_p(256)
     # int4 weights need bf16 activations; dense weights must match the activation dtype
-    assert L.moe_expert_ffn_grouped(a, 0, 4, 2048, 768, 128, 8, a, a, a, a, 128, a, 9437184, 2, None, a,
+    assert L.moe_expert_ffn_grouped(a, 0, 4, 2048, 768, 128, 8, a, a, a, a, 128, a, 9437184, 2, None, a, 0,
                                     a, 1 << 30, None) == moe._lib.MOE_EDTYPE
-    assert L.moe_expert_ffn_grouped(a, 0, 4, 2048, 768, 128, 8, a, a, a, a, 128, a, 9437184, 1, None, a,
+    assert L.moe_expert_ffn_grouped(a, 0, 4, 2048, 768, 128, 8, a, a, a, a, 128, a, 9437184, 1, None, a, 0,
+                                    a, 1 << 30, None) == moe._lib.MOE_EDTYPE
+    # bf16 y_perm needs bf16 activations; other y_perm types are refused
+    assert L.moe_expert_ffn_grouped(a, 0, 4, 2048, 768, 128, 8, a, a, a, a, 128, a, 9437184 * 2, 0, None, a, 1,
+                                    a, 1 << 30, None) == moe._lib.MOE_EDTYPE
+    assert L.moe_expert_ffn_grouped(a, 1, 4, 2048, 768, 128, 8, a, a, a, a, 128, a, 9437184, 1, None, a, 2,
                                     a, 1 << 30, None) == moe._lib.MOE_EDTYPE
     # stride smaller than a slot
-    assert L.moe_expert_ffn_grouped(a, 1, 4, 2048, 768, 128, 8, a, a, a, a, 128, a, 4096, 1, None, a,
+    assert L.moe_expert_ffn_grouped(a, 1, 4, 2048, 768, 128, 8, a, a, a, a, 128, a, 4096, 1, None, a, 0,
                                     a, 1 << 30, None) == moe._lib.MOE_EINVAL
     # T == 0 is a no-op
     assert L.moe_route(None, 1, 0, 128, None, None, 8, 2, None, None, None, None, None) == 0
     # workspace too small
     ws_need = moe.workspace_bytes(4, 2048, 768, 128, 8, False, 1, 1)
     assert L.moe_expert_ffn_grouped(ctypes.c_void_p(256), 1, 4, 2048, 768, 128, 8, vp, vp, vp, vp, 128,
-                                    ctypes.c_void_p(256), 9437184, 1, None, ctypes.c_void_p(256),
+                                    ctypes.c_void_p(256), 9437184, 1, None, ctypes.c_void_p(256), 1,
                                     ctypes.c_void_p(256), ws_need - 1, None) == moe._lib.MOE_ENOMEM
     # the decode step checks its arguments before any call: no cache, no layers, bad shapes
     # (after slot_table: topk_idx .. ws = 9 buffers, ws_bytes, host_idx, compute, copy)

@@ -33,8 +33,8 @@ def _check_experts_whole(out, x, wl, experts, shared, T, tight=None, int4_bf16=F
     """Every token of the 3 heaviest and 3 lightest touched experts (and of the shared expert):
     their rows of y_perm (the expert's own output, before the gates) against the oracle's expert on
     the same tokens, per-row normwise relative error <= 2e-2 against exact weights.  With `tight`,
-    also against the oracle with the GPU's roundings (h rounded to bf16; with int4_bf16, int4 weights
-    seen as bf16(q*s)): every row within `tight`, and the mean row error at most half of the mean
+    also against the oracle with the GPU's roundings (h rounded to bf16; bf16 y_perm rows rounded to
+    bf16; with int4_bf16, int4 weights seen as bf16(q*s)): every row within `tight`, and the mean row error at most half of the mean
     against the plain oracle (the roundings the oracle now models were most of the difference; what
     is left is binary32 accumulation and the h elements whose bf16 rounding flips between a binary32
     and a binary64 h)."""
@@ -49,6 +49,7 @@ def _check_experts_whole(out, x, wl, experts, shared, T, tight=None, int4_bf16=F
     pick = sorted(set(order[:3].tolist() + order[-3:].tolist()))
     xf = act_to_f64(x, "bf16")
     yp_all = out["y_perm"]
+    y_bf16 = str(yp_all.dtype) == "torch.bfloat16"  # prefill rows rounded once to bf16
     groups = [(int(e), perm[off[e]:off[e + 1]] // wl.k, yp_all[off[e]:off[e + 1]], experts[int(e)]) for e in pick]
     if shared is not None:
         groups.append((-1, np.arange(T), yp_all[T * wl.k:T * wl.k + T], shared))
@@ -58,14 +59,14 @@ def _check_experts_whole(out, x, wl, experts, shared, T, tight=None, int4_bf16=F
     gemv_max = lib().moe_prefill_gemv_tokens(MOE_INT4_G128) if int4_bf16 else 0
     worst, worst_t, errs, errs_t = 0.0, 0.0, [], []
     for e, toks, yp, ew in groups:
-        y = yp.cpu().numpy().astype(np.float64)
+        y = y_to_f64(yp)
         err = rel_err_per_token(y, swiglu_expert(xf[toks], *expert_to_f64(ew)))
         worst = max(worst, float(err.max()))
         errs.append(err)
         assert err.max() <= 2e-2, (e, len(toks), err.max())
         if tight is not None:
             on_gemm = int4_bf16 and (e == -1 or len(toks) > gemv_max)
-            ref = swiglu_expert(xf[toks], *expert_to_f64(ew, int4_bf16=on_gemm), h_bf16=True)
+            ref = swiglu_expert(xf[toks], *expert_to_f64(ew, int4_bf16=on_gemm), h_bf16=True, y_bf16=y_bf16)
             et = rel_err_per_token(y, ref)
             worst_t = max(worst_t, float(et.max()))
             errs_t.append(et)
@@ -225,13 +226,14 @@ def test_absent_slot_is_flagged_not_read(qwen_layer, T):
     soe[e_bad] = -1
     ws = layer.workspace(T)
     y_perm, ws = moe.expert_ffn_grouped(x, out["perm"], out["offsets"], out["counts"], soe, layer.pool,
-                                        layer.n_slots, layer.stride, "bf16", wl.f, wl.k, ws=ws)
+                                        layer.n_slots, layer.stride, "bf16", wl.f, wl.k, ws=ws,
+                                        y_dtype=out["y_perm"].dtype)
     torch.cuda.synchronize()
     assert int(ws[:4].view(torch.int32).item()) == 1
     off = out["offsets"].cpu().numpy()
-    yp = y_perm.cpu().numpy()
+    yp = y_to_f64(y_perm)
     assert np.all(yp[off[e_bad]:off[e_bad + 1]] == 0)
-    ref = out["y_perm"].cpu().numpy()
+    ref = y_to_f64(out["y_perm"])
     keep = np.ones(len(yp), bool)
     keep[off[e_bad]:off[e_bad + 1]] = False
     assert np.array_equal(yp[keep], ref[keep])
@@ -258,11 +260,11 @@ def test_int4_absent_slot_is_flagged_not_read(dsv4_int4_layer, T):
     torch.cuda.synchronize()
     assert int(ws[:4].view(torch.int32).item()) == 1
     off = out["offsets"].cpu().numpy()
-    yp = y_perm.cpu().numpy()
+    yp = y_to_f64(y_perm)
     assert np.all(yp[off[e_bad]:off[e_bad + 1]] == 0)
     keep = np.ones(len(yp), bool)
     keep[off[e_bad]:off[e_bad + 1]] = False
-    assert np.array_equal(yp[keep], out["y_perm"].cpu().numpy()[keep])
+    assert np.array_equal(yp[keep], y_to_f64(out["y_perm"])[keep])
 
 
 @pytest.fixture(scope="module")
@@ -429,4 +431,4 @@ def test_empty_batch_is_a_no_op():
     assert lib().moe_permute(None, 0, k, E, counts.data_ptr(), offsets.data_ptr(), None, None, None, 0, None) == 0
     torch.cuda.synchronize()
     assert counts.cpu().tolist() == [0] * E and offsets.cpu().tolist() == [0] * (E + 1)
-    assert lib().moe_combine(None, None, None, 0, k, d, 0, None, MOE_BF16, None) == 0
+    assert lib().moe_combine(None, 0, None, None, 0, k, d, 0, None, MOE_BF16, None) == 0
