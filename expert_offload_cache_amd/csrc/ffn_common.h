@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "ffn.h"
 #include "slot_layout.h"
 
@@ -23,15 +25,20 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
-// Stores into y_perm row `row`, column `c`: binary32, or bf16 (round to nearest even) when the
-// call asked for bf16 rows (a uniform flag of the launch).
-__device__ __forceinline__ void store_y(const FfnArgs& a, size_t row, int c, float v) {
-    if (a.y_bf16) ((uint16_t*)a.y_perm)[row * a.d + c] = f32_to_bf16(v);
+// Stores into y_perm row `row`, column `c`: binary32, or with YB bf16 (round to nearest even), the
+// element type the call asked for (a.y_bf16).  The decode kernels pick YB once, outside their
+// store loops (a test of the flag at every store measured 2 % slower at a few tokens); the other
+// kernels test the flag per store (store_y, store_y4).
+template <bool YB>
+__device__ __forceinline__ void store_y_as(const FfnArgs& a, size_t row, int c, float v) {
+    if constexpr (YB) ((uint16_t*)a.y_perm)[row * a.d + c] = f32_to_bf16(v);
     else ((float*)a.y_perm)[row * a.d + c] = v;
 }
 // four consecutive columns c .. c+3 (c a multiple of 4)
-__device__ __forceinline__ void store_y4(const FfnArgs& a, size_t row, int c, float v0, float v1, float v2, float v3) {
-    if (a.y_bf16) {
+template <bool YB>
+__device__ __forceinline__ void store_y4_as(const FfnArgs& a, size_t row, int c, float v0, float v1, float v2,
+                                            float v3) {
+    if constexpr (YB) {
         uint2 o;
         o.x = (uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
         o.y = (uint32_t)f32_to_bf16(v2) | ((uint32_t)f32_to_bf16(v3) << 16);
@@ -39,6 +46,21 @@ __device__ __forceinline__ void store_y4(const FfnArgs& a, size_t row, int c, fl
     } else {
         *(float4*)((float*)a.y_perm + row * a.d + c) = make_float4(v0, v1, v2, v3);
     }
+}
+__device__ __forceinline__ void store_y(const FfnArgs& a, size_t row, int c, float v) {
+    if (a.y_bf16) store_y_as<true>(a, row, c, v);
+    else store_y_as<false>(a, row, c, v);
+}
+__device__ __forceinline__ void store_y4(const FfnArgs& a, size_t row, int c, float v0, float v1, float v2, float v3) {
+    if (a.y_bf16) store_y4_as<true>(a, row, c, v0, v1, v2, v3);
+    else store_y4_as<false>(a, row, c, v0, v1, v2, v3);
+}
+// Runs f(std::true_type) when the call's y_perm rows are bf16 (only the down projection stores
+// them), else f(std::false_type): one test of the flag for a whole store loop.
+template <int MODE, typename F>
+__device__ __forceinline__ void with_y_type(const FfnArgs& a, F&& f) {
+    if (MODE == kDown && a.y_bf16) f(std::true_type{});
+    else f(std::false_type{});
 }
 
 // Work item a of the launch -> (expert, token chunk).  Expert e contributes ceil(n_e / ntg)

@@ -286,49 +286,52 @@ __global__ __launch_bounds__(64 * kKsWaves) void ffn_gemv_ks_kernel(FfnArgs a) {
     }
 
     // ---- outputs straight from the accumulators ------------------------------------------------
-    if constexpr (!kInt4) {
-        // lane l: token 16 j + l%16, rows 4(l/16) .. +3 of each row block
+    with_y_type<MODE>(a, [&](auto yt) __attribute__((always_inline)) {
+        constexpr bool YB = decltype(yt)::value;
+        if constexpr (!kInt4) {
+            // lane l: token 16 j + l%16, rows 4(l/16) .. +3 of each row block
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const int tok = 16 * j + r16;
-            if (tok >= nt) continue;
-            const size_t row = (size_t)(p0 + i0 + tok);
-            if constexpr (MODE == kGateUp) {
-#pragma unroll
-                for (int p = 0; p < RA / 2; ++p) {
-                    const f32x4_t g = acc[2 * p][j], u = acc[2 * p + 1][j];
-                    uint2 o;
-                    o.x = (uint32_t)f32_to_bf16(silu_mul(g[0], u[0])) | ((uint32_t)f32_to_bf16(silu_mul(g[1], u[1])) << 16);
-                    o.y = (uint32_t)f32_to_bf16(silu_mul(g[2], u[2])) | ((uint32_t)f32_to_bf16(silu_mul(g[3], u[3])) << 16);
-                    *(uint2*)((uint16_t*)a.h + row * a.f + orow0 + p * 16 + q * 4) = o;
-                }
-            } else {
-#pragma unroll
-                for (int u = 0; u < RA; ++u)
-                    store_y4(a, row, orow0 + u * 16 + q * 4, acc[u][j][0], acc[u][j][1], acc[u][j][2], acc[u][j][3]);
-            }
-        }
-    } else {
-        // lane l: row l%16 of each row block, tokens 16 j + 4(l/16) .. +3
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = 16 * j + 4 * q + i;
+            for (int j = 0; j < G; ++j) {
+                const int tok = 16 * j + r16;
                 if (tok >= nt) continue;
                 const size_t row = (size_t)(p0 + i0 + tok);
                 if constexpr (MODE == kGateUp) {
 #pragma unroll
-                    for (int p = 0; p < RA / 2; ++p)
-                        ((uint16_t*)a.h)[row * a.f + orow0 + p * 16 + r16] =
-                            f32_to_bf16(silu_mul(acc[2 * p][j][i], acc[2 * p + 1][j][i]));
+                    for (int p = 0; p < RA / 2; ++p) {
+                        const f32x4_t g = acc[2 * p][j], u = acc[2 * p + 1][j];
+                        uint2 o;
+                        o.x = (uint32_t)f32_to_bf16(silu_mul(g[0], u[0])) | ((uint32_t)f32_to_bf16(silu_mul(g[1], u[1])) << 16);
+                        o.y = (uint32_t)f32_to_bf16(silu_mul(g[2], u[2])) | ((uint32_t)f32_to_bf16(silu_mul(g[3], u[3])) << 16);
+                        *(uint2*)((uint16_t*)a.h + row * a.f + orow0 + p * 16 + q * 4) = o;
+                    }
                 } else {
 #pragma unroll
-                    for (int u = 0; u < RA; ++u) store_y(a, row, orow0 + u * 16 + r16, acc[u][j][i]);
+                    for (int u = 0; u < RA; ++u)
+                        store_y4_as<YB>(a, row, orow0 + u * 16 + q * 4, acc[u][j][0], acc[u][j][1], acc[u][j][2], acc[u][j][3]);
+                }
+            }
+        } else {
+            // lane l: row l%16 of each row block, tokens 16 j + 4(l/16) .. +3
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tok = 16 * j + 4 * q + i;
+                    if (tok >= nt) continue;
+                    const size_t row = (size_t)(p0 + i0 + tok);
+                    if constexpr (MODE == kGateUp) {
+#pragma unroll
+                        for (int p = 0; p < RA / 2; ++p)
+                            ((uint16_t*)a.h)[row * a.f + orow0 + p * 16 + r16] =
+                                f32_to_bf16(silu_mul(acc[2 * p][j][i], acc[2 * p + 1][j][i]));
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < RA; ++u) store_y_as<YB>(a, row, orow0 + u * 16 + r16, acc[u][j][i]);
+                    }
                 }
             }
         }
-    }
+    });
 }
 
 }  // namespace
