@@ -432,3 +432,50 @@ def test_empty_batch_is_a_no_op():
     torch.cuda.synchronize()
     assert counts.cpu().tolist() == [0] * E and offsets.cpu().tolist() == [0] * (E + 1)
     assert lib().moe_combine(None, 0, None, None, 0, k, d, 0, None, MOE_BF16, None) == 0
+
+
+# every kernel path that writes y_perm: decode GEMVs (deep int4, K-streaming bf16 and int4, the
+# split-input and vector-ALU kernels), the bf16 and int4 GEMMs and their light-expert launches
+Y16 = [
+    # (act, wdt, d, f, E, k, T, shared)
+    ("bf16", "bf16", 512, 256, 8, 2, 3, True),       # K-streaming bf16, few tokens
+    ("bf16", "bf16", 4096, 64, 4, 2, 20, False),     # K-streaming bf16, 32-token items
+    ("bf16", "bf16", 2112, 64, 4, 2, 20, False),     # split-input down (132 row blocks)
+    ("bf16", "bf16", 320, 96, 8, 2, 9, True),        # split-input kernel, both projections
+    ("bf16", "int4", 4096, 2048, 8, 2, 1, True),     # deep int4 decode kernel
+    ("bf16", "int4", 512, 512, 8, 2, 20, True),      # K-streaming int4
+    ("bf16", "int4", 256, 128, 8, 2, 5, True),       # vector-ALU int4 down
+    ("bf16", "bf16", 512, 256, 64, 2, 300, True),    # bf16 GEMM + its light-expert launch
+    ("bf16", "int4", 512, 256, 32, 2, 300, True),    # int4 GEMM + light experts
+    ("bf16", "bf16", 256, 256, 3, 1, 1000, True),    # GEMM tiles with ragged tails
+]
+
+
+@pytest.mark.parametrize("act,wdt,d,f,E,k,T,shared", Y16)
+def test_bf16_rows_are_the_binary32_rows_rounded(act, wdt, d, f, E, k, T, shared):
+    """y_perm as bf16 rows is the binary32 y_perm of the same call rounded to nearest even, bit for
+    bit (the kernels round their binary32 sums once at the store), and the combine over bf16 rows
+    equals the combine over binary32 rows holding the same values, bit for bit (widening is exact)."""
+    need_gpu()
+    import torch
+    import expert_offload_cache_amd as moe
+    from expert_offload_cache_amd.layer import DeviceLayer
+
+    print(f"bf16 rows {wdt} d={d} f={f} E={E} k={k} T={T}", flush=True)
+    wl = small_workload(act, wdt, d, f, E, k, shared=shared, bias=1.1)
+    li = synth.layer_inputs(wl, T, seed=11)
+    layer = DeviceLayer.from_inputs(li)
+    x = layer.x_to_device(li.x)
+    out = layer.forward(x)
+    args = (x, out["perm"], out["offsets"], out["counts"], layer.slot_of_expert, layer.pool, layer.n_slots,
+            layer.stride, layer.wdt, layer.f, layer.k)
+    y32, _ = moe.expert_ffn_grouped(*args, shared_w=layer.shared, y_dtype=torch.float32)
+    y16, _ = moe.expert_ffn_grouped(*args, shared_w=layer.shared, y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+    # combine: bf16 rows against the same values held as binary32
+    w, inv = out["topk_w"], out["inv_perm"]
+    a = moe.combine(y16, w, inv, k, shared, torch.bfloat16)
+    b = moe.combine(y16.float(), w, inv, k, shared, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
