@@ -57,8 +57,7 @@ moe_status ffn_grouped_status(const void* x, moe_dtype act, int T, int d, int f,
                               const int32_t* offsets, const int32_t* counts, const int32_t* slot_of_expert,
                               int n_slots, const void* slot_pool, size_t slot_stride, moe_dtype w,
                               const void* shared_w, void* y_perm, moe_dtype y_dtype, void* ws, size_t ws_bytes,
-                              int32_t* status,
-                              moe_stream s);
+                              int32_t* status, moe_stream s);
 
 // decode path: grouped GEMV kernels (ffn_gemv.hip), both projections or one (mode kGateUp = 0,
 // kDown = 1)
