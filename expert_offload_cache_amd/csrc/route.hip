@@ -146,6 +146,15 @@ __global__ __launch_bounds__(256) void route_logits_tiled(const void* __restrict
 // binary32 once while staged, then read back as float4 so one LDS read serves four steps.
 constexpr int kSplitRow = 36;  // padded LDS row (floats): the 8 rows one read touches hit distinct banks
 
+// Orders a wave's own LDS writes and reads (its lanes read rows other lanes of the wave staged); the
+// waves of a block stage into separate areas, so they need not meet there (a block barrier per
+// chunk instead measured 6-9 % slower, same bits).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ void widen_store(float* dst, u32x4_t v) {
     float4 lo = make_float4(as_f32(v.x << 16), as_f32(v.x & 0xFFFF0000u), as_f32(v.y << 16), as_f32(v.y & 0xFFFF0000u));
     float4 hi = make_float4(as_f32(v.z << 16), as_f32(v.z & 0xFFFF0000u), as_f32(v.w << 16), as_f32(v.w & 0xFFFF0000u));
@@ -204,7 +213,7 @@ __global__ __launch_bounds__(256) void route_logits_split(const uint16_t* __rest
 
     gload(0);
     sstore();
-    __syncthreads();
+    wave_lds_sync();
     for (int ch = 0; ch < nch; ++ch) {
         gload(min(ch + 1, nch - 1));
 #pragma unroll
@@ -254,10 +263,11 @@ __global__ __launch_bounds__(256) void route_logits_split(const uint16_t* __rest
                     for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
             }
         }
-        __syncthreads();
+        wave_lds_sync();
         sstore();
-        __syncthreads();
+        wave_lds_sync();
     }
+    __syncthreads();  // the join below reuses every wave's staging area
     // acc = this wave's subtree root.  Join the four: (q0 + q1) + (q2 + q3), then the bias.
     float* part = &lds[0][0][0][0];  // [4 waves][32 tokens][32 experts], staging no longer needed
 #pragma unroll
