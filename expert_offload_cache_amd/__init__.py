@@ -228,10 +228,17 @@ DECODE_LAYER = np.dtype([("x", "<u8"), ("w_router", "<u8"), ("bias", "<u8"), ("f
                          ("shared_w", "<u8"), ("y", "<u8"), ("layer", "<i4"), ("reserved", "<i4")])
 
 
+def _f32_rows(y_perm, fn: str):
+    """The decode steps keep y_perm in binary32 (their C signature takes float rows)."""
+    if _y_code(y_perm) != MOE_F32:
+        raise TypeError(f"{fn}: y_perm must be float32, got {y_perm.dtype}")
+
+
 def decode_step(cache, layers: np.ndarray, T: int, d: int, f: int, E: int, k: int, act: int, wdt: str, slot_pool,
                 n_slots: int, slot_stride: int, slot_table, route_bufs, perm_bufs, y_perm, ws, host_idx, compute,
                 copy):
     """One decode step of every layer in `layers` (a DECODE_LAYER array) through moe_decode_step."""
+    _f32_rows(y_perm, "decode_step")
     idx, w, logits = route_bufs
     c, o, p, ip = perm_bufs
     check(lib().moe_decode_step(cache.h, len(layers), layers.ctypes.data, T, d, f, E, k, act, WDT[wdt],
@@ -246,6 +253,7 @@ def decode_step_split(cache, layers: np.ndarray, T: int, d: int, f: int, E: int,
                       host_idx, host_tables, dev_tables, compute, copy):
     """One decode step of every layer in `layers` with split launches (moe_decode_step_split).
     host_tables: pinned int32 [2, E]; dev_tables: device int32 [2, E]."""
+    _f32_rows(y_perm, "decode_step_split")
     idx, w, logits = route_bufs
     c, o, p, ip = perm_bufs
     check(lib().moe_decode_step_split(cache.h, len(layers), layers.ctypes.data, T, d, f, E, k, act, WDT[wdt],
@@ -261,6 +269,7 @@ def decode_step_hybrid(cache, layers: np.ndarray, d: int, f: int, E: int, k: int
     """One batch-1 decode step of every layer in `layers` with hybrid miss handling
     (moe_decode_step_hybrid).  host_idx/host_x/host_y/host_table: pinned host tensors; dev_table:
     device int32 [E].  -> number of experts run on the host."""
+    _f32_rows(y_perm, "decode_step_hybrid")
     idx, w, logits = route_bufs
     c, o, p, ip = perm_bufs
     n_cpu = ctypes.c_int64(0)

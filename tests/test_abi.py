@@ -1,6 +1,7 @@
 """The C-ABI library: it loads, exports every declared symbol, rejects bad arguments on the host,
 and packs experts into the slot layout the header documents.  No GPU needed."""
 import ctypes
+import inspect
 import os
 import re
 
@@ -216,3 +217,25 @@ def test_pack_expert_layout_roundtrip(moe, wdt, d, f):
         assert np.array_equal(_unpack_dense(gate, f, d, dt), ew.wg)
         assert np.array_equal(_unpack_dense(up, f, d, dt), ew.wu)
         assert np.array_equal(_unpack_dense(down, d, f, dt), ew.wd)
+
+
+def test_y_perm_element_types_in_the_binding(moe):
+    """y_perm's element type goes to the library from the tensor (float32 or bfloat16, nothing
+    else); the layer orchestration keeps bf16 rows for bf16 prefill only; the decode steps, whose C
+    signature takes float rows, refuse anything but float32 before calling the library."""
+    import torch
+
+    assert moe._y_code(torch.empty(1, dtype=torch.float32)) == moe._lib.MOE_F32
+    assert moe._y_code(torch.empty(1, dtype=torch.bfloat16)) == moe._lib.MOE_BF16
+    with pytest.raises(TypeError):
+        moe._y_code(torch.empty(1, dtype=torch.float16))
+    assert moe.y_perm_dtype(torch.bfloat16, 65) == torch.bfloat16
+    assert moe.y_perm_dtype(torch.bfloat16, 64) == torch.float32
+    assert moe.y_perm_dtype(torch.float32, 4096) == torch.float32
+    y16 = torch.empty((4, 8), dtype=torch.bfloat16)
+    for fn, nargs in ((moe.decode_step, 20), (moe.decode_step_split, 22), (moe.decode_step_hybrid, 26)):
+        args = [None] * nargs
+        pos = list(inspect.signature(fn).parameters).index("y_perm")
+        args[pos] = y16
+        with pytest.raises(TypeError, match="y_perm must be float32"):
+            fn(*args)
