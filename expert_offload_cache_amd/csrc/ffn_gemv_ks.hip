@@ -400,15 +400,18 @@ moe_status ffn_gemv_ks(const FfnArgs& a, int mode, moe_dtype w, hipStream_t st) 
     if (plan < 0) return MOE_EDTYPE;
     if (w == MOE_BF16 && mode == kGateUp) {
         if (plan == 0) return launch_ks<kGateUp, MOE_BF16, 2, 1, 4, 4, false, true>(a, st, "ffn_gemv_gateup_bf16");
-        // Decode calls (up to 64 tokens) read the weights through the cache: an expert holding more
-        // tokens than a 32-token item has two items, which stream the same weights, and the later one
-        // (the next blockIdx.y with the same blockIdx.x, on the same XCD a few dispatches later)
-        // finds them in L2.  Measured at 64 tokens: 58.3 -> 56.7 us and 323.5 -> 294.2 MB a launch
-        // (1.02x its algorithmic bytes); the next step's router logits, whose weights the cached
-        // expert weights displace, take 0.4 us longer, and the layer time is unchanged.  The light
-        // experts of a bf16 prefill call (single items, nothing read twice) ran 3-5 % slower with
-        // cached weight loads, so calls above 64 tokens keep them non-temporal.
-        if (a.T <= 64) return launch_ks<kGateUp, MOE_BF16, 4, 2, 4, 4, false, true, true>(a, st, "ffn_gemv_gateup_bf16");
+        // Decode calls (17 to 64 tokens) take 16-token items and read the weights through the cache:
+        // an expert holding more than 16 tokens has several items, which stream the same weights,
+        // and the later ones (the next blockIdx.y with the same blockIdx.x, on the same XCD a few
+        // dispatches later) find them in L2, so the smaller items buy more workgroups for little
+        // HBM traffic.  Measured against 32-token items with non-temporal loads: 58.3 -> 56.3 us at
+        // 64 tokens (323.5 MB a launch before), 47.5 -> 44.5 us at 32 (with cached loads alone:
+        // 56.8 and 47.5).  The next step's router logits, whose weights the cached expert weights
+        // displace, take about 0.4 us longer.  The light experts of a bf16 prefill call (single
+        // items, nothing read twice) ran 3-5 % slower with cached weight loads, and up to 16 tokens
+        // the cached 16-token plan with two pairs a wave is slower than plan 0, so both stay as
+        // they were.
+        if (a.T <= 64) return launch_ks<kGateUp, MOE_BF16, 4, 1, 4, 4, false, true, true>(a, st, "ffn_gemv_gateup_bf16");
         return launch_ks<kGateUp, MOE_BF16, 4, 2, 4, 4, false, true>(a, st, "ffn_gemv_gateup_bf16");
     }
     if (w == MOE_BF16) {
