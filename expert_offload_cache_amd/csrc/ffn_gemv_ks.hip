@@ -368,12 +368,13 @@ static moe_status launch_ks(const FfnArgs& a, hipStream_t st, const char* name) 
 //   bf16 gate/up: four waves split the inputs of a wave's row blocks, interleaved (wave s takes
 //     stages s, s+4, ...: the group reads adjacent fragments at a time, measured 1-2 us faster
 //     than contiguous shares); one gate/up pair a wave over 16-token items up to 16 tokens, two
-//     pairs a wave over 32-token items above (58.8 against 60.4 us at 64 tokens for one pair;
-//     faster than the split-input kernel at 64 tokens although the experts holding more than 32
-//     tokens read their weights twice);
+//     pairs a wave over 16-token items with cached weight loads up to 64 (the dispatch below
+//     gives the figures), two pairs a wave over 32-token items above;
 //   bf16 down: one row block a wave with 5 stages in flight for up to 4 tokens, four row blocks
-//     a wave with one stage ahead up to 16 tokens (19.7 against 21.0 us at 16), else two row
-//     blocks a wave over 32-token items;
+//     a wave with one stage ahead up to 16 tokens (19.7 against 21.0 us at 16), two row blocks
+//     a wave over 32-token items with two waves splitting their inputs, interleaved, up to 32
+//     tokens (24.2 against 25.4 us at 24 tokens and 26.1 against 28.2 at 32; equal at 48 and
+//     35.4 against 33.1 at 64), else the same without the split;
 //   int4 gate/up: below 8 tokens four waves split the inputs of two gate/up pairs, interleaved
 //     (21.9 against 22.5 us for the vector-ALU kernel at one token, 29.0 against 31.9 for two
 //     waves splitting one pair at two); from 8 tokens one wave takes two pairs over all inputs
@@ -386,7 +387,7 @@ static moe_status launch_ks(const FfnArgs& a, hipStream_t st, const char* name) 
 static int ks_plan(int mode, moe_dtype w, int T) {
     if (w == MOE_BF16) {
         if (mode == kGateUp) return T <= 16 ? 0 : 1;
-        return T <= 4 ? 0 : T <= 16 ? 2 : 1;
+        return T <= 4 ? 0 : T <= 16 ? 2 : T <= 32 ? 3 : 1;
     }
     if (w == MOE_INT4_G128) {
         if (mode == kGateUp) return T >= 8 ? 1 : 2;
@@ -418,6 +419,10 @@ moe_status ffn_gemv_ks(const FfnArgs& a, int mode, moe_dtype w, hipStream_t st) 
         if (plan == 0) return launch_ks<kDown, MOE_BF16, 1, 1, 6, 1>(a, st, "ffn_gemv_down_bf16");
         if (plan == 2) {
             const moe_status r = launch_ks<kDown, MOE_BF16, 4, 2, 2, 1>(a, st, "ffn_gemv_down_bf16");
+            if (r != MOE_EDTYPE) return r;
+        }
+        if (plan == 3) {
+            const moe_status r = launch_ks<kDown, MOE_BF16, 2, 2, 4, 2, false, true>(a, st, "ffn_gemv_down_bf16");
             if (r != MOE_EDTYPE) return r;
         }
         return launch_ks<kDown, MOE_BF16, 2, 2, 4, 1>(a, st, "ffn_gemv_down_bf16");

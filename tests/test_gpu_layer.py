@@ -158,7 +158,7 @@ def qwen_layer():
     gc.collect()
 
 
-@pytest.mark.parametrize("T", [1, 4, 16, 64, 256])
+@pytest.mark.parametrize("T", [1, 4, 16, 32, 64, 256])
 def test_qwen_a3b_decode_layer(qwen_layer, T):
     wl, li64, layer = qwen_layer
     print(f"qwen-a3b decode bf16 T={T}", flush=True)
